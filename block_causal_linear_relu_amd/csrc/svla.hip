@@ -1,0 +1,1407 @@
+// libsvla -- block-causal ReLU linear attention for AMD Instinct MI355X (gfx950).
+//
+// The C ABI is declared in include/svla.h, which states the method and cites
+// the SANA-Video pages that define it.  This file holds the three kernels of
+// the path and the host code around them:
+//
+//   svla_state_build   per (b,h,block,split): S_part = sum_j R_j phi(k_j) (x) v_j
+//                      and z_part = sum_j phi(k_j) on bf16 (or fp32) MFMA with
+//                      fp32 accumulation; K/V tiles staged in LDS from
+//                      coalesced 128-bit buffer loads.
+//   svla_state_scan    per (b,h,state tile): sums the split partials and takes
+//                      the inclusive, optionally decayed prefix over blocks;
+//                      writes each block's state in the register layout the
+//                      apply kernel feeds to the matrix cores, and the final
+//                      state.
+//   svla_apply         per (b,h,block,token tile): O = phi~(Q) S / (phi(Q) z + eps)
+//                      with O^T = S^T phi~(Q)^T on MFMA, the denominator on the
+//                      vector ALU, RoPE on the numerator operand only.
+//
+// Every global access of the hot kernels goes through a buffer resource
+// sized to the (b,h) slice it belongs to: a lane whose token lies past the
+// end of its range is given an offset past the resource and reads zeros /
+// drops its store.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/svla.h"
+
+// ---------------------------------------------------------------------------
+// types and small device helpers
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) unsigned short u16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) short i16x2_t;
+
+namespace {
+
+constexpr int kThreads = 256;                 // every kernel: 4 waves of 64
+constexpr uint32_t kOOB = 0x80000000u;        // an offset past every resource
+constexpr int kMaxRopeEntries = 4096;         // (cos, sin) pairs per workgroup
+
+// gfx9 raw buffer: stride 0, range check on bytes, 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+// Reinterpretation helpers.  They take their operand by value on purpose:
+// this compiler folds a bit cast applied directly to a vector element
+// subscript (v[e]) to element 0, so element reads always go through these.
+__device__ __forceinline__ float as_f32(unsigned int x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ unsigned int as_u32(float x) { return __builtin_bit_cast(unsigned int, x); }
+
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(as_u32(v), r, (int)off, 0, 0);
+}
+
+// phi on two packed bf16: a bf16 with its sign bit set is negative as an
+// int16 as well, so max(x, 0) in int16 arithmetic is the ReLU (-0 -> +0).
+__device__ __forceinline__ unsigned int relu_bf16x2(unsigned int x)
+{
+    i16x2_t v = __builtin_bit_cast(i16x2_t, x);
+    v = __builtin_elementwise_max(v, (i16x2_t){0, 0});
+    return __builtin_bit_cast(unsigned int, v);
+}
+
+__device__ __forceinline__ float bf16lo(unsigned int x) { return as_f32(x << 16); }
+__device__ __forceinline__ float bf16hi(unsigned int x) { return as_f32(x & 0xFFFF0000u); }
+
+// round-to-nearest-even fp32 -> bf16 (the hardware conversion on gfx950)
+__device__ __forceinline__ unsigned short f2bf(float x)
+{
+    return __builtin_bit_cast(unsigned short, (__bf16)x);
+}
+
+__device__ __forceinline__ unsigned int pack_bf16(float lo, float hi)
+{
+    return (unsigned int)f2bf(lo) | ((unsigned int)f2bf(hi) << 16);
+}
+
+// Unsigned division by a divisor fixed per launch (multiply-high method of
+// Granlund and Montgomery): q = (t + ((x - t) >> s1)) >> s2, t = mulhi(x, mul).
+struct FastDiv {
+    uint32_t div, mul, s1, s2;
+};
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv &f)
+{
+    uint32_t t = __umulhi(x, f.mul);
+    return (t + ((x - t) >> f.s1)) >> f.s2;
+}
+
+// ---------------------------------------------------------------------------
+// 3D RoPE: per-workgroup (cos, sin) table in LDS, and the rotation of one
+// thread's 16-byte chunk of features.
+// ---------------------------------------------------------------------------
+struct RopeK {
+    int on;
+    int dt, dh, dw;          // dims per axis (even)
+    int gh, gw;              // latent grid
+    int t0;                  // absolute frame of the call's first token
+    float base;
+    FastDiv div_hw, div_w;   // p / (gh*gw), q / gw
+};
+
+// Table layout: [frames nf x dt/2][rows gh x dh/2][cols gw x dw/2] of float2.
+__device__ __forceinline__ int rope_entries(const RopeK &r, int nf)
+{
+    return nf * (r.dt / 2) + r.gh * (r.dh / 2) + r.gw * (r.dw / 2);
+}
+
+// Angles pos * theta_m with theta_m = base^(-2m/width) are reduced to a
+// fraction of a turn in fp64 before sin/cos, so large frame indices keep
+// their accuracy.
+__device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
+{
+    const int pt = r.dt / 2, ph = r.dh / 2, pw = r.dw / 2;
+    const int nT = nf * pt, nH = r.gh * ph, total = rope_entries(r, nf);
+    for (int e = threadIdx.x; e < total; e += blockDim.x) {
+        int pos, m, width;
+        if (e < nT) {
+            pos = f0 + e / pt; m = e % pt; width = r.dt;
+        } else if (e < nT + nH) {
+            int x = e - nT; pos = x / ph; m = x % ph; width = r.dh;
+        } else {
+            int x = e - nT - nH; pos = x / pw; m = x % pw; width = r.dw;
+        }
+        double theta = pow((double)r.base, -2.0 * (double)m / (double)width);
+        double turns = (double)pos * theta * (0.5 / M_PI);
+        turns -= floor(turns);
+        double s, c;
+        sincospi(2.0 * turns, &s, &c);
+        tab[e] = make_float2((float)c, (float)s);
+    }
+}
+
+// Per-thread description of the 4 (bf16 chunk) or 2 (fp32 chunk) pairs of
+// its fixed feature chunk: which axis each pair rotates with and where its
+// table column starts.
+template <int PAIRS>
+struct RopePairs {
+    int sel[PAIRS];      // 0 frame, 1 row, 2 col, 3 none
+    int base[PAIRS];     // table index of position 0 for this pair
+    int stride[PAIRS];   // table entries per position on that axis
+};
+
+template <int PAIRS>
+__device__ __forceinline__ RopePairs<PAIRS> rope_pairs(const RopeK &r, int first_feature, int nf)
+{
+    RopePairs<PAIRS> p;
+    const int pt = r.dt / 2, ph = r.dh / 2, pw = r.dw / 2;
+    const int offH = nf * pt, offW = offH + r.gh * ph;
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+        int f = first_feature + 2 * j;
+        if (f < r.dt) {
+            p.sel[j] = 0; p.base[j] = f / 2; p.stride[j] = pt;
+        } else if (f < r.dt + r.dh) {
+            p.sel[j] = 1; p.base[j] = offH + (f - r.dt) / 2; p.stride[j] = ph;
+        } else if (f < r.dt + r.dh + r.dw) {
+            p.sel[j] = 2; p.base[j] = offW + (f - r.dt - r.dh) / 2; p.stride[j] = pw;
+        } else {
+            p.sel[j] = 3; p.base[j] = 0; p.stride[j] = 0;
+        }
+    }
+    return p;
+}
+
+// Rotate x[2j], x[2j+1] of token p (call position) by its angles;
+// frame_lo = p_lo / (gh*gw) of the table's first frame.
+template <int PAIRS>
+__device__ __forceinline__ void rope_rotate(float *x, uint32_t p, uint32_t frame_lo,
+                                            const RopeK &r, const RopePairs<PAIRS> &pp,
+                                            const float2 *tab)
+{
+    uint32_t fr = fdiv(p, r.div_hw);
+    uint32_t rem = p - fr * (uint32_t)(r.gh * r.gw);
+    uint32_t row = fdiv(rem, r.div_w);
+    uint32_t col = rem - row * (uint32_t)r.gw;
+    int pos[4] = {(int)(fr - frame_lo), (int)row, (int)col, 0};
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+        if (pp.sel[j] == 3) continue;
+        float2 cs = tab[pp.base[j] + pos[pp.sel[j]] * pp.stride[j]];
+        float x0 = x[2 * j], x1 = x[2 * j + 1];
+        x[2 * j] = x0 * cs.x - x1 * cs.y;
+        x[2 * j + 1] = x0 * cs.y + x1 * cs.x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// kernel arguments
+// ---------------------------------------------------------------------------
+struct BuildArgs {
+    const void *K, *V;
+    float *S_part, *z_part;      // [BH*nb*splits][d*d], [BH*nb*splits][d]
+    int N, n, nb, splits, chunk; // chunk: tokens per split (multiple of the stage)
+    RopeK rope;
+};
+
+struct ScanArgs {
+    const float *S_part, *z_part;  // split partials (or local states, or prefix states)
+    const float *g;                // [BH][nb] or null
+    const float *S_in, *z_in;      // state entering block 0, or null
+    void *S_op;                    // packed operand [BH*nb][d*d] (bf16 or fp32)
+    float *z_pre;                  // [BH*nb][d]
+    float *S_pre;                  // fp32 prefix states [BH*nb][d*d] (export mode)
+    float *S_fin, *z_fin;          // final state or null
+    int nb, splits;
+};
+
+struct ApplyArgs {
+    const void *Q;
+    void *O;
+    const void *S_op;              // packed operand [BH*nb][d*d]
+    const float *z_pre;            // [BH*nb][d]
+    int N, n, nb, tile, tiles;     // tile: tokens per workgroup; tiles per block
+    float eps;
+    RopeK rope;
+};
+
+enum ScanMode { SCAN_FUSED = 0, SCAN_EXPORT = 1, SCAN_PACK = 2 };
+
+// ---------------------------------------------------------------------------
+// svla_state_build, bf16 inputs.
+//
+// Workgroup = (bh, block c, split s); it walks its token range in stages of
+// TT tokens.  Per stage every thread loads one 16-byte chunk of K and of V
+// (8 features of one token), applies phi to K, adds phi(k) to its running z,
+// and writes both chunks to LDS rows.  The MFMA v_mfma_f32_32x32x16_bf16
+// contracts over tokens, so each lane gathers 8 tokens of one feature from
+// the staged rows.  Which token feeds which k-slot does not matter for a
+// sum over tokens, as long as A and B use the same assignment; lanes 32-63
+// take the odd tokens so the two half-waves hit disjoint LDS banks.
+//   d = 32 : one 32x32 output tile; the 4 waves split the stage's tokens and
+//            their accumulators are summed through LDS at the end.
+//   d = 64 : 2x2 tiles, one per wave, every wave sees every token.
+//   d = 128: 4x4 tiles, 2x2 per wave.
+// With RoPE the rotated phi(k) is split into bf16 hi + lo parts, two MFMAs,
+// so the state keeps ~16 bits of the rotated key.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz16(int t, int chunk)
+{
+    // rows of d >= 64 span every LDS bank: odd rows swap chunk halves so
+    // the two half-waves (even/odd tokens) read disjoint banks.
+    return (D >= 64) ? (chunk ^ ((t & 1) << 2)) : chunk;
+}
+
+template <int D, bool ROPE>
+__global__ void __launch_bounds__(kThreads)
+svla_state_build_bf16(const BuildArgs a)
+{
+    constexpr int CPR = D / 8;            // 16-byte chunks per token row
+    constexpr int TT = kThreads / CPR;    // tokens per stage
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = TT * ROWB;      // 4096 bytes
+    constexpr int NK = ROPE ? 2 : 1;
+    constexpr int STAGEB = (NK + 1) * TILEB;
+    constexpr bool SPLITK = (D == 32);
+    constexpr int TPW = SPLITK ? 1 : D / 64;
+    constexpr int GPS = TT / 16;          // 16-token groups per stage
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = blockIdx.x % a.splits;
+    const int c = (blockIdx.x / a.splits) % a.nb;
+    const long bh = blockIdx.x / ((long)a.splits * a.nb);
+    const int tok_lo = c * a.n + s * a.chunk;
+    const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
+
+    const uint32_t slice = (uint32_t)a.N * D * 2;
+    const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
+    const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
+
+    // RoPE table (lives before the stage buffers)
+    float2 *tab = (float2 *)lds;
+    uint32_t frame_lo = 0;
+    RopePairs<4> pp;
+    const int row = tid / CPR, q = tid % CPR;
+    if constexpr (ROPE) {
+        frame_lo = tok_lo < tok_hi ? fdiv((uint32_t)tok_lo, a.rope.div_hw) : 0;
+        uint32_t frame_hi = tok_lo < tok_hi ? fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw) : 0;
+        int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+        pp = rope_pairs<4>(a.rope, q * 8, nf);
+        __syncthreads();
+    }
+    unsigned char *stage = lds + (ROPE ? ((kMaxRopeEntries * 8)) : 0);
+
+    float zacc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
+
+    f32x16_t acc[TPW][TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int ntiles = tok_hi > tok_lo ? (tok_hi - tok_lo + TT - 1) / TT : 0;
+    int tok = tok_lo + row;
+    uint32_t off = tok < tok_hi ? (uint32_t)(tok * D + q * 8) * 2u : kOOB;
+    u32x4_t kreg = load16(rK, off);
+    u32x4_t vreg = load16(rV, off);
+
+    const int m = lane & 31, g = lane >> 5;
+    const int mt0 = SPLITK ? 0 : (wave >> 1) * TPW;
+    const int nt0 = SPLITK ? 0 : (wave & 1) * TPW;
+
+    for (int it = 0; it < ntiles; ++it) {
+        unsigned char *st = stage + (it & 1) * STAGEB;
+        // phi(k), z, (rotation), stage to LDS
+        u32x4_t kr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kr[e] = relu_bf16x2(kreg[e]);
+        float kf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kf[2 * e] = bf16lo(kr[e]);
+            kf[2 * e + 1] = bf16hi(kr[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
+        const int cpos = swz16<D>(row, q);
+        if constexpr (ROPE) {
+            rope_rotate<4>(kf, (uint32_t)tok, frame_lo, a.rope, pp, tab);
+            u32x4_t hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                unsigned short h0 = f2bf(kf[2 * e]), h1 = f2bf(kf[2 * e + 1]);
+                float r0 = kf[2 * e] - as_f32((unsigned int)h0 << 16);
+                float r1 = kf[2 * e + 1] - as_f32((unsigned int)h1 << 16);
+                hi[e] = (unsigned int)h0 | ((unsigned int)h1 << 16);
+                lo[e] = pack_bf16(r0, r1);
+            }
+            *(u32x4_t *)(st + row * ROWB + cpos * 16) = hi;
+            *(u32x4_t *)(st + TILEB + row * ROWB + cpos * 16) = lo;
+        } else {
+            *(u32x4_t *)(st + row * ROWB + cpos * 16) = kr;
+        }
+        *(u32x4_t *)(st + NK * TILEB + row * ROWB + cpos * 16) = vreg;
+        __syncthreads();
+
+        // next stage's loads fly while this stage is contracted
+        if (it + 1 < ntiles) {
+            tok += TT;
+            off = tok < tok_hi ? (uint32_t)(tok * D + q * 8) * 2u : kOOB;
+            kreg = load16(rK, off);
+            vreg = load16(rV, off);
+        }
+
+        const unsigned short *Kh = (const unsigned short *)st;
+        const unsigned short *Kl = (const unsigned short *)(st + TILEB);
+        const unsigned short *Vs = (const unsigned short *)(st + NK * TILEB);
+#pragma unroll
+        for (int gi = 0; gi < GPS; ++gi) {
+            if (SPLITK && gi != wave) continue;
+            int t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t[i] = 16 * gi + 2 * i + g;
+            bf16x8_t av[TPW], al[TPW], bv[TPW];
+#pragma unroll
+            for (int tm = 0; tm < TPW; ++tm) {
+                const int f = 32 * (mt0 + tm) + m;
+                u16x8_t x, y;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int idx = t[i] * D + swz16<D>(t[i], f >> 3) * 8 + (f & 7);
+                    x[i] = Kh[idx];
+                    if constexpr (ROPE) y[i] = Kl[idx];
+                }
+                av[tm] = __builtin_bit_cast(bf16x8_t, x);
+                if constexpr (ROPE) al[tm] = __builtin_bit_cast(bf16x8_t, y);
+            }
+#pragma unroll
+            for (int tn = 0; tn < TPW; ++tn) {
+                const int f = 32 * (nt0 + tn) + m;
+                u16x8_t x;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    x[i] = Vs[t[i] * D + swz16<D>(t[i], f >> 3) * 8 + (f & 7)];
+                bv[tn] = __builtin_bit_cast(bf16x8_t, x);
+            }
+#pragma unroll
+            for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TPW; ++tn) {
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+                    if constexpr (ROPE)
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+                }
+        }
+    }
+    __syncthreads();   // every wave is done with the stage buffers
+
+    // ---- epilogue: write S_part (row-major [k][v]) and z_part
+    const long unit = (bh * a.nb + c) * a.splits + s;
+    const auto rS = make_rsrc(a.S_part + unit * D * D, D * D * 4);
+    const auto rz = make_rsrc(a.z_part + unit * D, D * 4);
+    float *red = (float *)stage;
+    float *zred = (float *)(stage + (SPLITK ? 4 * 16 * 64 * 4 : 0));
+    if constexpr (SPLITK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[0][0][r];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zred[tid * 8 + e] = zacc[e];
+    __syncthreads();
+    if constexpr (SPLITK) {
+        // thread -> 4 consecutive columns of one row; fixed summation order
+        const int e0 = tid * 4, rr = e0 / 32, c0 = e0 % 32;
+        u32x4_t out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ln = (c0 + j) + 32 * ((rr >> 2) & 1);
+            const int r = 4 * (rr >> 3) + (rr & 3);
+            float v = red[(0 * 16 + r) * 64 + ln];
+            v += red[(1 * 16 + r) * 64 + ln];
+            v += red[(2 * 16 + r) * 64 + ln];
+            v += red[(3 * 16 + r) * 64 + ln];
+            out[j] = as_u32(v);
+        }
+        store16(rS, (uint32_t)(rr * D + c0) * 4u, out);
+    } else {
+#pragma unroll
+        for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TPW; ++tn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = 32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const int cc = 32 * (nt0 + tn) + m;
+                    store4(rS, (uint32_t)(rr * D + cc) * 4u, acc[tm][tn][r]);
+                }
+    }
+    if (tid < D) {
+        const int qq = tid >> 3, e = tid & 7;
+        float v = 0.f;
+        for (int j = 0; j < kThreads / CPR; ++j) v += zred[(qq + CPR * j) * 8 + e];
+        store4(rz, (uint32_t)tid * 4u, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// svla_state_build, fp32 inputs: the same walk with fp32 rows staged and
+// v_mfma_f32_32x32x2_f32 (one token per half-wave per instruction).
+// ---------------------------------------------------------------------------
+template <int D, bool ROPE>
+__global__ void __launch_bounds__(kThreads)
+svla_state_build_f32(const BuildArgs a)
+{
+    constexpr int CPR = D / 4;            // 16-byte chunks (4 floats) per row
+    constexpr int TT = kThreads / CPR;    // 32, 16, 8 tokens per stage
+    constexpr int ROWB = D * 4;
+    constexpr int TILEB = TT * ROWB;      // 4096
+    constexpr int STAGEB = 2 * TILEB;
+    constexpr bool SPLITK = (D == 32);
+    constexpr int TPW = SPLITK ? 1 : D / 64;
+    constexpr int PPS = TT / 2;           // token pairs per stage
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int s = blockIdx.x % a.splits;
+    const int c = (blockIdx.x / a.splits) % a.nb;
+    const long bh = blockIdx.x / ((long)a.splits * a.nb);
+    const int tok_lo = c * a.n + s * a.chunk;
+    const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
+
+    const uint32_t slice = (uint32_t)a.N * D * 4;
+    const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
+    const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
+
+    float2 *tab = (float2 *)lds;
+    uint32_t frame_lo = 0;
+    RopePairs<2> pp;
+    const int row = tid / CPR, q = tid % CPR;
+    if constexpr (ROPE) {
+        frame_lo = tok_lo < tok_hi ? fdiv((uint32_t)tok_lo, a.rope.div_hw) : 0;
+        uint32_t frame_hi = tok_lo < tok_hi ? fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw) : 0;
+        int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+        pp = rope_pairs<2>(a.rope, q * 4, nf);
+        __syncthreads();
+    }
+    unsigned char *stage = lds + (ROPE ? kMaxRopeEntries * 8 : 0);
+
+    float zacc[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x16_t acc[TPW][TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int ntiles = tok_hi > tok_lo ? (tok_hi - tok_lo + TT - 1) / TT : 0;
+    int tok = tok_lo + row;
+    uint32_t off = tok < tok_hi ? (uint32_t)(tok * D + q * 4) * 4u : kOOB;
+    u32x4_t kreg = load16(rK, off);
+    u32x4_t vreg = load16(rV, off);
+    const int m = lane & 31, g = lane >> 5;
+    const int mt0 = SPLITK ? 0 : (wave >> 1) * TPW;
+    const int nt0 = SPLITK ? 0 : (wave & 1) * TPW;
+
+    for (int it = 0; it < ntiles; ++it) {
+        unsigned char *st = stage + (it & 1) * STAGEB;
+        float kf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kf[e] = fmaxf(as_f32(kreg[e]), 0.f);
+            zacc[e] += kf[e];
+        }
+        if constexpr (ROPE) rope_rotate<2>(kf, (uint32_t)tok, frame_lo, a.rope, pp, tab);
+        u32x4_t kw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kw[e] = as_u32(kf[e]);
+        *(u32x4_t *)(st + row * ROWB + q * 16) = kw;
+        *(u32x4_t *)(st + TILEB + row * ROWB + q * 16) = vreg;
+        __syncthreads();
+        if (it + 1 < ntiles) {
+            tok += TT;
+            off = tok < tok_hi ? (uint32_t)(tok * D + q * 4) * 4u : kOOB;
+            kreg = load16(rK, off);
+            vreg = load16(rV, off);
+        }
+        const float *Ks = (const float *)st;
+        const float *Vs = (const float *)(st + TILEB);
+        constexpr int PPW = SPLITK ? PPS / 4 : PPS;     // pairs per wave
+        const int p0 = SPLITK ? wave * PPW : 0;
+#pragma unroll
+        for (int pi = 0; pi < PPW; ++pi) {
+            const int t = 2 * (p0 + pi) + g;
+            float av[TPW], bv[TPW];
+#pragma unroll
+            for (int tm = 0; tm < TPW; ++tm) av[tm] = Ks[t * D + 32 * (mt0 + tm) + m];
+#pragma unroll
+            for (int tn = 0; tn < TPW; ++tn) bv[tn] = Vs[t * D + 32 * (nt0 + tn) + m];
+#pragma unroll
+            for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TPW; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+
+    const long unit = (bh * a.nb + c) * a.splits + s;
+    const auto rS = make_rsrc(a.S_part + unit * D * D, D * D * 4);
+    const auto rz = make_rsrc(a.z_part + unit * D, D * 4);
+    float *red = (float *)stage;
+    float *zred = (float *)(stage + (SPLITK ? 4 * 16 * 64 * 4 : 0));
+    if constexpr (SPLITK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[0][0][r];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) zred[tid * 4 + e] = zacc[e];
+    __syncthreads();
+    if constexpr (SPLITK) {
+        const int e0 = tid * 4, rr = e0 / 32, c0 = e0 % 32;
+        u32x4_t out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ln = (c0 + j) + 32 * ((rr >> 2) & 1);
+            const int r = 4 * (rr >> 3) + (rr & 3);
+            float v = red[(0 * 16 + r) * 64 + ln];
+            v += red[(1 * 16 + r) * 64 + ln];
+            v += red[(2 * 16 + r) * 64 + ln];
+            v += red[(3 * 16 + r) * 64 + ln];
+            out[j] = as_u32(v);
+        }
+        store16(rS, (uint32_t)(rr * D + c0) * 4u, out);
+    } else {
+#pragma unroll
+        for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TPW; ++tn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = 32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const int cc = 32 * (nt0 + tn) + m;
+                    store4(rS, (uint32_t)(rr * D + cc) * 4u, acc[tm][tn][r]);
+                }
+    }
+    if (tid < D) {
+        const int qq = tid >> 2, e = tid & 3;
+        float v = 0.f;
+        for (int j = 0; j < kThreads / CPR; ++j) v += zred[(qq + CPR * j) * 4 + e];
+        store4(rz, (uint32_t)tid * 4u, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// svla_state_scan.  Workgroup = (bh, 1024-element tile of S) or (bh, z).
+// Each thread owns 4 consecutive elements of S[k][v] and walks the blocks in
+// order: acc = g_c * acc + sum over splits, so the summation order is fixed
+// and the result repeats bit for bit.
+//
+// Packed operand layout read by svla_apply (per (bh, block), d*d entries):
+// bf16: fragment (m, ks) = 64 lanes x 8 values; lane (rho + 16 kg), value i
+//       holds S[32 ks + 8 kg + i][f(m, rho)]
+// fp32: fragment (m, kq) = 64 lanes x 4 values; lane (rho + 16 kg), value i
+//       holds S[16 kq + 4 kg + i][f(m, rho)]
+// with f(m, rho) = (d/4) (rho / 4) + 4 m + rho % 4: the output rows of the
+// MFMA land so that each lane ends up with consecutive O features.
+// ---------------------------------------------------------------------------
+template <int D, int MODE, bool OPBF16>
+__global__ void __launch_bounds__(kThreads)
+svla_state_scan_k(const ScanArgs a)
+{
+    constexpr int STILES = D * D / 1024;
+    const int tid = threadIdx.x;
+    const long bh = blockIdx.x / (STILES + 1);
+    const int tile = blockIdx.x % (STILES + 1);
+
+    if (tile < STILES) {
+        const int e0 = tile * 1024 + tid * 4;
+        const int k = e0 / D, v = e0 % D;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (MODE != SCAN_PACK && a.S_in) acc = *(const f32x4_t *)(a.S_in + bh * D * D + e0);
+        // operand positions of the 4 elements (k, v..v+3)
+        constexpr int MT = D / 16;
+        const int m = (v % (D / 4)) / 4, rho0 = 4 * (v / (D / 4));
+        int opos[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (OPBF16) {
+                const int ks = k / 32, kg = (k % 32) / 8, i = k % 8;
+                opos[j] = (((m * (D / 32) + ks) * 64 + rho0 + j + 16 * kg) * 8 + i);
+            } else {
+                const int kq = k / 16, kg = (k % 16) / 4, i = k % 4;
+                opos[j] = (((m * (D / 16) + kq) * 64 + rho0 + j + 16 * kg) * 4 + i);
+            }
+        }
+        (void)MT;
+        for (int c = 0; c < a.nb; ++c) {
+            const long unit = bh * a.nb + c;
+            if (MODE == SCAN_PACK) {
+                acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            } else if (a.g) {
+                const float gm = a.g[unit];
+                acc *= gm;
+            }
+            for (int sp = 0; sp < a.splits; ++sp)
+                acc += *(const f32x4_t *)(a.S_part + (unit * a.splits + sp) * D * D + e0);
+            if (MODE == SCAN_EXPORT) {
+                *(f32x4_t *)(a.S_pre + unit * D * D + e0) = acc;
+            } else {
+                if constexpr (OPBF16) {
+                    unsigned short *op = (unsigned short *)a.S_op + unit * D * D;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) op[opos[j]] = f2bf(acc[j]);
+                } else {
+                    float *op = (float *)a.S_op + unit * D * D;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) op[opos[j]] = acc[j];
+                }
+            }
+        }
+        if (MODE != SCAN_PACK && a.S_fin) *(f32x4_t *)(a.S_fin + bh * D * D + e0) = acc;
+    } else if (MODE != SCAN_PACK) {
+        if (tid >= D / 4) return;
+        const int e0 = tid * 4;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (a.z_in) acc = *(const f32x4_t *)(a.z_in + bh * D + e0);
+        for (int c = 0; c < a.nb; ++c) {
+            const long unit = bh * a.nb + c;
+            if (a.g) acc *= a.g[unit];
+            for (int sp = 0; sp < a.splits; ++sp)
+                acc += *(const f32x4_t *)(a.z_part + (unit * a.splits + sp) * D + e0);
+            *(f32x4_t *)(a.z_pre + unit * D + e0) = acc;
+        }
+        if (a.z_fin) *(f32x4_t *)(a.z_fin + bh * D + e0) = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// svla_apply, bf16 inputs.  Workgroup = (bh, block c, token tile).
+// O^T = S^T phi~(Q)^T on v_mfma_f32_16x16x32_bf16: the state is the A
+// operand (kept in registers for the whole tile, loaded once from the
+// packed layout), phi~(q) the B operand straight from a 16-byte load per
+// lane (token = lane % 16, 8 features of chunk 4 ks + lane / 16).  The
+// denominator phi(q) . z is a per-lane partial dot product reduced over the
+// 4 lanes that share a token.
+//   d = 32, 64: each wave takes every 4th 16-token group, all output features.
+//   d = 128   : every wave takes every group, for its own 32 output features.
+// ---------------------------------------------------------------------------
+template <int D, bool ROPE>
+__global__ void __launch_bounds__(kThreads)
+svla_apply_bf16(const ApplyArgs a)
+{
+    constexpr int MT = D / 16;
+    constexpr int KS = D / 32;
+    constexpr bool SPLITM = (D == 128);
+    constexpr int MW = SPLITM ? 2 : MT;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tile = blockIdx.x % a.tiles;
+    const int c = (blockIdx.x / a.tiles) % a.nb;
+    const long bh = blockIdx.x / ((long)a.tiles * a.nb);
+    const int t_lo = c * a.n + tile * a.tile;
+    const int t_hi = min(t_lo + a.tile, (c + 1) * a.n);
+    const long unit = bh * a.nb + c;
+
+    const uint32_t slice = (uint32_t)a.N * D * 2;
+    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
+    const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
+    const auto rS = make_rsrc((const char *)a.S_op + unit * D * D * 2, D * D * 2);
+    const auto rz = make_rsrc(a.z_pre + unit * D, D * 4);
+
+    const int kg = lane >> 4, tl = lane & 15;
+    const int m0 = SPLITM ? 2 * wave : 0;
+
+    bf16x8_t sf[MW][KS];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            sf[mi][ks] = __builtin_bit_cast(bf16x8_t,
+                load16(rS, (uint32_t)((((m0 + mi) * KS + ks) * 64 + lane) * 16)));
+    float zf[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t z0 = load16(rz, (uint32_t)(8 * (4 * ks + kg)) * 4u);
+        u32x4_t z1 = load16(rz, (uint32_t)(8 * (4 * ks + kg) + 4) * 4u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            zf[ks][e] = as_f32(z0[e]);
+            zf[ks][4 + e] = as_f32(z1[e]);
+        }
+    }
+
+    float2 *tab = (float2 *)lds;
+    uint32_t frame_lo = 0;
+    RopePairs<4> pp[KS];
+    if constexpr (ROPE) {
+        frame_lo = t_lo < t_hi ? fdiv((uint32_t)t_lo, a.rope.div_hw) : 0;
+        uint32_t frame_hi = t_lo < t_hi ? fdiv((uint32_t)(t_hi - 1), a.rope.div_hw) : 0;
+        int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pp[ks] = rope_pairs<4>(a.rope, 8 * (4 * ks + kg), nf);
+        __syncthreads();
+    }
+
+    const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
+    const int g_first = SPLITM ? 0 : wave, g_step = SPLITM ? 1 : 4;
+    for (int gi = g_first; gi < ngroups; gi += g_step) {
+        const int tok = t_lo + 16 * gi + tl;
+        const bool valid = tok < t_hi;
+        u32x4_t qr[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qr[ks] = load16(rQ, valid ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB);
+        float den = 0.f;
+        bf16x8_t qf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4_t p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = relu_bf16x2(qr[ks][e]);
+            float pf[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pf[2 * e] = bf16lo(p[e]);
+                pf[2 * e + 1] = bf16hi(p[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) den = fmaf(pf[e], zf[ks][e], den);
+            if constexpr (ROPE) {
+                rope_rotate<4>(pf, (uint32_t)tok, frame_lo, a.rope, pp[ks], tab);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
+            }
+            qf[ks] = __builtin_bit_cast(bf16x8_t, p);
+        }
+        den += __shfl_xor(den, 16);
+        den += __shfl_xor(den, 32);
+        den += a.eps;
+        const float inv = den != 0.f ? 1.0f / den : 0.f;
+
+        f32x4_t acc[MW];
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi) {
+            acc[mi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mi][ks], qf[ks], acc[mi], 0, 0, 0);
+        }
+        // lane holds O[tok][4 MT kg + 4 (m0 + mi) + r], consecutive in (mi, r)
+#pragma unroll
+        for (int h = 0; h < MW / 2; ++h) {
+            u32x4_t o;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                o[2 * e] = pack_bf16(acc[2 * h + e][0] * inv, acc[2 * h + e][1] * inv);
+                o[2 * e + 1] = pack_bf16(acc[2 * h + e][2] * inv, acc[2 * h + e][3] * inv);
+            }
+            const int v0 = 4 * MT * kg + 4 * (m0 + 2 * h);
+            store16(rO, valid ? (uint32_t)(tok * D + v0) * 2u : kOOB, o);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// svla_apply, fp32 inputs: v_mfma_f32_16x16x4_f32, lane chunk = 4 features
+// of chunk 4 kq + lane / 16; the state operand stays fp32.
+// ---------------------------------------------------------------------------
+template <int D, bool ROPE>
+__global__ void __launch_bounds__(kThreads)
+svla_apply_f32(const ApplyArgs a)
+{
+    constexpr int MT = D / 16;
+    constexpr int KQ = D / 16;
+    constexpr bool SPLITM = (D == 128);
+    constexpr int MW = SPLITM ? 2 : MT;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tile = blockIdx.x % a.tiles;
+    const int c = (blockIdx.x / a.tiles) % a.nb;
+    const long bh = blockIdx.x / ((long)a.tiles * a.nb);
+    const int t_lo = c * a.n + tile * a.tile;
+    const int t_hi = min(t_lo + a.tile, (c + 1) * a.n);
+    const long unit = bh * a.nb + c;
+
+    const uint32_t slice = (uint32_t)a.N * D * 4;
+    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
+    const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
+    const auto rS = make_rsrc((const char *)a.S_op + unit * D * D * 4, D * D * 4);
+    const auto rz = make_rsrc(a.z_pre + unit * D, D * 4);
+
+    const int kg = lane >> 4, tl = lane & 15;
+    const int m0 = SPLITM ? 2 * wave : 0;
+
+    f32x4_t sf[MW][KQ];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq)
+            sf[mi][kq] = __builtin_bit_cast(f32x4_t,
+                load16(rS, (uint32_t)((((m0 + mi) * KQ + kq) * 64 + lane) * 16)));
+    f32x4_t zf[KQ];
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq)
+        zf[kq] = __builtin_bit_cast(f32x4_t, load16(rz, (uint32_t)(4 * (4 * kq + kg)) * 4u));
+
+    float2 *tab = (float2 *)lds;
+    uint32_t frame_lo = 0;
+    RopePairs<2> pp[KQ];
+    if constexpr (ROPE) {
+        frame_lo = t_lo < t_hi ? fdiv((uint32_t)t_lo, a.rope.div_hw) : 0;
+        uint32_t frame_hi = t_lo < t_hi ? fdiv((uint32_t)(t_hi - 1), a.rope.div_hw) : 0;
+        int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) pp[kq] = rope_pairs<2>(a.rope, 4 * (4 * kq + kg), nf);
+        __syncthreads();
+    }
+
+    const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
+    const int g_first = SPLITM ? 0 : wave, g_step = SPLITM ? 1 : 4;
+    for (int gi = g_first; gi < ngroups; gi += g_step) {
+        const int tok = t_lo + 16 * gi + tl;
+        const bool valid = tok < t_hi;
+        float qv[KQ][4];
+        float den = 0.f;
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) {
+            u32x4_t r = load16(rQ, valid ? (uint32_t)(tok * D + 4 * (4 * kq + kg)) * 4u : kOOB);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qv[kq][e] = fmaxf(as_f32(r[e]), 0.f);
+                den = fmaf(qv[kq][e], zf[kq][e], den);
+            }
+            if constexpr (ROPE) rope_rotate<2>(qv[kq], (uint32_t)tok, frame_lo, a.rope, pp[kq], tab);
+        }
+        den += __shfl_xor(den, 16);
+        den += __shfl_xor(den, 32);
+        den += a.eps;
+        const float inv = den != 0.f ? 1.0f / den : 0.f;
+        f32x4_t acc[MW];
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi) {
+            acc[mi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(sf[mi][kq][i], qv[kq][i], acc[mi], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi) {
+            u32x4_t o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = as_u32(acc[mi][r] * inv);
+            const int v0 = 4 * MT * kg + 4 * (m0 + mi);
+            store16(rO, valid ? (uint32_t)(tok * D + v0) * 4u : kOOB, o);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+thread_local char g_err[512] = "";
+
+svla_status fail(svla_status s, const char *fn, const char *fmt, ...) __attribute__((format(printf, 3, 4)));
+svla_status fail(svla_status s, const char *fn, const char *fmt, ...)
+{
+    char msg[400];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, sizeof msg, fmt, ap);
+    va_end(ap);
+    snprintf(g_err, sizeof g_err, "%s: %s", fn, msg);
+    return s;
+}
+
+FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.div = d;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;                  // l = ceil(log2 d)
+    f.mul = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    f.s1 = l ? 1 : 0;
+    f.s2 = l ? l - 1 : 0;
+    return f;
+}
+
+struct Plan {
+    int B, H, nb, n, d;
+    long BH;
+    int esize;                 // bytes per Q/K/V/O element
+    int splits, chunk;         // build
+    int tile, tiles;           // apply
+    size_t lds_build, lds_apply;
+    size_t off_spart, off_zpart, off_sop, off_zpre, total;
+    RopeK rope;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int stage_tokens(int d, int esize) { return kThreads / (d * esize / 16); }
+
+// Splits of a block's tokens over workgroups: enough workgroups to fill the
+// chip (about 2048), but never fewer than 8*d tokens per split, so the fp32
+// partial state (4 d^2 bytes) stays under 1/8 of the K/V bytes it summarises.
+int pick_splits(long units, int n, int d, int TT, int *chunk_out)
+{
+    if (n <= 0 || units <= 0) { *chunk_out = TT; return 0; }
+    long want = (2048 + units - 1) / units;
+    long cap = n / (8 * d);
+    if (cap < 1) cap = 1;
+    long s = want < cap ? want : cap;
+    if (s < 1) s = 1;
+    int chunk = (int)((n + s - 1) / s);
+    chunk = (chunk + TT - 1) / TT * TT;
+    *chunk_out = chunk;
+    return (n + chunk - 1) / chunk;
+}
+
+int frames_spanned_max(int tokens, int hw) { return tokens <= 0 ? 1 : (tokens - 1) / hw + 2; }
+
+svla_status check_rope(const char *fn, const svla_rope *r, int d, RopeK *out)
+{
+    memset(out, 0, sizeof *out);
+    if (!r) return SVLA_OK;
+    if (r->dt_dims < 0 || r->dh_dims < 0 || r->dw_dims < 0 || (r->dt_dims & 1) ||
+        (r->dh_dims & 1) || (r->dw_dims & 1))
+        return fail(SVLA_ERR_VALUE, fn, "rope dims must be even and >= 0 (got %d/%d/%d)",
+                    r->dt_dims, r->dh_dims, r->dw_dims);
+    if (r->dt_dims + r->dh_dims + r->dw_dims > d)
+        return fail(SVLA_ERR_VALUE, fn, "rope dims %d+%d+%d exceed d=%d", r->dt_dims,
+                    r->dh_dims, r->dw_dims, d);
+    if (r->grid_h < 1 || r->grid_w < 1 || (long)r->grid_h * r->grid_w > (1L << 30))
+        return fail(SVLA_ERR_VALUE, fn, "rope grid %dx%d invalid", r->grid_h, r->grid_w);
+    if (r->t0 < 0) return fail(SVLA_ERR_VALUE, fn, "rope t0 must be >= 0 (got %d)", r->t0);
+    if (!(r->base > 0.f) || !isfinite(r->base))
+        return fail(SVLA_ERR_VALUE, fn, "rope base must be finite and > 0");
+    out->on = 1;
+    out->dt = r->dt_dims; out->dh = r->dh_dims; out->dw = r->dw_dims;
+    out->gh = r->grid_h; out->gw = r->grid_w; out->t0 = r->t0; out->base = r->base;
+    out->div_hw = make_fastdiv((uint32_t)(r->grid_h * r->grid_w));
+    out->div_w = make_fastdiv((uint32_t)r->grid_w);
+    return SVLA_OK;
+}
+
+svla_status check_sizes(const char *fn, svla_dtype dt, int B, int H, int nb, int n, int d)
+{
+    if (dt != SVLA_F32 && dt != SVLA_BF16)
+        return fail(SVLA_ERR_DTYPE, fn, "dtype %d is not SVLA_F32 or SVLA_BF16", (int)dt);
+    if (B < 0 || H < 0 || nb < 0 || n < 0)
+        return fail(SVLA_ERR_SHAPE, fn, "negative size (B=%d H=%d nb=%d n=%d)", B, H, nb, n);
+    if (d != 32 && d != 64 && d != 128)
+        return fail(SVLA_ERR_UNSUPPORTED, fn, "d=%d not in {32, 64, 128}", d);
+    const int es = dt == SVLA_BF16 ? 2 : 4;
+    if ((long long)nb * n * d * es >= (1LL << 31))
+        return fail(SVLA_ERR_SHAPE, fn, "one (b,h) slice of %lld tokens x d=%d exceeds 2 GiB",
+                    (long long)nb * n, d);
+    if ((long long)B * H * nb >= (1LL << 31) / 64)
+        return fail(SVLA_ERR_SHAPE, fn, "B*H*nb=%lld too large", (long long)B * H * nb);
+    return SVLA_OK;
+}
+
+svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, int nb, int n,
+                      int d, const svla_rope *rope, Plan *p)
+{
+    svla_status st = check_sizes(fn, dt, B, H, nb, n, d);
+    if (st) return st;
+    memset(p, 0, sizeof *p);
+    p->B = B; p->H = H; p->nb = nb; p->n = n; p->d = d;
+    p->BH = (long)B * H;
+    p->esize = dt == SVLA_BF16 ? 2 : 4;
+    st = check_rope(fn, rope, d, &p->rope);
+    if (st) return st;
+    const int TT = stage_tokens(d, p->esize);
+    if (op == SVLA_OP_STATE_BUILD) {
+        p->splits = n > 0 ? 1 : 0;
+        p->chunk = (n + TT - 1) / TT * TT;
+        if (p->chunk == 0) p->chunk = TT;
+    } else {
+        p->splits = pick_splits(p->BH * nb, n, d, TT, &p->chunk);
+    }
+    p->tile = d == 128 ? 128 : 256;
+    p->tiles = n > 0 ? (n + p->tile - 1) / p->tile : 0;
+
+    // LDS: [RoPE table][stage buffers | epilogue]
+    const size_t stage = (size_t)2 * ((p->esize == 2 && p->rope.on) ? 3 : 2) * 4096;
+    const size_t epi = (d == 32 ? 16384 : 0) + 8192;
+    p->lds_build = stage > epi ? stage : epi;
+    p->lds_apply = 0;
+    if (p->rope.on) {
+        const int hw = p->rope.gh * p->rope.gw;
+        const long eb = (long)frames_spanned_max(p->chunk, hw) * (p->rope.dt / 2) +
+                        (long)p->rope.gh * (p->rope.dh / 2) + (long)p->rope.gw * (p->rope.dw / 2);
+        const long ea = (long)frames_spanned_max(p->tile, hw) * (p->rope.dt / 2) +
+                        (long)p->rope.gh * (p->rope.dh / 2) + (long)p->rope.gw * (p->rope.dw / 2);
+        if (eb > kMaxRopeEntries || ea > kMaxRopeEntries)
+            return fail(SVLA_ERR_UNSUPPORTED, fn,
+                        "RoPE table of %ld entries exceeds %d (grid %dx%d too large)",
+                        eb > ea ? eb : ea, kMaxRopeEntries, p->rope.gh, p->rope.gw);
+        p->lds_build += (size_t)kMaxRopeEntries * 8;
+        p->lds_apply = (size_t)kMaxRopeEntries * 8;
+    }
+
+    // workspace
+    size_t off = 0;
+    const size_t units = (size_t)p->BH * nb;
+    const bool fused = op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP;
+    if (fused) {
+        p->off_spart = off; off = align256(off + units * p->splits * d * d * 4);
+        p->off_zpart = off; off = align256(off + units * p->splits * d * 4);
+    }
+    if (fused || op == SVLA_OP_APPLY) {
+        p->off_sop = off; off = align256(off + units * d * d * p->esize);
+    }
+    if (fused) {
+        p->off_zpre = off; off = align256(off + units * d * 4);
+    }
+    p->total = off;
+    return SVLA_OK;
+}
+
+inline bool misaligned(const void *ptr) { return ((uintptr_t)ptr & 15) != 0; }
+
+// ---- launchers ---------------------------------------------------------------
+
+template <int D>
+void launch_build(const Plan &p, const BuildArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(p.BH * p.nb * p.splits));
+    if (p.esize == 2) {
+        if (p.rope.on) svla_state_build_bf16<D, true><<<grid, kThreads, p.lds_build, s>>>(a);
+        else svla_state_build_bf16<D, false><<<grid, kThreads, p.lds_build, s>>>(a);
+    } else {
+        if (p.rope.on) svla_state_build_f32<D, true><<<grid, kThreads, p.lds_build, s>>>(a);
+        else svla_state_build_f32<D, false><<<grid, kThreads, p.lds_build, s>>>(a);
+    }
+}
+
+template <int D, int MODE>
+void launch_scan_d(const Plan &p, const ScanArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(p.BH * (D * D / 1024 + 1)));
+    if (p.esize == 2) svla_state_scan_k<D, MODE, true><<<grid, kThreads, 0, s>>>(a);
+    else svla_state_scan_k<D, MODE, false><<<grid, kThreads, 0, s>>>(a);
+}
+
+template <int D>
+void launch_apply(const Plan &p, const ApplyArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(p.BH * p.nb * p.tiles));
+    if (p.esize == 2) {
+        if (p.rope.on) svla_apply_bf16<D, true><<<grid, kThreads, p.lds_apply, s>>>(a);
+        else svla_apply_bf16<D, false><<<grid, kThreads, p.lds_apply, s>>>(a);
+    } else {
+        if (p.rope.on) svla_apply_f32<D, true><<<grid, kThreads, p.lds_apply, s>>>(a);
+        else svla_apply_f32<D, false><<<grid, kThreads, p.lds_apply, s>>>(a);
+    }
+}
+
+void build_any(const Plan &p, const BuildArgs &a, hipStream_t s)
+{
+    if (p.d == 32) launch_build<32>(p, a, s);
+    else if (p.d == 64) launch_build<64>(p, a, s);
+    else launch_build<128>(p, a, s);
+}
+
+template <int MODE>
+void scan_any(const Plan &p, const ScanArgs &a, hipStream_t s)
+{
+    if (p.d == 32) launch_scan_d<32, MODE>(p, a, s);
+    else if (p.d == 64) launch_scan_d<64, MODE>(p, a, s);
+    else launch_scan_d<128, MODE>(p, a, s);
+}
+
+void apply_any(const Plan &p, const ApplyArgs &a, hipStream_t s)
+{
+    if (p.d == 32) launch_apply<32>(p, a, s);
+    else if (p.d == 64) launch_apply<64>(p, a, s);
+    else launch_apply<128>(p, a, s);
+}
+
+svla_status check_launch(const char *fn)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SVLA_ERR_HIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+    return SVLA_OK;
+}
+
+// The fused forward shared by the non-causal call, the one-shot block-causal
+// calls and the block steps: build -> scan -> apply on one stream.
+svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int nb, int n,
+                    int d, const void *Q, const void *K, const void *V, void *O,
+                    const float *S0, const float *z0, float *S_fin, float *z_fin,
+                    const float *g, const svla_rope *rope, float eps, void *ws,
+                    size_t ws_bytes, svla_stream stream)
+{
+    Plan p;
+    svla_status st = make_plan(fn, op, dt, B, H, nb, n, d, rope, &p);
+    if (st) return st;
+    if (!(eps >= 0.f) || !isfinite(eps))
+        return fail(SVLA_ERR_VALUE, fn, "eps must be finite and >= 0");
+    if (p.BH == 0) return SVLA_OK;
+    const bool tokens = (long)nb * n > 0;
+    if (tokens && (!Q || !K || !V || !O)) return fail(SVLA_ERR_NULL, fn, "Q, K, V and O are required");
+    if ((S0 == nullptr) != (z0 == nullptr)) return fail(SVLA_ERR_NULL, fn, "pass both S0 and z0, or neither");
+    if ((S_fin == nullptr) != (z_fin == nullptr))
+        return fail(SVLA_ERR_NULL, fn, "pass both final-state outputs, or neither");
+    if (op == SVLA_OP_BLOCK_STEP && !S_fin) return fail(SVLA_ERR_NULL, fn, "S_out and z_out are required");
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(O) || misaligned(S0) ||
+        misaligned(z0) || misaligned(S_fin) || misaligned(z_fin) || misaligned(g) || misaligned(ws))
+        return fail(SVLA_ERR_ALIGN, fn, "device pointers must be 16-byte aligned");
+    if (p.total > 0 && !ws) return fail(SVLA_ERR_NULL, fn, "workspace of %zu bytes required", p.total);
+    if (ws_bytes < p.total)
+        return fail(SVLA_ERR_WORKSPACE, fn, "workspace of %zu bytes is smaller than the %zu needed",
+                    ws_bytes, p.total);
+
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    (void)hipGetLastError();
+    if (p.splits > 0 && nb > 0) {
+        BuildArgs ba;
+        ba.K = K; ba.V = V;
+        ba.S_part = (float *)(w + p.off_spart);
+        ba.z_part = (float *)(w + p.off_zpart);
+        ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = p.splits; ba.chunk = p.chunk;
+        ba.rope = p.rope;
+        build_any(p, ba, s);
+        if ((st = check_launch(fn))) return st;
+    }
+    ScanArgs sa;
+    memset(&sa, 0, sizeof sa);
+    sa.S_part = (const float *)(w + p.off_spart);
+    sa.z_part = (const float *)(w + p.off_zpart);
+    sa.g = g; sa.S_in = S0; sa.z_in = z0;
+    sa.S_op = w + p.off_sop;
+    sa.z_pre = (float *)(w + p.off_zpre);
+    sa.S_fin = S_fin; sa.z_fin = z_fin;
+    sa.nb = nb; sa.splits = p.splits;
+    scan_any<SCAN_FUSED>(p, sa, s);
+    if ((st = check_launch(fn))) return st;
+    if (tokens) {
+        ApplyArgs aa;
+        aa.Q = Q; aa.O = O; aa.S_op = w + p.off_sop; aa.z_pre = (const float *)(w + p.off_zpre);
+        aa.N = nb * n; aa.n = n; aa.nb = nb; aa.tile = p.tile; aa.tiles = p.tiles; aa.eps = eps;
+        aa.rope = p.rope;
+        apply_any(p, aa, s);
+        if ((st = check_launch(fn))) return st;
+    }
+    return SVLA_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int svla_abi_version(void) { return SVLA_ABI_VERSION; }
+
+const char *svla_status_string(svla_status s)
+{
+    switch (s) {
+    case SVLA_OK: return "SVLA_OK";
+    case SVLA_ERR_NULL: return "SVLA_ERR_NULL";
+    case SVLA_ERR_SHAPE: return "SVLA_ERR_SHAPE";
+    case SVLA_ERR_DTYPE: return "SVLA_ERR_DTYPE";
+    case SVLA_ERR_ALIGN: return "SVLA_ERR_ALIGN";
+    case SVLA_ERR_UNSUPPORTED: return "SVLA_ERR_UNSUPPORTED";
+    case SVLA_ERR_WORKSPACE: return "SVLA_ERR_WORKSPACE";
+    case SVLA_ERR_VALUE: return "SVLA_ERR_VALUE";
+    case SVLA_ERR_HIP: return "SVLA_ERR_HIP";
+    }
+    return "SVLA_ERR_UNKNOWN";
+}
+
+const char *svla_last_error(void) { return g_err; }
+
+svla_status svla_workspace_size(svla_op op, svla_dtype dt, int B, int H, int nb, int n, int d,
+                                size_t *bytes)
+{
+    const char *fn = "svla_workspace_size";
+    if (!bytes) return fail(SVLA_ERR_NULL, fn, "bytes is NULL");
+    if ((int)op < SVLA_OP_NONCAUSAL || (int)op > SVLA_OP_APPLY)
+        return fail(SVLA_ERR_VALUE, fn, "unknown op %d", (int)op);
+    Plan p;
+    svla_status st = make_plan(fn, op, dt, B, H, nb, n, d, nullptr, &p);
+    if (st) return st;
+    *bytes = p.total;
+    return SVLA_OK;
+}
+
+svla_status svla_noncausal(svla_dtype dt, int B, int H, int N, int d, const void *Q,
+                           const void *K, const void *V, void *O, float eps, float *S_out,
+                           float *z_out, void *ws, size_t ws_bytes, svla_stream stream)
+{
+    return forward("svla_noncausal", SVLA_OP_NONCAUSAL, dt, B, H, 1, N, d, Q, K, V, O, nullptr,
+                   nullptr, S_out, z_out, nullptr, nullptr, eps, ws, ws_bytes, stream);
+}
+
+svla_status svla_block_causal(svla_dtype dt, int B, int H, int nb, int n, int d, const void *Q,
+                              const void *K, const void *V, void *O, const float *S0,
+                              const float *z0, float *S_final, float *z_final,
+                              const svla_rope *rope, float eps, void *ws, size_t ws_bytes,
+                              svla_stream stream)
+{
+    return forward("svla_block_causal", SVLA_OP_BLOCK_CAUSAL, dt, B, H, nb, n, d, Q, K, V, O, S0,
+                   z0, S_final, z_final, nullptr, rope, eps, ws, ws_bytes, stream);
+}
+
+svla_status svla_block_causal_gated(svla_dtype dt, int B, int H, int nb, int n, int d,
+                                    const void *Q, const void *K, const void *V, void *O,
+                                    const float *S0, const float *z0, float *S_final,
+                                    float *z_final, const float *g, const svla_rope *rope,
+                                    float eps, void *ws, size_t ws_bytes, svla_stream stream)
+{
+    const char *fn = "svla_block_causal_gated";
+    if (!g && (long)B * H * nb > 0) return fail(SVLA_ERR_NULL, fn, "g is required");
+    return forward(fn, SVLA_OP_BLOCK_CAUSAL, dt, B, H, nb, n, d, Q, K, V, O, S0, z0, S_final,
+                   z_final, g, rope, eps, ws, ws_bytes, stream);
+}
+
+svla_status svla_block_step(svla_dtype dt, int B, int H, int n, int d, const void *Q,
+                            const void *K, const void *V, void *O, const float *S_in,
+                            const float *z_in, float *S_out, float *z_out,
+                            const svla_rope *rope, float eps, void *ws, size_t ws_bytes,
+                            svla_stream stream)
+{
+    return forward("svla_block_step", SVLA_OP_BLOCK_STEP, dt, B, H, 1, n, d, Q, K, V, O, S_in,
+                   z_in, S_out, z_out, nullptr, rope, eps, ws, ws_bytes, stream);
+}
+
+svla_status svla_block_step_gated(svla_dtype dt, int B, int H, int n, int d, const void *Q,
+                                  const void *K, const void *V, void *O, const float *S_in,
+                                  const float *z_in, float *S_out, float *z_out,
+                                  const float *g, const svla_rope *rope, float eps, void *ws,
+                                  size_t ws_bytes, svla_stream stream)
+{
+    const char *fn = "svla_block_step_gated";
+    if (!g && (long)B * H > 0) return fail(SVLA_ERR_NULL, fn, "g is required");
+    return forward(fn, SVLA_OP_BLOCK_STEP, dt, B, H, 1, n, d, Q, K, V, O, S_in, z_in, S_out,
+                   z_out, g, rope, eps, ws, ws_bytes, stream);
+}
+
+svla_status svla_state_build(svla_dtype dt, int B, int H, int nb, int n, int d, const void *K,
+                             const void *V, const svla_rope *rope, float *S_local,
+                             float *z_local, void *ws, size_t ws_bytes, svla_stream stream)
+{
+    const char *fn = "svla_state_build";
+    Plan p;
+    svla_status st = make_plan(fn, SVLA_OP_STATE_BUILD, dt, B, H, nb, n, d, rope, &p);
+    if (st) return st;
+    (void)ws; (void)ws_bytes;
+    if (p.BH * nb == 0) return SVLA_OK;
+    if (!S_local || !z_local) return fail(SVLA_ERR_NULL, fn, "S_local and z_local are required");
+    if (n > 0 && (!K || !V)) return fail(SVLA_ERR_NULL, fn, "K and V are required");
+    if (misaligned(K) || misaligned(V) || misaligned(S_local) || misaligned(z_local))
+        return fail(SVLA_ERR_ALIGN, fn, "device pointers must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (n == 0) {
+        // no tokens: every local contribution is zero
+        ScanArgs sa;
+        memset(&sa, 0, sizeof sa);
+        sa.nb = nb; sa.splits = 0; sa.S_pre = S_local; sa.z_pre = z_local;
+        // an export scan over zero splits writes a zero state for every block
+        scan_any<SCAN_EXPORT>(p, sa, s);
+        return check_launch(fn);
+    }
+    BuildArgs ba;
+    ba.K = K; ba.V = V; ba.S_part = S_local; ba.z_part = z_local;
+    ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = 1; ba.chunk = p.chunk; ba.rope = p.rope;
+    build_any(p, ba, s);
+    return check_launch(fn);
+}
+
+svla_status svla_state_scan(int B, int H, int nb, int d, const float *S_local,
+                            const float *z_local, const float *g, const float *S0,
+                            const float *z0, float *S_prefix, float *z_prefix,
+                            svla_stream stream)
+{
+    const char *fn = "svla_state_scan";
+    Plan p;
+    svla_status st = make_plan(fn, SVLA_OP_STATE_SCAN, SVLA_F32, B, H, nb, 1, d, nullptr, &p);
+    if (st) return st;
+    if (p.BH * nb == 0) return SVLA_OK;
+    if (!S_local || !z_local || !S_prefix || !z_prefix)
+        return fail(SVLA_ERR_NULL, fn, "S_local, z_local, S_prefix and z_prefix are required");
+    if ((S0 == nullptr) != (z0 == nullptr)) return fail(SVLA_ERR_NULL, fn, "pass both S0 and z0, or neither");
+    if (misaligned(S_local) || misaligned(z_local) || misaligned(S_prefix) ||
+        misaligned(z_prefix) || misaligned(S0) || misaligned(z0) || misaligned(g))
+        return fail(SVLA_ERR_ALIGN, fn, "device pointers must be 16-byte aligned");
+    ScanArgs sa;
+    memset(&sa, 0, sizeof sa);
+    sa.S_part = S_local; sa.z_part = z_local; sa.g = g; sa.S_in = S0; sa.z_in = z0;
+    sa.S_pre = S_prefix; sa.z_pre = z_prefix; sa.nb = nb; sa.splits = 1;
+    (void)hipGetLastError();
+    scan_any<SCAN_EXPORT>(p, sa, (hipStream_t)stream);
+    return check_launch(fn);
+}
+
+svla_status svla_apply(svla_dtype dt, int B, int H, int nb, int n, int d, const void *Q,
+                       const float *S_prefix, const float *z_prefix, const svla_rope *rope,
+                       float eps, void *O, void *ws, size_t ws_bytes, svla_stream stream)
+{
+    const char *fn = "svla_apply";
+    Plan p;
+    svla_status st = make_plan(fn, SVLA_OP_APPLY, dt, B, H, nb, n, d, rope, &p);
+    if (st) return st;
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(SVLA_ERR_VALUE, fn, "eps must be finite and >= 0");
+    if (p.BH * nb * n == 0) return SVLA_OK;
+    if (!Q || !O || !S_prefix || !z_prefix)
+        return fail(SVLA_ERR_NULL, fn, "Q, O, S_prefix and z_prefix are required");
+    if (!ws) return fail(SVLA_ERR_NULL, fn, "workspace of %zu bytes required", p.total);
+    if (misaligned(Q) || misaligned(O) || misaligned(S_prefix) || misaligned(z_prefix) || misaligned(ws))
+        return fail(SVLA_ERR_ALIGN, fn, "device pointers must be 16-byte aligned");
+    if (ws_bytes < p.total)
+        return fail(SVLA_ERR_WORKSPACE, fn, "workspace of %zu bytes is smaller than the %zu needed",
+                    ws_bytes, p.total);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    ScanArgs sa;
+    memset(&sa, 0, sizeof sa);
+    sa.S_part = S_prefix; sa.nb = nb; sa.splits = 1; sa.S_op = ws;
+    scan_any<SCAN_PACK>(p, sa, s);
+    if ((st = check_launch(fn))) return st;
+    ApplyArgs aa;
+    aa.Q = Q; aa.O = O; aa.S_op = ws; aa.z_pre = z_prefix;
+    aa.N = nb * n; aa.n = n; aa.nb = nb; aa.tile = p.tile; aa.tiles = p.tiles; aa.eps = eps;
+    aa.rope = p.rope;
+    apply_any(p, aa, s);
+    return check_launch(fn);
+}
+
+}  // extern "C"

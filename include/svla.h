@@ -1,0 +1,215 @@
+/*
+ * svla.h -- C ABI of libsvla: block-causal ReLU linear attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (SANA-Video, "Efficient Video Generation with Block Linear
+ * Diffusion Transformer"):
+ *   - linear attention is the core operation of the Linear DiT (abstract,
+ *     design (1) "Linear DiT");
+ *   - its state is a d x d matrix whose shape does not depend on the
+ *     sequence length, cached after each block and increased by the next
+ *     block's KV contribution (ICLR 2026 oral talk, "block KV cache"
+ *     review; abstract, design (2) "Constant-Memory KV cache");
+ *   - video is generated block by block, causally across blocks and
+ *     bidirectionally inside a block (talk, "block by block causally and
+ *     diffuse within the block");
+ *   - SANA-Video 2.0 uses gated linear attention layers (SANA-Video 2.0
+ *     news page, "Hybrid Linear-Softmax Attention"; comfyui-wiki model page,
+ *     2.0 section);
+ *   - the linear attention carries 3D RoPE (talk, "3D RoPE for the linear
+ *     attention"; comfyui-wiki model page, rotary position embeddings).
+ *
+ * Definitions used by every call, per (batch b, head h):
+ *   phi(x)  = max(x, 0), elementwise, on Q and K only.
+ *   local_c = sum over tokens j of block c of  R_j phi(k_j) (x) v_j   (d x d)
+ *   zloc_c  = sum over tokens j of block c of  phi(k_j)               (d)
+ *   S_c     = g_c * S_{c-1} + local_c,   z_c = g_c * z_{c-1} + zloc_c,
+ *             S_{-1} = S0 (or 0), g_c = 1 when ungated.
+ *   O_i     = (R_i phi(q_i))^T S_c / (phi(q_i) . z_c + eps) for i in block c.
+ * R_j is the identity without RoPE.  With RoPE, R_j rotates adjacent pairs
+ * (2m, 2m+1) of three dimension slices by +pos*theta_m, theta_m =
+ * base^(-2m/width): dims [0,dt) by the frame index t, [dt,dt+dh) by the
+ * grid row, [dt+dh,dt+dh+dw) by the grid column; dims past dt+dh+dw are not
+ * rotated.  Token p of a call (p counts from 0 over the call's tokens) sits at
+ * frame t0 + p/(grid_h*grid_w), row (p/grid_w)%grid_h, column p%grid_w.
+ * The rotation touches the numerator only: z and the denominator use phi(.)
+ * unrotated.
+ *
+ * Conventions shared by every entry point:
+ *   Layout   Q, K, V, O: contiguous [B,H,N,d] (d fastest), one dtype.
+ *            S: [B,H,d,d] fp32, S[k][v] (row = key feature, column = value
+ *            feature).  z: [B,H,d] fp32.  g: fp32.
+ *   Memory   All pointers except `rope` are device pointers (HIP), 16-byte
+ *            aligned.  The caller owns every buffer.  The library never
+ *            allocates or frees memory and never synchronises: it only
+ *            enqueues kernels on `stream` (NULL = the default stream).
+ *            O must not overlap Q, K, V or the workspace.
+ *   Sizes    d in {32, 64, 128}; B, H, nb, n >= 0.  One (b,h) slice of Q
+ *            must stay below 2 GiB.  Empty inputs (B*H == 0) return SVLA_OK
+ *            without launching anything.
+ *   Errors   Every call returns a status.  All validation runs on the host
+ *            before any HIP call; on any error nothing is launched and no
+ *            output is written.  svla_last_error() returns a thread-local
+ *            message for the last failing call of the thread.
+ *            SVLA_ERR_HIP reports a launch failure only; faults during
+ *            execution surface at the caller's next synchronisation.
+ *   Workspace  Scratch device memory of at least svla_workspace_size()
+ *            bytes for the same op and sizes.  Its content on entry does
+ *            not matter; the size does not depend on how many blocks came
+ *            before (the state is the only thing carried).
+ *   Threads  Calls are re-entrant.  Two calls that share a workspace must be
+ *            ordered on one stream.
+ */
+#ifndef SVLA_H
+#define SVLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVLA_ABI_VERSION 1
+
+typedef enum svla_status {
+    SVLA_OK = 0,
+    SVLA_ERR_NULL = 1,        /* a required pointer is NULL                   */
+    SVLA_ERR_SHAPE = 2,       /* negative size, slice too large, N % nb != 0  */
+    SVLA_ERR_DTYPE = 3,       /* dtype not SVLA_F32 / SVLA_BF16               */
+    SVLA_ERR_ALIGN = 4,       /* a device pointer not 16-byte aligned         */
+    SVLA_ERR_UNSUPPORTED = 5, /* d not in {32,64,128}; RoPE split or grid too large */
+    SVLA_ERR_WORKSPACE = 6,   /* workspace smaller than svla_workspace_size() */
+    SVLA_ERR_VALUE = 7,       /* eps < 0 or not finite; bad RoPE parameters   */
+    SVLA_ERR_HIP = 8          /* a kernel launch failed                       */
+} svla_status;
+
+typedef enum svla_dtype {
+    SVLA_F32 = 0,   /* IEEE binary32 Q/K/V/O */
+    SVLA_BF16 = 1   /* bfloat16 Q/K/V/O; arithmetic accumulates in fp32 */
+} svla_dtype;
+
+/* Which call a workspace is sized for. */
+typedef enum svla_op {
+    SVLA_OP_NONCAUSAL = 0,
+    SVLA_OP_BLOCK_CAUSAL = 1,   /* also the gated variant */
+    SVLA_OP_BLOCK_STEP = 2,     /* also the gated variant */
+    SVLA_OP_STATE_BUILD = 3,
+    SVLA_OP_STATE_SCAN = 4,
+    SVLA_OP_APPLY = 5
+} svla_op;
+
+/* 3D RoPE on the numerator (host struct; may live on the stack).
+ * dt_dims/dh_dims/dw_dims: even, >= 0, sum <= d.  grid_h, grid_w >= 1.
+ * t0 >= 0: absolute frame index of the call's first token.  base > 0. */
+typedef struct svla_rope {
+    int dt_dims, dh_dims, dw_dims;
+    int grid_h, grid_w;
+    int t0;
+    float base;
+} svla_rope;
+
+/* A hipStream_t; NULL means the default stream. */
+typedef void *svla_stream;
+
+/* ---- versioning and errors ------------------------------------------------ */
+
+int svla_abi_version(void);                       /* == SVLA_ABI_VERSION */
+const char *svla_status_string(svla_status s);    /* static string */
+const char *svla_last_error(void);                /* thread-local; "" if none */
+
+/* Bytes of workspace the call `op` needs for these sizes (nb = 1 for the
+ * non-causal call and the block step; N = nb*n).  *bytes is written on
+ * SVLA_OK only. */
+svla_status svla_workspace_size(svla_op op, svla_dtype dt, int B, int H,
+                                int nb, int n, int d, size_t *bytes);
+
+/* ---- the method ------------------------------------------------------------ */
+
+/* Non-causal linear attention over one block of N tokens (the base Linear
+ * DiT: abstract, design (1)).  O = phi(Q) S / (phi(Q) z + eps) with
+ * S = phi(K)^T V, z = sum phi(K) over all N tokens.
+ * S_out [B,H,d,d] and z_out [B,H,d] (nullable, both or neither) receive S, z. */
+svla_status svla_noncausal(svla_dtype dt, int B, int H, int N, int d,
+                           const void *Q, const void *K, const void *V, void *O,
+                           float eps, float *S_out, float *z_out,
+                           void *ws, size_t ws_bytes, svla_stream stream);
+
+/* Block-causal linear attention over nb blocks of n tokens in one call
+ * (talk, block KV cache and block-causal schedule).  Tokens of block c read
+ * the inclusive state S_c.  S0/z0 (nullable, both or neither): state that
+ * enters block 0.  S_final/z_final (nullable, both or neither): S_{nb-1}.
+ * rope: NULL for none. */
+svla_status svla_block_causal(svla_dtype dt, int B, int H, int nb, int n, int d,
+                              const void *Q, const void *K, const void *V, void *O,
+                              const float *S0, const float *z0,
+                              float *S_final, float *z_final,
+                              const svla_rope *rope, float eps,
+                              void *ws, size_t ws_bytes, svla_stream stream);
+
+/* As svla_block_causal with a decay g [B,H,nb] (fp32, device) applied to the
+ * state entering each block (SANA-Video 2.0 gated layers):
+ * S_c = g[b,h,c] * S_{c-1} + local_c, and likewise for z. */
+svla_status svla_block_causal_gated(svla_dtype dt, int B, int H, int nb, int n, int d,
+                                    const void *Q, const void *K, const void *V, void *O,
+                                    const float *S0, const float *z0,
+                                    float *S_final, float *z_final,
+                                    const float *g, const svla_rope *rope, float eps,
+                                    void *ws, size_t ws_bytes, svla_stream stream);
+
+/* One streaming block step (talk: cache the state, add the next block's KV
+ * contribution): Q, K, V, O are [B,H,n,d] for this block only.
+ * S_out = S_in + phi(K)^T V, z_out = z_in + sum phi(K); O reads S_out.
+ * S_in/z_in nullable (zero state).  S_out/z_out required; S_out may equal
+ * S_in (commit in place) or differ (evaluate without committing, as a
+ * denoising loop does before a block is final).  With RoPE, rope->t0 is the
+ * absolute frame index of this block's first token. */
+svla_status svla_block_step(svla_dtype dt, int B, int H, int n, int d,
+                            const void *Q, const void *K, const void *V, void *O,
+                            const float *S_in, const float *z_in,
+                            float *S_out, float *z_out,
+                            const svla_rope *rope, float eps,
+                            void *ws, size_t ws_bytes, svla_stream stream);
+
+/* As svla_block_step with decay g [B,H] (fp32, device):
+ * S_out = g * S_in + phi(K)^T V, z_out = g * z_in + sum phi(K). */
+svla_status svla_block_step_gated(svla_dtype dt, int B, int H, int n, int d,
+                                  const void *Q, const void *K, const void *V, void *O,
+                                  const float *S_in, const float *z_in,
+                                  float *S_out, float *z_out,
+                                  const float *g, const svla_rope *rope, float eps,
+                                  void *ws, size_t ws_bytes, svla_stream stream);
+
+/* ---- the three kernels, one by one ------------------------------------------ */
+
+/* Each block's own contribution: S_local [B,H,nb,d,d] = sum_j R_j phi(k_j) (x) v_j,
+ * z_local [B,H,nb,d] = sum_j phi(k_j) (talk: the current block's KV
+ * contribution).  K, V: [B,H,nb*n,d]. */
+svla_status svla_state_build(svla_dtype dt, int B, int H, int nb, int n, int d,
+                             const void *K, const void *V, const svla_rope *rope,
+                             float *S_local, float *z_local,
+                             void *ws, size_t ws_bytes, svla_stream stream);
+
+/* Inclusive (optionally decayed) prefix over blocks (talk: the cached state
+ * plus the current block's contribution):
+ * S_prefix[b,h,c] = g[b,h,c] * S_prefix[b,h,c-1] + S_local[b,h,c], starting
+ * from S0 (nullable = 0); z likewise.  g nullable (= 1).
+ * S_local, S_prefix: [B,H,nb,d,d]; z_local, z_prefix: [B,H,nb,d]. */
+svla_status svla_state_scan(int B, int H, int nb, int d,
+                            const float *S_local, const float *z_local,
+                            const float *g, const float *S0, const float *z0,
+                            float *S_prefix, float *z_prefix, svla_stream stream);
+
+/* Read-out of every token against its block's state:
+ * O_i = (R_i phi(q_i))^T S_prefix[c] / (phi(q_i) . z_prefix[c] + eps).
+ * Q, O: [B,H,nb*n,d]; S_prefix [B,H,nb,d,d]; z_prefix [B,H,nb,d].
+ * With dt == SVLA_BF16 the state enters the matrix cores rounded to bf16. */
+svla_status svla_apply(svla_dtype dt, int B, int H, int nb, int n, int d,
+                       const void *Q, const float *S_prefix, const float *z_prefix,
+                       const svla_rope *rope, float eps, void *O,
+                       void *ws, size_t ws_bytes, svla_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVLA_H */

@@ -1,0 +1,143 @@
+"""C-ABI contract on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments before any HIP call (nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_causal_linear_relu_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "svla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svla_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _lib.PROTOTYPES, name
+
+
+def test_version_and_strings(lib):
+    assert lib.svla_abi_version() == 1
+    assert lib.svla_status_string(0) == b"SVLA_OK"
+    assert lib.svla_status_string(6) == b"SVLA_ERR_WORKSPACE"
+
+
+def _ws(lib, *args):
+    out = ctypes.c_size_t(12345)
+    st = lib.svla_workspace_size(*args, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size(lib):
+    st, n1 = _ws(lib, _lib.OP_BLOCK_STEP, _lib.SVLA_BF16, 1, 70, 1, 1170, 32)
+    assert st == 0 and n1 > 0
+    # the state is the only thing carried: the step's workspace does not grow
+    st, n2 = _ws(lib, _lib.OP_BLOCK_STEP, _lib.SVLA_BF16, 1, 70, 1, 1170, 32)
+    assert n2 == n1
+    st, n3 = _ws(lib, _lib.OP_STATE_BUILD, _lib.SVLA_BF16, 1, 70, 7, 2640, 32)
+    assert st == 0 and n3 == 0
+    st, _ = _ws(lib, _lib.OP_BLOCK_CAUSAL, _lib.SVLA_BF16, 1, 70, 7, 2640, 48)
+    assert st == 5
+    st, _ = _ws(lib, _lib.OP_BLOCK_CAUSAL, 7, 1, 70, 7, 2640, 32)
+    assert st == 3
+    st, _ = _ws(lib, 99, _lib.SVLA_BF16, 1, 70, 7, 2640, 32)
+    assert st == 7
+    st, n = _ws(lib, _lib.OP_NONCAUSAL, _lib.SVLA_BF16, 0, 70, 1, 10, 32)
+    assert st == 0
+
+
+# Fake, aligned, never dereferenced "device" addresses: every case below
+# must fail validation before any HIP call.
+A = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)
+
+
+def _bc(lib, **kw):
+    a = dict(dt=_lib.SVLA_BF16, B=1, H=2, nb=2, n=64, d=32, Q=A, K=A, V=A, O=A2, S0=None,
+             z0=None, Sf=None, zf=None, rope=None, eps=1e-6, ws=A, wsb=1 << 30)
+    a.update(kw)
+    st = lib.svla_block_causal(a["dt"], a["B"], a["H"], a["nb"], a["n"], a["d"], a["Q"], a["K"],
+                               a["V"], a["O"], a["S0"], a["z0"], a["Sf"], a["zf"], a["rope"],
+                               a["eps"], a["ws"], a["wsb"], None)
+    return st, lib.svla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), 1),
+    (dict(O=None), 1),
+    (dict(ws=None), 1),
+    (dict(S0=A), 1),                      # S0 without z0
+    (dict(Sf=A), 1),                      # S_final without z_final
+    (dict(B=-1), 2),
+    (dict(n=-5), 2),
+    (dict(nb=1, n=(1 << 31) // 64), 2),   # one slice >= 2 GiB
+    (dict(dt=5), 3),
+    (dict(Q=MIS), 4),
+    (dict(O=MIS), 4),
+    (dict(d=16), 5),
+    (dict(d=256), 5),
+    (dict(wsb=16), 6),
+    (dict(eps=-1.0), 7),
+    (dict(eps=float("nan")), 7),
+    (dict(eps=float("inf")), 7),
+])
+def test_block_causal_rejects(lib, kw, status):
+    st, msg = _bc(lib, **kw)
+    assert st == status, msg
+    assert msg.startswith("svla_block_causal:")
+
+
+@pytest.mark.parametrize("rope,status", [
+    (_lib.SvlaRope(7, 12, 12, 15, 26, 0, 1e4), 7),      # odd split
+    (_lib.SvlaRope(8, 12, 14, 15, 26, 0, 1e4), 7),      # 34 > d
+    (_lib.SvlaRope(8, 12, 12, 0, 26, 0, 1e4), 7),       # empty grid
+    (_lib.SvlaRope(8, 12, 12, 15, 26, -3, 1e4), 7),     # negative t0
+    (_lib.SvlaRope(8, 12, 12, 15, 26, 0, 0.0), 7),      # base 0
+    (_lib.SvlaRope(8, 12, 12, 4000, 4000, 0, 1e4), 5),  # table too large
+])
+def test_rope_rejects(lib, rope, status):
+    st, msg = _bc(lib, rope=ctypes.byref(rope))
+    assert st == status, msg
+
+
+def test_empty_is_ok_without_launch(lib):
+    st, msg = _bc(lib, B=0, Q=None, K=None, V=None, O=None, ws=None, wsb=0)
+    assert st == 0, msg
+
+
+def test_gated_needs_g(lib):
+    st = lib.svla_block_causal_gated(_lib.SVLA_BF16, 1, 2, 2, 64, 32, A, A, A, A2, None, None,
+                                     None, None, None, None, 1e-6, A, 1 << 30, None)
+    assert st == 1
+
+
+def test_step_needs_state_out(lib):
+    st = lib.svla_block_step(_lib.SVLA_BF16, 1, 2, 64, 32, A, A, A, A2, None, None, None, None,
+                             None, 1e-6, A, 1 << 30, None)
+    assert st == 1
+
+
+def test_other_entry_points_validate(lib):
+    assert lib.svla_noncausal(_lib.SVLA_BF16, 1, 2, 100, 32, A, A, A, A2, -1.0, None, None, A,
+                              1 << 30, None) == 7
+    assert lib.svla_state_build(_lib.SVLA_BF16, 1, 2, 2, 64, 32, A, A, None, None, A, None, 0,
+                                None) == 1
+    assert lib.svla_state_scan(1, 2, 2, 32, A, A, None, A, None, A, A, None) == 1
+    assert lib.svla_state_scan(1, 2, 2, 32, MIS, A, None, None, None, A, A, None) == 4
+    assert lib.svla_apply(_lib.SVLA_BF16, 1, 2, 2, 64, 32, A, A, A, None, 1e-6, A2, A, 8,
+                          None) == 6
