@@ -25,7 +25,7 @@ from . import _lib
 from ._lib import SvlaError, rope_struct  # noqa: F401
 
 __all__ = ["noncausal", "block_causal", "block_step", "state_build", "state_scan", "apply",
-           "workspace_size", "SvlaError", "library"]
+           "workspace_size", "set_timing_events", "SvlaError", "library"]
 
 _DT = {torch.bfloat16: _lib.SVLA_BF16, torch.float32: _lib.SVLA_F32}
 _OPS = {"noncausal": _lib.OP_NONCAUSAL, "block_causal": _lib.OP_BLOCK_CAUSAL,
@@ -97,16 +97,36 @@ def _qkv(Q, K, V):
     return dt
 
 
-def noncausal(Q, K, V, eps: float = 1e-6, return_state: bool = False):
+def _ws_arg(workspace, op, Q, B, H, nb, n, d):
+    if workspace is None:
+        workspace = _workspace(workspace_size(op, Q.dtype, B, H, nb, n, d), Q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, nbytes
+
+
+def set_timing_events(events) -> None:
+    """Record ``events`` (torch.cuda.Event, each recorded once already) between
+    the kernels of every following fused call on this thread; None stops."""
+    lib = library()
+    if not events:
+        _lib.check(lib, lib.svla_set_timing_events(None, 0))
+        set_timing_events._keep = None
+        return
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    set_timing_events._keep = arr
+    _lib.check(lib, lib.svla_set_timing_events(arr, len(events)))
+
+
+def noncausal(Q, K, V, eps: float = 1e-6, return_state: bool = False,
+              out: Optional[torch.Tensor] = None, workspace=None):
     """Bidirectional linear attention over all N tokens (one block)."""
     dt = _qkv(Q, K, V)
     B, H, N, d = Q.shape
     lib = library()
-    O = torch.empty_like(Q)
+    O = torch.empty_like(Q) if out is None else _dev(out, "out", Q.dtype)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=Q.device) if return_state else None
     z = torch.empty((B, H, d), dtype=torch.float32, device=Q.device) if return_state else None
-    ws = _workspace(workspace_size("noncausal", Q.dtype, B, H, 1, N, d), Q.device)
-    nbytes = 0 if ws is None else ws.numel()
+    ws, nbytes = _ws_arg(workspace, "noncausal", Q, B, H, 1, N, d)
     _lib.check(lib, lib.svla_noncausal(dt, B, H, N, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
                                        float(eps), _ptr(S), _ptr(z), _ptr(ws), nbytes,
                                        _stream(Q.device)))
@@ -114,7 +134,8 @@ def noncausal(Q, K, V, eps: float = 1e-6, return_state: bool = False):
 
 
 def block_causal(Q, K, V, nb: int, S0=None, z0=None, g=None, rope=None, eps: float = 1e-6,
-                 return_state: bool = False, out: Optional[torch.Tensor] = None):
+                 return_state: bool = False, out: Optional[torch.Tensor] = None,
+                 workspace=None):
     """Block-causal linear attention over nb blocks of N/nb tokens in one call.
 
     ``g`` [B,H,nb] float32 selects the gated variant."""
@@ -128,8 +149,7 @@ def block_causal(Q, K, V, nb: int, S0=None, z0=None, g=None, rope=None, eps: flo
     O = torch.empty_like(Q) if out is None else _dev(out, "out", Q.dtype)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=Q.device) if return_state else None
     z = torch.empty((B, H, d), dtype=torch.float32, device=Q.device) if return_state else None
-    ws = _workspace(workspace_size("block_causal", Q.dtype, B, H, nb, n, d), Q.device)
-    nbytes = 0 if ws is None else ws.numel()
+    ws, nbytes = _ws_arg(workspace, "block_causal", Q, B, H, nb, n, d)
     rp, _keep = _rope_arg(rope)
     if g is None:
         st = lib.svla_block_causal(dt, B, H, nb, n, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
@@ -160,9 +180,7 @@ def block_step(Q, K, V, S_in=None, z_in=None, S_out=None, z_out=None, g=None, ro
         z_out = torch.empty((B, H, d), dtype=torch.float32, device=Q.device)
     _dev(S_out, "S_out", torch.float32)
     _dev(z_out, "z_out", torch.float32)
-    need = workspace_size("block_step", Q.dtype, B, H, 1, n, d)
-    ws = workspace if workspace is not None else _workspace(need, Q.device)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ws, nbytes = _ws_arg(workspace, "block_step", Q, B, H, 1, n, d)
     rp, _keep = _rope_arg(rope)
     if g is None:
         st = lib.svla_block_step(dt, B, H, n, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(S_in),

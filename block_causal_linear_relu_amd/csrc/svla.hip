@@ -21,6 +21,7 @@
 // sized to the (b,h) slice it belongs to: a lane whose token lies past the
 // end of its range is given an offset past the resource and reads zeros /
 // drops its store.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -932,6 +933,24 @@ svla_apply_f32(const ApplyArgs a)
 // host side
 // ---------------------------------------------------------------------------
 thread_local char g_err[512] = "";
+thread_local void *const *t_events = nullptr;   // svla_set_timing_events
+thread_local int t_nev = 0;
+
+enum Slot { SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2 };
+
+// Every kernel goes through here.  With timing events set, the launch
+// carries a start/stop event pair that the runtime records around the
+// kernel's own execution.
+template <typename Arg>
+void launch(void (*kernel)(Arg), unsigned grid, size_t lds, hipStream_t s, Slot slot, const Arg &a)
+{
+    const int e = 2 * (int)slot;
+    if (t_events && e + 1 < t_nev)
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), (uint32_t)lds, s,
+                              (hipEvent_t)t_events[e], (hipEvent_t)t_events[e + 1], 0, a);
+    else
+        kernel<<<dim3(grid), dim3(kThreads), lds, s>>>(a);
+}
 
 svla_status fail(svla_status s, const char *fn, const char *fmt, ...) __attribute__((format(printf, 3, 4)));
 svla_status fail(svla_status s, const char *fn, const char *fmt, ...)
@@ -1098,34 +1117,34 @@ inline bool misaligned(const void *ptr) { return ((uintptr_t)ptr & 15) != 0; }
 template <int D>
 void launch_build(const Plan &p, const BuildArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(p.BH * p.nb * p.splits));
+    const unsigned grid = (unsigned)(p.BH * p.nb * p.splits);
     if (p.esize == 2) {
-        if (p.rope.on) svla_state_build_bf16<D, true><<<grid, kThreads, p.lds_build, s>>>(a);
-        else svla_state_build_bf16<D, false><<<grid, kThreads, p.lds_build, s>>>(a);
+        if (p.rope.on) launch(svla_state_build_bf16<D, true>, grid, p.lds_build, s, SLOT_BUILD, a);
+        else launch(svla_state_build_bf16<D, false>, grid, p.lds_build, s, SLOT_BUILD, a);
     } else {
-        if (p.rope.on) svla_state_build_f32<D, true><<<grid, kThreads, p.lds_build, s>>>(a);
-        else svla_state_build_f32<D, false><<<grid, kThreads, p.lds_build, s>>>(a);
+        if (p.rope.on) launch(svla_state_build_f32<D, true>, grid, p.lds_build, s, SLOT_BUILD, a);
+        else launch(svla_state_build_f32<D, false>, grid, p.lds_build, s, SLOT_BUILD, a);
     }
 }
 
 template <int D, int MODE>
 void launch_scan_d(const Plan &p, const ScanArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(p.BH * (D * D / 1024 + 1)));
-    if (p.esize == 2) svla_state_scan_k<D, MODE, true><<<grid, kThreads, 0, s>>>(a);
-    else svla_state_scan_k<D, MODE, false><<<grid, kThreads, 0, s>>>(a);
+    const unsigned grid = (unsigned)(p.BH * (D * D / 1024 + 1));
+    if (p.esize == 2) launch(svla_state_scan_k<D, MODE, true>, grid, 0, s, SLOT_SCAN, a);
+    else launch(svla_state_scan_k<D, MODE, false>, grid, 0, s, SLOT_SCAN, a);
 }
 
 template <int D>
 void launch_apply(const Plan &p, const ApplyArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(p.BH * p.nb * p.tiles));
+    const unsigned grid = (unsigned)(p.BH * p.nb * p.tiles);
     if (p.esize == 2) {
-        if (p.rope.on) svla_apply_bf16<D, true><<<grid, kThreads, p.lds_apply, s>>>(a);
-        else svla_apply_bf16<D, false><<<grid, kThreads, p.lds_apply, s>>>(a);
+        if (p.rope.on) launch(svla_apply_bf16<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a);
+        else launch(svla_apply_bf16<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a);
     } else {
-        if (p.rope.on) svla_apply_f32<D, true><<<grid, kThreads, p.lds_apply, s>>>(a);
-        else svla_apply_f32<D, false><<<grid, kThreads, p.lds_apply, s>>>(a);
+        if (p.rope.on) launch(svla_apply_f32<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a);
+        else launch(svla_apply_f32<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a);
     }
 }
 
@@ -1247,6 +1266,14 @@ const char *svla_status_string(svla_status s)
 }
 
 const char *svla_last_error(void) { return g_err; }
+
+svla_status svla_set_timing_events(void *const *events, int n)
+{
+    if (events && n < 0) return fail(SVLA_ERR_VALUE, "svla_set_timing_events", "n must be >= 0");
+    t_events = (events && n > 0) ? events : nullptr;
+    t_nev = t_events ? n : 0;
+    return SVLA_OK;
+}
 
 svla_status svla_workspace_size(svla_op op, svla_dtype dt, int B, int H, int nb, int n, int d,
                                 size_t *bytes)

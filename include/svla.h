@@ -208,6 +208,18 @@ svla_status svla_apply(svla_dtype dt, int B, int H, int nb, int n, int d,
                        const svla_rope *rope, float eps, void *O,
                        void *ws, size_t ws_bytes, svla_stream stream);
 
+/* ---- instrumentation ----------------------------------------------------------- */
+
+/* For benchmarks that time each kernel with HIP events.  While set, every
+ * kernel that a call made by this thread launches for slot k (0 = state
+ * build, 1 = scan, 2 = apply) is launched with the start/stop pair
+ * events[2k], events[2k+1], which the runtime records around that kernel's
+ * execution (a kernel a call does not need is not launched and leaves its
+ * pair alone; pairs past n are not used).  `events` are hipEvent_t handles
+ * created by the caller and must stay valid while set; the array is not
+ * copied.  Pass NULL (or n = 0) to stop.  Timing adds no other work. */
+svla_status svla_set_timing_events(void *const *events, int n);
+
 #ifdef __cplusplus
 }
 #endif
