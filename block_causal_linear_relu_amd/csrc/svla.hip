@@ -24,6 +24,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -31,6 +33,60 @@
 #include <string.h>
 
 #include "../../include/svla.h"
+
+// Tuning knobs (compile-time; the defaults are the measured choices).
+#ifndef SVLA_BUILD_PF
+#define SVLA_BUILD_PF 2            // stages of K/V loads in flight in the state build
+#endif
+#ifndef SVLA_BUILD_U
+#define SVLA_BUILD_U 2             // 16-byte K and V chunks per thread per stage
+#endif
+#ifndef SVLA_BUILD_PF_ROPE
+#define SVLA_BUILD_PF_ROPE 1       // the same two knobs for the RoPE build
+#endif
+#ifndef SVLA_BUILD_U_ROPE
+#define SVLA_BUILD_U_ROPE 1
+#endif
+#ifndef SVLA_DMA_U32
+#define SVLA_DMA_U32 1             // direct-to-LDS build, d = 32: chunks per thread per stage
+#endif
+#ifndef SVLA_DMA_R32
+#define SVLA_DMA_R32 3             // ... and LDS ring depth
+#endif
+#ifndef SVLA_DMA_U
+#define SVLA_DMA_U 1               // the same for d = 64, 128
+#endif
+#ifndef SVLA_DMA_R
+#define SVLA_DMA_R 4
+#endif
+#ifndef SVLA_USE_DMA
+#define SVLA_USE_DMA 1             // non-RoPE bf16 builds load straight to LDS
+#endif
+// Cache-policy bits of the streaming accesses (gfx950 buffer instructions:
+// bit 1 = nt, non-temporal).  Measured: nt pays for K/V (read once by the
+// state build) and for Q when every element is read once (d <= 64); the
+// d = 128 apply re-reads Q from four waves and wants it cached.
+#ifndef SVLA_KV_AUX
+#define SVLA_KV_AUX 2
+#endif
+#ifndef SVLA_Q_AUX
+#define SVLA_Q_AUX 2
+#endif
+#ifndef SVLA_O_AUX
+#define SVLA_O_AUX 0
+#endif
+#ifndef SVLA_SCAN_LA
+#define SVLA_SCAN_LA 16            // partial-state loads in flight per scan thread
+#endif
+#ifndef SVLA_TARGET_WGS
+#define SVLA_TARGET_WGS 2048       // state-build workgroups wanted per launch
+#endif
+#ifndef SVLA_MIN_SPLIT_PER_D
+#define SVLA_MIN_SPLIT_PER_D 8     // tokens per split >= this * d
+#endif
+#ifndef SVLA_FUSE_MAX_D
+#define SVLA_FUSE_MAX_D 0          // fuse the scan into the build for d <= this
+#endif
 
 // ---------------------------------------------------------------------------
 // types and small device helpers
@@ -44,7 +100,8 @@ typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 
 namespace {
 
-constexpr int kThreads = 256;                 // every kernel: 4 waves of 64
+constexpr int kThreads = 256;                 // build and apply: 4 waves of 64
+constexpr int kScanThreads = 64;              // scan: one wave, 256 state elements per workgroup
 constexpr uint32_t kOOB = 0x80000000u;        // an offset past every resource
 constexpr int kMaxRopeEntries = 4096;         // (cos, sin) pairs per workgroup
 
@@ -63,6 +120,19 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off
 __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+// Streaming accesses with an explicit cache policy.
+template <int AUX>
+__device__ __forceinline__ u32x4_t load16p(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+}
+
+template <int AUX>
+__device__ __forceinline__ void store16p(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, AUX);
 }
 
 // Reinterpretation helpers.  They take their operand by value on purpose:
@@ -99,6 +169,16 @@ __device__ __forceinline__ unsigned int pack_bf16(float lo, float hi)
     return (unsigned int)f2bf(lo) | ((unsigned int)f2bf(hi) << 16);
 }
 
+// Barrier for LDS hand-offs inside a workgroup.  __syncthreads() also
+// fences global memory, which on this architecture waits for every load in
+// flight (loads and stores share one counter), so it would drain the
+// prefetched stages; this waits for this wave's LDS operations only.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Unsigned division by a divisor fixed per launch (multiply-high method of
 // Granlund and Montgomery): q = (t + ((x - t) >> s1)) >> s2, t = mulhi(x, mul).
 struct FastDiv {
@@ -122,6 +202,7 @@ struct RopeK {
     int t0;                  // absolute frame of the call's first token
     float base;
     FastDiv div_hw, div_w;   // p / (gh*gw), q / gw
+    int tab_bytes;           // LDS reserved for the table in front of the stage buffers
 };
 
 // Table layout: [frames nf x dt/2][rows gh x dh/2][cols gw x dw/2] of float2.
@@ -130,28 +211,40 @@ __device__ __forceinline__ int rope_entries(const RopeK &r, int nf)
     return nf * (r.dt / 2) + r.gh * (r.dh / 2) + r.gw * (r.dw / 2);
 }
 
-// Angles pos * theta_m with theta_m = base^(-2m/width) are reduced to a
-// fraction of a turn in fp64 before sin/cos, so large frame indices keep
-// their accuracy.
+// Angles pos * theta_m with theta_m = base^(-2m/width): the per-pair
+// frequencies (in turns, theta_m / 2 pi) are computed once per workgroup in
+// fp64, each entry's angle is reduced to a fraction of a turn in fp64 (so
+// large frame indices keep their accuracy) and only then goes through an
+// fp32 sin/cos of pi times that small argument.
+constexpr int kMaxRopePairs = 64;
+
 __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
 {
+    __shared__ double turns_per_pos[3 * kMaxRopePairs];
     const int pt = r.dt / 2, ph = r.dh / 2, pw = r.dw / 2;
+    for (int e = threadIdx.x; e < pt + ph + pw; e += blockDim.x) {
+        const int a = e < pt ? 0 : e < pt + ph ? 1 : 2;
+        const int m = a == 0 ? e : a == 1 ? e - pt : e - pt - ph;
+        const int width = a == 0 ? r.dt : a == 1 ? r.dh : r.dw;
+        turns_per_pos[a * kMaxRopePairs + m] =
+            pow((double)r.base, -2.0 * (double)m / (double)width) * (0.5 / M_PI);
+    }
+    __syncthreads();
     const int nT = nf * pt, nH = r.gh * ph, total = rope_entries(r, nf);
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
-        int pos, m, width;
+        int pos, m, a;
         if (e < nT) {
-            pos = f0 + e / pt; m = e % pt; width = r.dt;
+            pos = f0 + e / pt; m = e % pt; a = 0;
         } else if (e < nT + nH) {
-            int x = e - nT; pos = x / ph; m = x % ph; width = r.dh;
+            int x = e - nT; pos = x / ph; m = x % ph; a = 1;
         } else {
-            int x = e - nT - nH; pos = x / pw; m = x % pw; width = r.dw;
+            int x = e - nT - nH; pos = x / pw; m = x % pw; a = 2;
         }
-        double theta = pow((double)r.base, -2.0 * (double)m / (double)width);
-        double turns = (double)pos * theta * (0.5 / M_PI);
+        double turns = (double)pos * turns_per_pos[a * kMaxRopePairs + m];
         turns -= floor(turns);
-        double s, c;
-        sincospi(2.0 * turns, &s, &c);
-        tab[e] = make_float2((float)c, (float)s);
+        float s, c;
+        sincospif(2.0f * (float)turns, &s, &c);
+        tab[e] = make_float2(c, s);
     }
 }
 
@@ -212,13 +305,6 @@ __device__ __forceinline__ void rope_rotate(float *x, uint32_t p, uint32_t frame
 // ---------------------------------------------------------------------------
 // kernel arguments
 // ---------------------------------------------------------------------------
-struct BuildArgs {
-    const void *K, *V;
-    float *S_part, *z_part;      // [BH*nb*splits][d*d], [BH*nb*splits][d]
-    int N, n, nb, splits, chunk; // chunk: tokens per split (multiple of the stage)
-    RopeK rope;
-};
-
 struct ScanArgs {
     const float *S_part, *z_part;  // split partials (or local states, or prefix states)
     const float *g;                // [BH][nb] or null
@@ -228,6 +314,16 @@ struct ScanArgs {
     float *S_pre;                  // fp32 prefix states [BH*nb][d*d] (export mode)
     float *S_fin, *z_fin;          // final state or null
     int nb, splits;
+};
+
+struct BuildArgs {
+    const void *K, *V;
+    float *S_part, *z_part;        // [BH*nb*splits][d*d], [BH*nb*splits][d]
+    int N, n, nb, splits, chunk;   // chunk: tokens per split (multiple of the stage)
+    RopeK rope;
+    unsigned long long *counters;  // [BH] arrival counters of the fused scan
+    unsigned epoch;                // distinct per call (see arrive())
+    ScanArgs scan;                 // what the last workgroup of a (b,h) runs
 };
 
 struct ApplyArgs {
@@ -243,12 +339,196 @@ struct ApplyArgs {
 enum ScanMode { SCAN_FUSED = 0, SCAN_EXPORT = 1, SCAN_PACK = 2 };
 
 // ---------------------------------------------------------------------------
+// The scan of one (bh, tile): tile < d*d/1024 is a 1024-element slice of S
+// (each thread owns 4 consecutive elements of S[k][v]), tile == d*d/1024 is
+// z.  Blocks are walked in order, acc = g_c * acc + sum over splits, with the
+// splits added in index order, so the result repeats bit for bit.
+//
+// Packed operand layout read by svla_apply (per (bh, block), d*d entries):
+// bf16: fragment (m, ks) = 64 lanes x 8 values; lane (rho + 16 kg), value i
+//       holds S[32 ks + 8 kg + i][f(m, rho)]
+// fp32: fragment (m, kq) = 64 lanes x 4 values; lane (rho + 16 kg), value i
+//       holds S[16 kq + 4 kg + i][f(m, rho)]
+// with f(m, rho) = (d/4) (rho / 4) + 4 m + rho % 4: the output rows of the
+// MFMA land so that each lane ends up with consecutive O features.
+// ---------------------------------------------------------------------------
+template <int D, int MODE, bool OPBF16, int NT>
+__device__ __forceinline__ void scan_tile(const ScanArgs &a, long bh, int tile, int tid)
+{
+    constexpr int STILES = D * D / (NT * 4);
+    if (tile < STILES) {
+        const int e0 = tile * (NT * 4) + tid * 4;
+        const int k = e0 / D, v = e0 % D;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (MODE != SCAN_PACK && a.S_in) acc = *(const f32x4_t *)(a.S_in + bh * D * D + e0);
+        // operand positions of the 4 elements (k, v..v+3)
+        const int m = (v % (D / 4)) / 4, rho0 = 4 * (v / (D / 4));
+        int opos[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (OPBF16) {
+                const int ks = k / 32, kg = (k % 32) / 8, i = k % 8;
+                opos[j] = (((m * (D / 32) + ks) * 64 + rho0 + j + 16 * kg) * 8 + i);
+            } else {
+                const int kq = k / 16, kg = (k % 16) / 4, i = k % 4;
+                opos[j] = (((m * (D / 16) + kq) * 64 + rho0 + j + 16 * kg) * 4 + i);
+            }
+        }
+        // The partials of (block c, split sp) form one stream, idx = c*splits + sp,
+        // read through a ring of LA loads in flight; a refill past the end
+        // re-reads the last partial (always in bounds) and is never used.
+        constexpr int LA = SVLA_SCAN_LA;
+        const int total = a.nb * a.splits;
+        const float *base = a.S_part + bh * (long)total * D * D + e0;
+        f32x4_t ring[LA];
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            ring[j] = total > 0 ? *(const f32x4_t *)(base + (long)min(j, total - 1) * D * D)
+                                : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        int c = 0, sp = 0;
+        if (a.splits == 0) {
+            // no tokens: each block only decays the carried state
+            for (; c < a.nb; ++c) {
+                const long unit = bh * a.nb + c;
+                if (a.g) acc *= a.g[unit];
+                if (MODE == SCAN_EXPORT) *(f32x4_t *)(a.S_pre + unit * D * D + e0) = acc;
+            }
+        }
+        for (int idx0 = 0; idx0 < total; idx0 += LA) {
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                const int idx = idx0 + j;
+                if (idx < total) {
+                    const long unit = bh * a.nb + c;
+                    if (sp == 0) {
+                        if (MODE == SCAN_PACK) acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+                        else if (a.g) acc *= a.g[unit];
+                    }
+                    acc += ring[j];
+                    if (sp == a.splits - 1) {
+                        if (MODE == SCAN_EXPORT) {
+                            *(f32x4_t *)(a.S_pre + unit * D * D + e0) = acc;
+                        } else if constexpr (OPBF16) {
+                            unsigned short *op = (unsigned short *)a.S_op + unit * D * D;
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) op[opos[jj]] = f2bf(acc[jj]);
+                        } else {
+                            float *op = (float *)a.S_op + unit * D * D;
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) op[opos[jj]] = acc[jj];
+                        }
+                        sp = 0;
+                        ++c;
+                    } else {
+                        ++sp;
+                    }
+                }
+                ring[j] = *(const f32x4_t *)(base + (long)min(idx + LA, total - 1) * D * D);
+            }
+        }
+        if (MODE != SCAN_PACK && a.S_fin) *(f32x4_t *)(a.S_fin + bh * D * D + e0) = acc;
+    } else if (MODE != SCAN_PACK && tid < D / 4) {
+        const int e0 = tid * 4;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (a.z_in) acc = *(const f32x4_t *)(a.z_in + bh * D + e0);
+        constexpr int LA = SVLA_SCAN_LA;   // same look-ahead ring as for S
+        const int total = a.nb * a.splits;
+        const float *base = a.z_part + bh * (long)total * D + e0;
+        f32x4_t ring[LA];
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            ring[j] = total > 0 ? *(const f32x4_t *)(base + (long)min(j, total - 1) * D)
+                                : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        int c = 0, sp = 0;
+        if (a.splits == 0) {
+            for (; c < a.nb; ++c) {
+                const long unit = bh * a.nb + c;
+                if (a.g) acc *= a.g[unit];
+                *(f32x4_t *)(a.z_pre + unit * D + e0) = acc;
+            }
+        }
+        for (int idx0 = 0; idx0 < total; idx0 += LA) {
+#pragma unroll
+            for (int j = 0; j < LA; ++j) {
+                const int idx = idx0 + j;
+                if (idx < total) {
+                    const long unit = bh * a.nb + c;
+                    if (sp == 0 && a.g) acc *= a.g[unit];
+                    acc += ring[j];
+                    if (sp == a.splits - 1) {
+                        *(f32x4_t *)(a.z_pre + unit * D + e0) = acc;
+                        sp = 0;
+                        ++c;
+                    } else {
+                        ++sp;
+                    }
+                }
+                ring[j] = *(const f32x4_t *)(base + (long)min(idx + LA, total - 1) * D);
+            }
+        }
+        if (a.z_fin) *(f32x4_t *)(a.z_fin + bh * D + e0) = acc;
+    }
+}
+
+template <int D, int MODE, bool OPBF16>
+__global__ void __launch_bounds__(kScanThreads)
+svla_state_scan_k(const ScanArgs a)
+{
+    constexpr int STILES = D * D / (kScanThreads * 4);
+    const long bh = blockIdx.x / (STILES + 1);
+    scan_tile<D, MODE, OPBF16, kScanThreads>(a, bh, blockIdx.x % (STILES + 1), threadIdx.x);
+}
+
+// Arrival of one workgroup at a (b,h) counter; true for the last of `total`.
+// The counter holds (epoch << 32 | count).  A count left by any other call
+// (a different epoch), or whatever an unused workspace held, is restarted,
+// so the workspace needs no initialisation; the last arrival rewinds the
+// count to 0 under the same epoch, so replaying a captured launch works too.
+// The loop ends: a failed compare-and-swap means another workgroup's swap
+// succeeded, and at most `total` workgroups arrive per launch.
+__device__ bool arrive(unsigned long long *ctr, unsigned epoch, unsigned total)
+{
+    const unsigned long long tag = (unsigned long long)epoch << 32;
+    unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const unsigned long long nw = ((old >> 32) == epoch) ? old + 1 : (tag | 1ull);
+        const unsigned long long prev = atomicCAS(ctr, old, nw);
+        if (prev == old) {
+            if ((unsigned)(nw & 0xffffffffull) == total) {
+                __hip_atomic_store(ctr, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return true;
+            }
+            return false;
+        }
+        old = prev;
+    }
+}
+
+// After a build workgroup has written its partials: the last workgroup of the
+// (b,h) runs the scan of every tile of that (b,h) (the inclusive prefix over
+// blocks, the packed operands, the final state).
+template <int D, bool OPBF16>
+__device__ __forceinline__ void fused_scan(const BuildArgs &a, long bh, int tid)
+{
+    __shared__ int s_last;
+    __threadfence();                 // release this workgroup's partial stores
+    __syncthreads();
+    if (tid == 0) s_last = arrive(a.counters + bh, a.epoch, (unsigned)(a.nb * a.splits));
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();                 // acquire every other workgroup's partials
+#pragma unroll 1
+    for (int tile = 0; tile <= D * D / 1024; ++tile) scan_tile<D, SCAN_FUSED, OPBF16, kThreads>(a.scan, bh, tile, tid);
+}
+
+// ---------------------------------------------------------------------------
 // svla_state_build, bf16 inputs.
 //
 // Workgroup = (bh, block c, split s); it walks its token range in stages of
 // TT tokens.  Per stage every thread loads one 16-byte chunk of K and of V
 // (8 features of one token), applies phi to K, adds phi(k) to its running z,
-// and writes both chunks to LDS rows.  The MFMA v_mfma_f32_32x32x16_bf16
+// and writes both chunks to LDS rows.  PF stages of loads are in flight while
+// the current stage is contracted.  The MFMA v_mfma_f32_32x32x16_bf16
 // contracts over tokens, so each lane gathers 8 tokens of one feature from
 // the staged rows.  Which token feeds which k-slot does not matter for a
 // sum over tokens, as long as A and B use the same assignment; lanes 32-63
@@ -259,6 +539,7 @@ enum ScanMode { SCAN_FUSED = 0, SCAN_EXPORT = 1, SCAN_PACK = 2 };
 //   d = 128: 4x4 tiles, 2x2 per wave.
 // With RoPE the rotated phi(k) is split into bf16 hi + lo parts, two MFMAs,
 // so the state keeps ~16 bits of the rotated key.
+// FUSE: the last workgroup of each (b,h) also runs the scan (fused_scan).
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ int swz16(int t, int chunk)
@@ -268,14 +549,15 @@ __device__ __forceinline__ int swz16(int t, int chunk)
     return (D >= 64) ? (chunk ^ ((t & 1) << 2)) : chunk;
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, int PF, int U, bool FUSE>
 __global__ void __launch_bounds__(kThreads)
 svla_state_build_bf16(const BuildArgs a)
 {
     constexpr int CPR = D / 8;            // 16-byte chunks per token row
-    constexpr int TT = kThreads / CPR;    // tokens per stage
+    constexpr int RPS = kThreads / CPR;   // token rows one pass of the threads covers
+    constexpr int TT = U * RPS;           // tokens per stage (U chunks per thread per tensor)
     constexpr int ROWB = D * 2;
-    constexpr int TILEB = TT * ROWB;      // 4096 bytes
+    constexpr int TILEB = TT * ROWB;      // U * 4096 bytes
     constexpr int NK = ROPE ? 2 : 1;
     constexpr int STAGEB = (NK + 1) * TILEB;
     constexpr bool SPLITK = (D == 32);
@@ -285,9 +567,10 @@ svla_state_build_bf16(const BuildArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int s = blockIdx.x % a.splits;
-    const int c = (blockIdx.x / a.splits) % a.nb;
-    const long bh = blockIdx.x / ((long)a.splits * a.nb);
+    const unsigned per_bh = (unsigned)(a.splits * a.nb);
+    const long bh = blockIdx.x / per_bh;
+    const int rest = (int)(blockIdx.x - bh * per_bh);
+    const int c = rest / a.splits, s = rest % a.splits;
     const int tok_lo = c * a.n + s * a.chunk;
     const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
 
@@ -308,7 +591,7 @@ svla_state_build_bf16(const BuildArgs a)
         pp = rope_pairs<4>(a.rope, q * 8, nf);
         __syncthreads();
     }
-    unsigned char *stage = lds + (ROPE ? ((kMaxRopeEntries * 8)) : 0);
+    unsigned char *stage = lds + (ROPE ? a.rope.tab_bytes : 0);
 
     float zacc[8];
 #pragma unroll
@@ -322,98 +605,120 @@ svla_state_build_bf16(const BuildArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // The stage loop is kept regular so the compiler can count the loads in
+    // flight: the stage count is rounded up to a multiple of PF (extra stages
+    // load nothing and add zeros) and every slot is refilled unconditionally
+    // (a refill past the range gets the out-of-range offset).
     const int ntiles = tok_hi > tok_lo ? (tok_hi - tok_lo + TT - 1) / TT : 0;
-    int tok = tok_lo + row;
-    uint32_t off = tok < tok_hi ? (uint32_t)(tok * D + q * 8) * 2u : kOOB;
-    u32x4_t kreg = load16(rK, off);
-    u32x4_t vreg = load16(rV, off);
+    const int nstages = (ntiles + PF - 1) / PF * PF;
+    auto offset = [&](int t) -> uint32_t {
+        return t < tok_hi ? (uint32_t)(t * D + q * 8) * 2u : kOOB;
+    };
+    u32x4_t kreg[PF][U], vreg[PF][U];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t off = offset(tok_lo + row + u * RPS + p * TT);
+            kreg[p][u] = load16p<SVLA_KV_AUX>(rK, off);
+            vreg[p][u] = load16p<SVLA_KV_AUX>(rV, off);
+        }
 
     const int m = lane & 31, g = lane >> 5;
     const int mt0 = SPLITK ? 0 : (wave >> 1) * TPW;
     const int nt0 = SPLITK ? 0 : (wave & 1) * TPW;
 
-    for (int it = 0; it < ntiles; ++it) {
-        unsigned char *st = stage + (it & 1) * STAGEB;
-        // phi(k), z, (rotation), stage to LDS
-        u32x4_t kr;
+    for (int it0 = 0; it0 < nstages; it0 += PF) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kr[e] = relu_bf16x2(kreg[e]);
-        float kf[8];
+        for (int p = 0; p < PF; ++p) {
+            const int it = it0 + p;
+            unsigned char *st = stage + (it & 1) * STAGEB;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kf[2 * e] = bf16lo(kr[e]);
-            kf[2 * e + 1] = bf16hi(kr[e]);
-        }
+            for (int u = 0; u < U; ++u) {
+                const int r = row + u * RPS;              // row within the stage
+                const int tok = tok_lo + r + it * TT;
+                // phi(k), z, (rotation), stage to LDS
+                u32x4_t kr;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
-        const int cpos = swz16<D>(row, q);
-        if constexpr (ROPE) {
-            rope_rotate<4>(kf, (uint32_t)tok, frame_lo, a.rope, pp, tab);
-            u32x4_t hi, lo;
+                for (int e = 0; e < 4; ++e) kr[e] = relu_bf16x2(kreg[p][u][e]);
+                float kf[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                unsigned short h0 = f2bf(kf[2 * e]), h1 = f2bf(kf[2 * e + 1]);
-                float r0 = kf[2 * e] - as_f32((unsigned int)h0 << 16);
-                float r1 = kf[2 * e + 1] - as_f32((unsigned int)h1 << 16);
-                hi[e] = (unsigned int)h0 | ((unsigned int)h1 << 16);
-                lo[e] = pack_bf16(r0, r1);
-            }
-            *(u32x4_t *)(st + row * ROWB + cpos * 16) = hi;
-            *(u32x4_t *)(st + TILEB + row * ROWB + cpos * 16) = lo;
-        } else {
-            *(u32x4_t *)(st + row * ROWB + cpos * 16) = kr;
-        }
-        *(u32x4_t *)(st + NK * TILEB + row * ROWB + cpos * 16) = vreg;
-        __syncthreads();
-
-        // next stage's loads fly while this stage is contracted
-        if (it + 1 < ntiles) {
-            tok += TT;
-            off = tok < tok_hi ? (uint32_t)(tok * D + q * 8) * 2u : kOOB;
-            kreg = load16(rK, off);
-            vreg = load16(rV, off);
-        }
-
-        const unsigned short *Kh = (const unsigned short *)st;
-        const unsigned short *Kl = (const unsigned short *)(st + TILEB);
-        const unsigned short *Vs = (const unsigned short *)(st + NK * TILEB);
-#pragma unroll
-        for (int gi = 0; gi < GPS; ++gi) {
-            if (SPLITK && gi != wave) continue;
-            int t[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) t[i] = 16 * gi + 2 * i + g;
-            bf16x8_t av[TPW], al[TPW], bv[TPW];
-#pragma unroll
-            for (int tm = 0; tm < TPW; ++tm) {
-                const int f = 32 * (mt0 + tm) + m;
-                u16x8_t x, y;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int idx = t[i] * D + swz16<D>(t[i], f >> 3) * 8 + (f & 7);
-                    x[i] = Kh[idx];
-                    if constexpr (ROPE) y[i] = Kl[idx];
+                for (int e = 0; e < 4; ++e) {
+                    kf[2 * e] = bf16lo(kr[e]);
+                    kf[2 * e + 1] = bf16hi(kr[e]);
                 }
-                av[tm] = __builtin_bit_cast(bf16x8_t, x);
-                if constexpr (ROPE) al[tm] = __builtin_bit_cast(bf16x8_t, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
+                const int cpos = swz16<D>(r, q);
+                if constexpr (ROPE) {
+                    rope_rotate<4>(kf, (uint32_t)tok, frame_lo, a.rope, pp, tab);
+                    u32x4_t hi, lo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        unsigned short h0 = f2bf(kf[2 * e]), h1 = f2bf(kf[2 * e + 1]);
+                        float r0 = kf[2 * e] - as_f32((unsigned int)h0 << 16);
+                        float r1 = kf[2 * e + 1] - as_f32((unsigned int)h1 << 16);
+                        hi[e] = (unsigned int)h0 | ((unsigned int)h1 << 16);
+                        lo[e] = pack_bf16(r0, r1);
+                    }
+                    *(u32x4_t *)(st + r * ROWB + cpos * 16) = hi;
+                    *(u32x4_t *)(st + TILEB + r * ROWB + cpos * 16) = lo;
+                } else {
+                    *(u32x4_t *)(st + r * ROWB + cpos * 16) = kr;
+                }
+                *(u32x4_t *)(st + NK * TILEB + r * ROWB + cpos * 16) = vreg[p][u];
             }
+            lds_barrier();
+
+            // refill this register slot with the stage PF ahead
 #pragma unroll
-            for (int tn = 0; tn < TPW; ++tn) {
-                const int f = 32 * (nt0 + tn) + m;
-                u16x8_t x;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    x[i] = Vs[t[i] * D + swz16<D>(t[i], f >> 3) * 8 + (f & 7)];
-                bv[tn] = __builtin_bit_cast(bf16x8_t, x);
+            for (int u = 0; u < U; ++u) {
+                const uint32_t off = offset(tok_lo + row + u * RPS + (it + PF) * TT);
+                kreg[p][u] = load16p<SVLA_KV_AUX>(rK, off);
+                vreg[p][u] = load16p<SVLA_KV_AUX>(rV, off);
             }
+
+            const unsigned short *Kh = (const unsigned short *)st;
+            const unsigned short *Kl = (const unsigned short *)(st + TILEB);
+            const unsigned short *Vs = (const unsigned short *)(st + NK * TILEB);
 #pragma unroll
-            for (int tm = 0; tm < TPW; ++tm)
+            for (int gi = 0; gi < GPS; ++gi) {
+                if (SPLITK && (gi & 3) != wave) continue;   // d = 32: waves split the groups
+                int t[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[i] = 16 * gi + 2 * i + g;
+                bf16x8_t av[TPW], al[TPW], bv[TPW];
+#pragma unroll
+                for (int tm = 0; tm < TPW; ++tm) {
+                    const int f = 32 * (mt0 + tm) + m;
+                    u16x8_t x, y;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int idx = t[i] * D + swz16<D>(t[i], f >> 3) * 8 + (f & 7);
+                        x[i] = Kh[idx];
+                        if constexpr (ROPE) y[i] = Kl[idx];
+                    }
+                    av[tm] = __builtin_bit_cast(bf16x8_t, x);
+                    if constexpr (ROPE) al[tm] = __builtin_bit_cast(bf16x8_t, y);
+                }
 #pragma unroll
                 for (int tn = 0; tn < TPW; ++tn) {
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
-                    if constexpr (ROPE)
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+                    const int f = 32 * (nt0 + tn) + m;
+                    u16x8_t x;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        x[i] = Vs[t[i] * D + swz16<D>(t[i], f >> 3) * 8 + (f & 7)];
+                    bv[tn] = __builtin_bit_cast(bf16x8_t, x);
                 }
+#pragma unroll
+                for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < TPW; ++tn) {
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+                        if constexpr (ROPE)
+                            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+                    }
+            }
         }
     }
     __syncthreads();   // every wave is done with the stage buffers
@@ -464,13 +769,240 @@ svla_state_build_bf16(const BuildArgs a)
         for (int j = 0; j < kThreads / CPR; ++j) v += zred[(qq + CPR * j) * 8 + e];
         store4(rz, (uint32_t)tid * 4u, v);
     }
+    if constexpr (FUSE) fused_scan<D, true>(a, bh, tid);
+    (void)RPS;
+}
+
+// ---------------------------------------------------------------------------
+// svla_state_build, bf16 inputs without RoPE, loads straight to LDS.
+//
+// The same contraction as svla_state_build_bf16, but K and V travel from
+// global memory into an R-deep ring of LDS stages with buffer_load ... lds
+// (16 bytes per lane, one kilobyte per wave instruction), so R - 1 stages of
+// loads stay in flight without holding registers.  phi is applied to the
+// K fragments after they are read from LDS, and z is summed from those
+// fragments.  Rows past the end of the range are masked when fragments are
+// read, so whatever an out-of-range load leaves in LDS never enters a sum.
+// Each stage buffer is its own LDS object, which lets the compiler tell the
+// loads of different stages apart instead of waiting for all of them.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int D, int U, int R>
+__global__ void __launch_bounds__(kThreads)
+svla_state_build_dma(const BuildArgs a)
+{
+    constexpr int CPR = D / 8;            // 16-byte chunks per token row
+    constexpr int RPW = 64 / CPR;         // rows one wave instruction covers
+    constexpr int RPS = kThreads / CPR;   // rows one pass of the 4 waves covers
+    constexpr int TT = U * RPS;           // tokens per stage
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = TT * ROWB;      // U * 4096
+    constexpr int STAGEB = 2 * TILEB;     // K tile, then V tile
+    constexpr bool SPLITK = (D == 32);
+    constexpr int TPW = SPLITK ? 1 : D / 64;
+    constexpr int GPS = TT / 16;
+    constexpr int L = 2 * U;              // loads per thread per stage
+    static_assert(R >= 3 && R <= 4, "ring depth");
+    static_assert(!SPLITK || STAGEB >= 8192, "epilogue reuses two stage buffers");
+
+    __shared__ __attribute__((aligned(16))) unsigned char b0[STAGEB];
+    __shared__ __attribute__((aligned(16))) unsigned char b1[STAGEB];
+    __shared__ __attribute__((aligned(16))) unsigned char b2[STAGEB];
+    __shared__ __attribute__((aligned(16))) unsigned char b3[R > 3 ? STAGEB : 16];
+    __shared__ float zred[4 * D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const unsigned per_bh = (unsigned)(a.splits * a.nb);
+    const long bh = blockIdx.x / per_bh;
+    const int rest = (int)(blockIdx.x - bh * per_bh);
+    const int c = rest / a.splits, s = rest % a.splits;
+    const int tok_lo = c * a.n + s * a.chunk;
+    const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
+
+    const uint32_t slice = (uint32_t)a.N * D * 2;
+    const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
+    const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
+
+    auto buf = [&](int j) -> unsigned char * {
+        return j == 0 ? b0 : j == 1 ? b1 : j == 2 ? b2 : b3;
+    };
+    // stage `st` into buffer `dst`: lane -> (row lane / CPR, LDS slot lane % CPR),
+    // the slot holding global chunk slot ^ swizzle(row)
+    auto issue = [&](unsigned char *dst, int st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = (u * 4 + wave) * RPW + lane / CPR;
+            const int t = tok_lo + st * TT + r;
+            const int cg = swz16<D>(r, lane % CPR);
+            const uint32_t off = t < tok_hi ? (uint32_t)(t * D + cg * 8) * 2u : kOOB;
+            unsigned char *kd = dst + (u * 4 + wave) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)kd, 16, off, 0, 0, SVLA_KV_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(kd + TILEB), 16, off, 0, 0, SVLA_KV_AUX);
+        }
+    };
+
+    float zacc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) zacc[i] = 0.f;
+    f32x16_t acc[TPW][TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int m = lane & 31, g = lane >> 5;
+    const int mt0 = SPLITK ? 0 : (wave >> 1) * TPW;
+    const int nt0 = SPLITK ? 0 : (wave & 1) * TPW;
+    const bool zwave = SPLITK || nt0 == 0;     // one wave per K fragment sums z
+    constexpr int GPW = SPLITK ? GPS / 4 : GPS;  // 16-token groups per wave per stage
+    // Lane part of a fragment element's LDS index: k-slot i of a group reads
+    // row 16 gi + g + 2 i, and the row's parity (= g) fixes the swizzle.
+    int kl[TPW], vl[TPW];
+#pragma unroll
+    for (int tm = 0; tm < TPW; ++tm) {
+        const int f = 32 * (mt0 + tm) + m;
+        kl[tm] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
+    }
+#pragma unroll
+    for (int tn = 0; tn < TPW; ++tn) {
+        const int f = 32 * (nt0 + tn) + m;
+        vl[tn] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
+    }
+
+    const int ntiles = tok_hi > tok_lo ? (tok_hi - tok_lo + TT - 1) / TT : 0;
+    const int nst = (ntiles + R - 1) / R * R;
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j) issue(buf(j), j);
+
+    for (int it0 = 0; it0 < nst; it0 += R) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int it = it0 + j;
+            wait_vmcnt<(R - 2) * L>();     // this wave's loads of stage `it` have landed
+            lds_barrier();                 // ... everyone's have; stage it-1 is consumed
+            issue(buf((j + R - 1) % R), it + R - 1);
+            // Stages past the range are computed too, fully masked (they add
+            // zero), so the stage body has no branch around the accumulators.
+            const unsigned short *Ks = (const unsigned short *)buf(j);
+            const unsigned short *Vs = Ks + TT * D;
+            const int vrows = tok_hi - (tok_lo + it * TT);   // valid rows of this stage
+#pragma unroll
+            for (int gg = 0; gg < GPW; ++gg) {
+                const int gi = SPLITK ? wave + 4 * gg : gg;
+                const int tb = 16 * gi + g;            // k-slot i reads token row tb + 2 i
+                bf16x8_t av[TPW], bv[TPW];
+#pragma unroll
+                for (int tm = 0; tm < TPW; ++tm) {
+                    const unsigned short *pk = Ks + 16 * gi * D + kl[tm];
+                    u16x8_t x;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const unsigned short v = pk[2 * i * D];
+                        x[i] = tb + 2 * i < vrows ? v : (unsigned short)0;
+                    }
+                    u32x4_t w = __builtin_bit_cast(u32x4_t, x);
+                    float zs = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        w[e] = relu_bf16x2(w[e]);
+                        zs += bf16lo(w[e]) + bf16hi(w[e]);
+                    }
+                    if (zwave) zacc[tm] += zs;
+                    av[tm] = __builtin_bit_cast(bf16x8_t, w);
+                }
+#pragma unroll
+                for (int tn = 0; tn < TPW; ++tn) {
+                    const unsigned short *pv = Vs + 16 * gi * D + vl[tn];
+                    u16x8_t x;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const unsigned short v = pv[2 * i * D];
+                        x[i] = tb + 2 * i < vrows ? v : (unsigned short)0;
+                    }
+                    bv[tn] = __builtin_bit_cast(bf16x8_t, x);
+                }
+#pragma unroll
+                for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < TPW; ++tn)
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+            }
+        }
+    }
+    wait_vmcnt<0>();      // the trailing out-of-range loads target the ring too
+    __syncthreads();
+
+    // ---- epilogue: S_part (row-major [k][v]) and z_part
+    const long unit = (bh * a.nb + c) * a.splits + s;
+    const auto rS = make_rsrc(a.S_part + unit * D * D, D * D * 4);
+    const auto rz = make_rsrc(a.z_part + unit * D, D * 4);
+#pragma unroll
+    for (int tm = 0; tm < TPW; ++tm) zacc[tm] += __shfl_xor(zacc[tm], 32);
+    if constexpr (SPLITK) {
+        float *red = (float *)(wave < 2 ? b0 : b1);   // 2 waves x 16 x 64 floats each
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((wave & 1) * 16 + r) * 64 + lane] = acc[0][0][r];
+        if (lane < 32) zred[wave * 32 + lane] = zacc[0];
+    } else {
+        if (zwave && lane < 32) {
+#pragma unroll
+            for (int tm = 0; tm < TPW; ++tm) zred[32 * (mt0 + tm) + lane] = zacc[tm];
+        }
+    }
+    __syncthreads();
+    if constexpr (SPLITK) {
+        const int e0 = tid * 4, rr = e0 / 32, c0 = e0 % 32;
+        const float *r01 = (const float *)b0, *r23 = (const float *)b1;
+        u32x4_t out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ln = (c0 + j) + 32 * ((rr >> 2) & 1);
+            const int r = 4 * (rr >> 3) + (rr & 3);
+            float v = r01[(0 * 16 + r) * 64 + ln];
+            v += r01[(1 * 16 + r) * 64 + ln];
+            v += r23[(0 * 16 + r) * 64 + ln];
+            v += r23[(1 * 16 + r) * 64 + ln];
+            out[j] = as_u32(v);
+        }
+        store16(rS, (uint32_t)(rr * D + c0) * 4u, out);
+        if (tid < D) {
+            float v = zred[tid];
+            v += zred[32 + tid];
+            v += zred[64 + tid];
+            v += zred[96 + tid];
+            store4(rz, (uint32_t)tid * 4u, v);
+        }
+    } else {
+#pragma unroll
+        for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TPW; ++tn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = 32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const int cc = 32 * (nt0 + tn) + m;
+                    store4(rS, (uint32_t)(rr * D + cc) * 4u, acc[tm][tn][r]);
+                }
+        if (tid < D) store4(rz, (uint32_t)tid * 4u, zred[tid]);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // svla_state_build, fp32 inputs: the same walk with fp32 rows staged and
 // v_mfma_f32_32x32x2_f32 (one token per half-wave per instruction).
 // ---------------------------------------------------------------------------
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool FUSE>
 __global__ void __launch_bounds__(kThreads)
 svla_state_build_f32(const BuildArgs a)
 {
@@ -486,9 +1018,10 @@ svla_state_build_f32(const BuildArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int s = blockIdx.x % a.splits;
-    const int c = (blockIdx.x / a.splits) % a.nb;
-    const long bh = blockIdx.x / ((long)a.splits * a.nb);
+    const unsigned per_bh = (unsigned)(a.splits * a.nb);
+    const long bh = blockIdx.x / per_bh;
+    const int rest = (int)(blockIdx.x - bh * per_bh);
+    const int c = rest / a.splits, s = rest % a.splits;
     const int tok_lo = c * a.n + s * a.chunk;
     const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
 
@@ -508,7 +1041,7 @@ svla_state_build_f32(const BuildArgs a)
         pp = rope_pairs<2>(a.rope, q * 4, nf);
         __syncthreads();
     }
-    unsigned char *stage = lds + (ROPE ? kMaxRopeEntries * 8 : 0);
+    unsigned char *stage = lds + (ROPE ? a.rope.tab_bytes : 0);
 
     float zacc[4] = {0.f, 0.f, 0.f, 0.f};
     f32x16_t acc[TPW][TPW];
@@ -614,90 +1147,7 @@ svla_state_build_f32(const BuildArgs a)
         for (int j = 0; j < kThreads / CPR; ++j) v += zred[(qq + CPR * j) * 4 + e];
         store4(rz, (uint32_t)tid * 4u, v);
     }
-}
-
-// ---------------------------------------------------------------------------
-// svla_state_scan.  Workgroup = (bh, 1024-element tile of S) or (bh, z).
-// Each thread owns 4 consecutive elements of S[k][v] and walks the blocks in
-// order: acc = g_c * acc + sum over splits, so the summation order is fixed
-// and the result repeats bit for bit.
-//
-// Packed operand layout read by svla_apply (per (bh, block), d*d entries):
-// bf16: fragment (m, ks) = 64 lanes x 8 values; lane (rho + 16 kg), value i
-//       holds S[32 ks + 8 kg + i][f(m, rho)]
-// fp32: fragment (m, kq) = 64 lanes x 4 values; lane (rho + 16 kg), value i
-//       holds S[16 kq + 4 kg + i][f(m, rho)]
-// with f(m, rho) = (d/4) (rho / 4) + 4 m + rho % 4: the output rows of the
-// MFMA land so that each lane ends up with consecutive O features.
-// ---------------------------------------------------------------------------
-template <int D, int MODE, bool OPBF16>
-__global__ void __launch_bounds__(kThreads)
-svla_state_scan_k(const ScanArgs a)
-{
-    constexpr int STILES = D * D / 1024;
-    const int tid = threadIdx.x;
-    const long bh = blockIdx.x / (STILES + 1);
-    const int tile = blockIdx.x % (STILES + 1);
-
-    if (tile < STILES) {
-        const int e0 = tile * 1024 + tid * 4;
-        const int k = e0 / D, v = e0 % D;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (MODE != SCAN_PACK && a.S_in) acc = *(const f32x4_t *)(a.S_in + bh * D * D + e0);
-        // operand positions of the 4 elements (k, v..v+3)
-        constexpr int MT = D / 16;
-        const int m = (v % (D / 4)) / 4, rho0 = 4 * (v / (D / 4));
-        int opos[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (OPBF16) {
-                const int ks = k / 32, kg = (k % 32) / 8, i = k % 8;
-                opos[j] = (((m * (D / 32) + ks) * 64 + rho0 + j + 16 * kg) * 8 + i);
-            } else {
-                const int kq = k / 16, kg = (k % 16) / 4, i = k % 4;
-                opos[j] = (((m * (D / 16) + kq) * 64 + rho0 + j + 16 * kg) * 4 + i);
-            }
-        }
-        (void)MT;
-        for (int c = 0; c < a.nb; ++c) {
-            const long unit = bh * a.nb + c;
-            if (MODE == SCAN_PACK) {
-                acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-            } else if (a.g) {
-                const float gm = a.g[unit];
-                acc *= gm;
-            }
-            for (int sp = 0; sp < a.splits; ++sp)
-                acc += *(const f32x4_t *)(a.S_part + (unit * a.splits + sp) * D * D + e0);
-            if (MODE == SCAN_EXPORT) {
-                *(f32x4_t *)(a.S_pre + unit * D * D + e0) = acc;
-            } else {
-                if constexpr (OPBF16) {
-                    unsigned short *op = (unsigned short *)a.S_op + unit * D * D;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) op[opos[j]] = f2bf(acc[j]);
-                } else {
-                    float *op = (float *)a.S_op + unit * D * D;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) op[opos[j]] = acc[j];
-                }
-            }
-        }
-        if (MODE != SCAN_PACK && a.S_fin) *(f32x4_t *)(a.S_fin + bh * D * D + e0) = acc;
-    } else if (MODE != SCAN_PACK) {
-        if (tid >= D / 4) return;
-        const int e0 = tid * 4;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (a.z_in) acc = *(const f32x4_t *)(a.z_in + bh * D + e0);
-        for (int c = 0; c < a.nb; ++c) {
-            const long unit = bh * a.nb + c;
-            if (a.g) acc *= a.g[unit];
-            for (int sp = 0; sp < a.splits; ++sp)
-                acc += *(const f32x4_t *)(a.z_part + (unit * a.splits + sp) * D + e0);
-            *(f32x4_t *)(a.z_pre + unit * D + e0) = acc;
-        }
-        if (a.z_fin) *(f32x4_t *)(a.z_fin + bh * D + e0) = acc;
-    }
+    if constexpr (FUSE) fused_scan<D, false>(a, bh, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -771,15 +1221,27 @@ svla_apply_bf16(const ApplyArgs a)
         __syncthreads();
     }
 
+    // groups of this wave: g_first, g_first + g_step, ...; the loads of GB
+    // groups are issued together before any of them is used.
+    constexpr int GB = SPLITM ? 2 : 4;
     const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
     const int g_first = SPLITM ? 0 : wave, g_step = SPLITM ? 1 : 4;
-    for (int gi = g_first; gi < ngroups; gi += g_step) {
-        const int tok = t_lo + 16 * gi + tl;
-        const bool valid = tok < t_hi;
-        u32x4_t qr[KS];
+    for (int gb = g_first; gb < ngroups; gb += GB * g_step) {
+    u32x4_t qb[GB][KS];
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+        const int tok = t_lo + 16 * (gb + j * g_step) + tl;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qr[ks] = load16(rQ, valid ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB);
+            qb[j][ks] = load16p<SPLITM ? 0 : SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB);
+    }
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+        const int gi = gb + j * g_step;
+        if (gi >= ngroups) break;
+        const int tok = t_lo + 16 * gi + tl;
+        const bool valid = tok < t_hi;
+        const u32x4_t *qr = qb[j];
         float den = 0.f;
         bf16x8_t qf[KS];
 #pragma unroll
@@ -825,8 +1287,9 @@ svla_apply_bf16(const ApplyArgs a)
                 o[2 * e + 1] = pack_bf16(acc[2 * h + e][2] * inv, acc[2 * h + e][3] * inv);
             }
             const int v0 = 4 * MT * kg + 4 * (m0 + 2 * h);
-            store16(rO, valid ? (uint32_t)(tok * D + v0) * 2u : kOOB, o);
+            store16p<SVLA_O_AUX>(rO, valid ? (uint32_t)(tok * D + v0) * 2u : kOOB, o);
         }
+    }
     }
 }
 
@@ -929,6 +1392,7 @@ svla_apply_f32(const ApplyArgs a)
     }
 }
 
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -942,14 +1406,15 @@ enum Slot { SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2 };
 // carries a start/stop event pair that the runtime records around the
 // kernel's own execution.
 template <typename Arg>
-void launch(void (*kernel)(Arg), unsigned grid, size_t lds, hipStream_t s, Slot slot, const Arg &a)
+void launch(void (*kernel)(Arg), unsigned grid, size_t lds, hipStream_t s, Slot slot, const Arg &a,
+            unsigned threads = kThreads)
 {
     const int e = 2 * (int)slot;
     if (t_events && e + 1 < t_nev)
-        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), (uint32_t)lds, s,
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), (uint32_t)lds, s,
                               (hipEvent_t)t_events[e], (hipEvent_t)t_events[e + 1], 0, a);
     else
-        kernel<<<dim3(grid), dim3(kThreads), lds, s>>>(a);
+        kernel<<<dim3(grid), dim3(threads), lds, s>>>(a);
 }
 
 svla_status fail(svla_status s, const char *fn, const char *fmt, ...) __attribute__((format(printf, 3, 4)));
@@ -982,28 +1447,42 @@ struct Plan {
     int esize;                 // bytes per Q/K/V/O element
     int splits, chunk;         // build
     int tile, tiles;           // apply
+    bool fuse;                 // scan runs in the build's last workgroup per (b,h)
     size_t lds_build, lds_apply;
-    size_t off_spart, off_zpart, off_sop, off_zpre, total;
+    size_t off_ctr, off_spart, off_zpart, off_sop, off_zpre, total;
     RopeK rope;
 };
 
+// A value that differs between any two calls of the process (see arrive()).
+unsigned next_epoch()
+{
+    static std::atomic<unsigned> e{(unsigned)std::chrono::steady_clock::now().time_since_epoch().count()};
+    return e.fetch_add(1, std::memory_order_relaxed);
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int stage_tokens(int d, int esize) { return kThreads / (d * esize / 16); }
+// bf16 state build: chunks per thread per stage and stages of loads in flight
+constexpr int build_u(bool rope) { return rope ? SVLA_BUILD_U_ROPE : SVLA_BUILD_U; }
+constexpr int build_pf(bool rope) { return rope ? SVLA_BUILD_PF_ROPE : SVLA_BUILD_PF; }
+
 
 // Splits of a block's tokens over workgroups: enough workgroups to fill the
-// chip (about 2048), but never fewer than 8*d tokens per split, so the fp32
-// partial state (4 d^2 bytes) stays under 1/8 of the K/V bytes it summarises.
-int pick_splits(long units, int n, int d, int TT, int *chunk_out)
+// chip (about SVLA_TARGET_WGS), but never fewer than SVLA_MIN_SPLIT_PER_D * d
+// tokens per split, so the fp32 partial state (4 d^2 bytes) stays a small
+// fraction of the K/V bytes it summarises (1/8 at the default).
+int pick_splits(long units, int n, int d, int *chunk_out)
 {
-    if (n <= 0 || units <= 0) { *chunk_out = TT; return 0; }
-    long want = (2048 + units - 1) / units;
-    long cap = n / (8 * d);
+    constexpr int G = 64;   // chunk granularity; independent of the stage size, so the
+                            // workspace size does not depend on RoPE or tuning
+    if (n <= 0 || units <= 0) { *chunk_out = G; return 0; }
+    long want = (SVLA_TARGET_WGS + units - 1) / units;
+    long cap = n / (SVLA_MIN_SPLIT_PER_D * d);
     if (cap < 1) cap = 1;
     long s = want < cap ? want : cap;
     if (s < 1) s = 1;
     int chunk = (int)((n + s - 1) / s);
-    chunk = (chunk + TT - 1) / TT * TT;
+    chunk = (chunk + G - 1) / G * G;
     *chunk_out = chunk;
     return (n + chunk - 1) / chunk;
 }
@@ -1062,19 +1541,18 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     p->esize = dt == SVLA_BF16 ? 2 : 4;
     st = check_rope(fn, rope, d, &p->rope);
     if (st) return st;
-    const int TT = stage_tokens(d, p->esize);
     if (op == SVLA_OP_STATE_BUILD) {
         p->splits = n > 0 ? 1 : 0;
-        p->chunk = (n + TT - 1) / TT * TT;
-        if (p->chunk == 0) p->chunk = TT;
+        p->chunk = n > 0 ? n : 1;
     } else {
-        p->splits = pick_splits(p->BH * nb, n, d, TT, &p->chunk);
+        p->splits = pick_splits(p->BH * nb, n, d, &p->chunk);
     }
     p->tile = d == 128 ? 128 : 256;
     p->tiles = n > 0 ? (n + p->tile - 1) / p->tile : 0;
 
     // LDS: [RoPE table][stage buffers | epilogue]
-    const size_t stage = (size_t)2 * ((p->esize == 2 && p->rope.on) ? 3 : 2) * 4096;
+    const size_t stage = (size_t)2 * ((p->esize == 2 && p->rope.on) ? 3 : 2) * 4096 *
+                         (p->esize == 2 ? build_u(p->rope.on) : 1);
     const size_t epi = (d == 32 ? 16384 : 0) + 8192;
     p->lds_build = stage > epi ? stage : epi;
     p->lds_apply = 0;
@@ -1088,15 +1566,21 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
             return fail(SVLA_ERR_UNSUPPORTED, fn,
                         "RoPE table of %ld entries exceeds %d (grid %dx%d too large)",
                         eb > ea ? eb : ea, kMaxRopeEntries, p->rope.gh, p->rope.gw);
-        p->lds_build += (size_t)kMaxRopeEntries * 8;
-        p->lds_apply = (size_t)kMaxRopeEntries * 8;
+        // the table takes only what the largest range of this call needs
+        // (build and apply share it: the larger of the two)
+        const long e = eb > ea ? eb : ea;
+        p->rope.tab_bytes = (int)((e * 8 + 255) & ~255L);
+        p->lds_build += (size_t)p->rope.tab_bytes;
+        p->lds_apply = (size_t)p->rope.tab_bytes;
     }
 
     // workspace
     size_t off = 0;
     const size_t units = (size_t)p->BH * nb;
     const bool fused = op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP;
+    p->fuse = fused && d <= SVLA_FUSE_MAX_D && p->splits > 0 && nb > 0;
     if (fused) {
+        p->off_ctr = off; off = align256(off + (size_t)p->BH * 8);
         p->off_spart = off; off = align256(off + units * p->splits * d * d * 4);
         p->off_zpart = off; off = align256(off + units * p->splits * d * 4);
     }
@@ -1114,25 +1598,44 @@ inline bool misaligned(const void *ptr) { return ((uintptr_t)ptr & 15) != 0; }
 
 // ---- launchers ---------------------------------------------------------------
 
+template <int D, bool FUSE>
+void launch_build_f(const Plan &p, const BuildArgs &a, hipStream_t s)
+{
+    const unsigned grid = (unsigned)(p.BH * p.nb * p.splits);
+    if (SVLA_USE_DMA && p.esize == 2 && !p.rope.on && !FUSE) {
+        constexpr int U = D == 32 ? SVLA_DMA_U32 : SVLA_DMA_U;
+        constexpr int R = D == 32 ? SVLA_DMA_R32 : SVLA_DMA_R;
+        launch(svla_state_build_dma<D, U, R>, grid, 0, s, SLOT_BUILD, a);
+        return;
+    }
+    if (p.esize == 2) {
+        if (p.rope.on)
+            launch(svla_state_build_bf16<D, true, build_pf(true), build_u(true), FUSE>, grid,
+                   p.lds_build, s, SLOT_BUILD, a);
+        else
+            launch(svla_state_build_bf16<D, false, build_pf(false), build_u(false), FUSE>, grid,
+                   p.lds_build, s, SLOT_BUILD, a);
+    } else {
+        if (p.rope.on) launch(svla_state_build_f32<D, true, FUSE>, grid, p.lds_build, s, SLOT_BUILD, a);
+        else launch(svla_state_build_f32<D, false, FUSE>, grid, p.lds_build, s, SLOT_BUILD, a);
+    }
+}
+
 template <int D>
 void launch_build(const Plan &p, const BuildArgs &a, hipStream_t s)
 {
-    const unsigned grid = (unsigned)(p.BH * p.nb * p.splits);
-    if (p.esize == 2) {
-        if (p.rope.on) launch(svla_state_build_bf16<D, true>, grid, p.lds_build, s, SLOT_BUILD, a);
-        else launch(svla_state_build_bf16<D, false>, grid, p.lds_build, s, SLOT_BUILD, a);
-    } else {
-        if (p.rope.on) launch(svla_state_build_f32<D, true>, grid, p.lds_build, s, SLOT_BUILD, a);
-        else launch(svla_state_build_f32<D, false>, grid, p.lds_build, s, SLOT_BUILD, a);
+    if constexpr (D <= SVLA_FUSE_MAX_D) {
+        if (p.fuse) { launch_build_f<D, true>(p, a, s); return; }
     }
+    launch_build_f<D, false>(p, a, s);
 }
 
 template <int D, int MODE>
 void launch_scan_d(const Plan &p, const ScanArgs &a, hipStream_t s)
 {
-    const unsigned grid = (unsigned)(p.BH * (D * D / 1024 + 1));
-    if (p.esize == 2) launch(svla_state_scan_k<D, MODE, true>, grid, 0, s, SLOT_SCAN, a);
-    else launch(svla_state_scan_k<D, MODE, false>, grid, 0, s, SLOT_SCAN, a);
+    const unsigned grid = (unsigned)(p.BH * (D * D / (kScanThreads * 4) + 1));
+    if (p.esize == 2) launch(svla_state_scan_k<D, MODE, true>, grid, 0, s, SLOT_SCAN, a, kScanThreads);
+    else launch(svla_state_scan_k<D, MODE, false>, grid, 0, s, SLOT_SCAN, a, kScanThreads);
 }
 
 template <int D>
@@ -1208,16 +1711,6 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
     (void)hipGetLastError();
-    if (p.splits > 0 && nb > 0) {
-        BuildArgs ba;
-        ba.K = K; ba.V = V;
-        ba.S_part = (float *)(w + p.off_spart);
-        ba.z_part = (float *)(w + p.off_zpart);
-        ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = p.splits; ba.chunk = p.chunk;
-        ba.rope = p.rope;
-        build_any(p, ba, s);
-        if ((st = check_launch(fn))) return st;
-    }
     ScanArgs sa;
     memset(&sa, 0, sizeof sa);
     sa.S_part = (const float *)(w + p.off_spart);
@@ -1227,8 +1720,26 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
     sa.z_pre = (float *)(w + p.off_zpre);
     sa.S_fin = S_fin; sa.z_fin = z_fin;
     sa.nb = nb; sa.splits = p.splits;
-    scan_any<SCAN_FUSED>(p, sa, s);
-    if ((st = check_launch(fn))) return st;
+    if (p.splits > 0 && nb > 0) {
+        BuildArgs ba;
+        memset(&ba, 0, sizeof ba);
+        ba.K = K; ba.V = V;
+        ba.S_part = (float *)(w + p.off_spart);
+        ba.z_part = (float *)(w + p.off_zpart);
+        ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = p.splits; ba.chunk = p.chunk;
+        ba.rope = p.rope;
+        if (p.fuse) {
+            ba.counters = (unsigned long long *)(w + p.off_ctr);
+            ba.epoch = next_epoch();
+            ba.scan = sa;
+        }
+        build_any(p, ba, s);
+        if ((st = check_launch(fn))) return st;
+    }
+    if (!p.fuse) {
+        scan_any<SCAN_FUSED>(p, sa, s);
+        if ((st = check_launch(fn))) return st;
+    }
     if (tokens) {
         ApplyArgs aa;
         aa.Q = Q; aa.O = O; aa.S_op = w + p.off_sop; aa.z_pre = (const float *)(w + p.off_zpre);
@@ -1367,6 +1878,7 @@ svla_status svla_state_build(svla_dtype dt, int B, int H, int nb, int n, int d, 
         return check_launch(fn);
     }
     BuildArgs ba;
+    memset(&ba, 0, sizeof ba);
     ba.K = K; ba.V = V; ba.S_part = S_local; ba.z_part = z_local;
     ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = 1; ba.chunk = p.chunk; ba.rope = p.rope;
     build_any(p, ba, s);
