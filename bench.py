@@ -170,6 +170,16 @@ class Workload:
                 svla.block_causal(q, k, v, self.nb, g=self.g, rope=self.cfg.rope, out=o,
                                   workspace=self.ws)
 
+    def describe_plan(self) -> dict:
+        """The library's launch plan for one call of this workload."""
+        torch = self.torch
+        if self.stream_mode:
+            return self.svla.describe("block_step", torch.bfloat16, self.B, self.H, 1, self.n,
+                                      self.d, rope=self.ropes[0])
+        op = "noncausal" if self.nb == 1 else "block_causal"
+        return self.svla.describe(op, torch.bfloat16, self.B, self.H, self.nb, self.n, self.d,
+                                  rope=self.cfg.rope)
+
     def describe(self) -> dict:
         c = self.cfg
         d = {"workload": "%s: %s" % (c.name, c.description), "B": c.B, "H": c.H, "N": c.N,
@@ -363,8 +373,8 @@ def main():
     dominant = max(("build", "apply"), key=lambda k: kern[k])
     dur_s = kern[dominant] * 1e-3
     achieved = ab["per_launch"][dominant] / dur_s / 1e9
-    kname = {"build": "svla_state_build_bf16", "apply": "svla_apply_bf16"}[dominant]
-    kernel_full = "void %s<%d, %s>" % (kname, w.d, "true" if w.cfg.rope is not None else "false")
+    plan = w.describe_plan()
+    kernel_full = {k["slot"]: k["name"] for k in plan["kernels"]}[dominant]
     traffic = load_traffic(args.config, kernel_full, w.launches_per_step())
     path_gbps = ab["path"] / (ms * 1e-3) / 1e9
     line = {
@@ -388,7 +398,8 @@ def main():
                      "avg_launch_ms": kern[dominant]},
         "path": {"algorithmic_bytes_per_step": ab["path"], "achieved_GBps": path_gbps,
                  "frac_of_peak": path_gbps / HBM_PEAK_GBPS,
-                 "kernel_ms_per_launch": kern, "launches_per_step": w.launches_per_step()},
+                 "kernel_ms_per_launch": kern, "launches_per_step": w.launches_per_step(),
+                 "plan": plan},
         "source_sha256": source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -25,7 +25,7 @@ from . import _lib
 from ._lib import SvlaError, rope_struct  # noqa: F401
 
 __all__ = ["noncausal", "block_causal", "block_step", "state_build", "state_scan", "apply",
-           "workspace_size", "set_timing_events", "SvlaError", "library"]
+           "workspace_size", "describe", "set_timing_events", "SvlaError", "library"]
 
 _DT = {torch.bfloat16: _lib.SVLA_BF16, torch.float32: _lib.SVLA_F32}
 _OPS = {"noncausal": _lib.OP_NONCAUSAL, "block_causal": _lib.OP_BLOCK_CAUSAL,
@@ -74,6 +74,17 @@ def workspace_size(op: str, dtype: torch.dtype, B: int, H: int, nb: int, n: int,
     _lib.check(lib, lib.svla_workspace_size(_OPS[op], _DT[dtype], B, H, nb, n, d,
                                             ctypes.byref(out)))
     return int(out.value)
+
+
+def describe(op: str, dtype: torch.dtype, B: int, H: int, nb: int, n: int, d: int, rope=None) -> dict:
+    """The launch plan of a fused call (kernel names, grids, splits, workspace)."""
+    import json
+    lib = library()
+    buf = ctypes.create_string_buffer(4096)
+    rs = rope_struct(rope)
+    _lib.check(lib, lib.svla_describe(_OPS[op], _DT[dtype], B, H, nb, n, d,
+                                      ctypes.byref(rs) if rs is not None else None, buf, 4096))
+    return json.loads(buf.value.decode())
 
 
 def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:

@@ -55,6 +55,7 @@ PROTOTYPES = {
     "svla_state_scan": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "svla_apply": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _rp, _f, _vp, _vp, _sz, _vp]),
     "svla_set_timing_events": (_i, [ctypes.POINTER(_vp), _i]),
+    "svla_describe": (_i, [_i, _i, _i, _i, _i, _i, _i, _rp, ctypes.c_char_p, _sz]),
 }
 
 _lib = None

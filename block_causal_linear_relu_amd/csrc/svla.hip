@@ -26,6 +26,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <type_traits>
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -42,7 +43,7 @@
 #define SVLA_BUILD_U 2             // 16-byte K and V chunks per thread per stage
 #endif
 #ifndef SVLA_BUILD_PF_ROPE
-#define SVLA_BUILD_PF_ROPE 1       // the same two knobs for the RoPE build
+#define SVLA_BUILD_PF_ROPE 2       // the same two knobs for the RoPE build
 #endif
 #ifndef SVLA_BUILD_U_ROPE
 #define SVLA_BUILD_U_ROPE 1
@@ -58,6 +59,18 @@
 #endif
 #ifndef SVLA_DMA_R
 #define SVLA_DMA_R 4
+#endif
+#ifndef SVLA_QUAD128
+#define SVLA_QUAD128 1             // d = 128 build: one workgroup per 64 x 64 quadrant of S
+#endif
+#ifndef SVLA_APPLY_TILE32
+#define SVLA_APPLY_TILE32 256      // apply: tokens per workgroup for d = 32, 64
+#endif
+#ifndef SVLA_APPLY_TILE_ROPE
+#define SVLA_APPLY_TILE_ROPE 512   // ... with RoPE (amortises the per-workgroup angle table)
+#endif
+#ifndef SVLA_APPLY_TILE128
+#define SVLA_APPLY_TILE128 128     // ... and for d = 128
 #endif
 #ifndef SVLA_USE_DMA
 #define SVLA_USE_DMA 1             // non-RoPE bf16 builds load straight to LDS
@@ -246,16 +259,18 @@ __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
         sincospif(2.0f * (float)turns, &s, &c);
         tab[e] = make_float2(c, s);
     }
+    if (threadIdx.x == 0) tab[total] = make_float2(1.f, 0.f);   // identity, for unrotated dims
 }
 
 // Per-thread description of the 4 (bf16 chunk) or 2 (fp32 chunk) pairs of
-// its fixed feature chunk: which axis each pair rotates with and where its
-// table column starts.
+// its fixed feature chunk.  A pair's table index for a token at (frame
+// offset fr, row, col) is base + fr * mt + row * mh + col * mw, with exactly
+// one multiplier non-zero for a rotated pair; a pair outside the three
+// slices points at the identity entry (cos 1, sin 0) that ends the table, so
+// the rotation has no branches.
 template <int PAIRS>
 struct RopePairs {
-    int sel[PAIRS];      // 0 frame, 1 row, 2 col, 3 none
-    int base[PAIRS];     // table index of position 0 for this pair
-    int stride[PAIRS];   // table entries per position on that axis
+    int base[PAIRS], mt[PAIRS], mh[PAIRS], mw[PAIRS];
 };
 
 template <int PAIRS>
@@ -267,36 +282,44 @@ __device__ __forceinline__ RopePairs<PAIRS> rope_pairs(const RopeK &r, int first
 #pragma unroll
     for (int j = 0; j < PAIRS; ++j) {
         int f = first_feature + 2 * j;
+        p.mt[j] = p.mh[j] = p.mw[j] = 0;
         if (f < r.dt) {
-            p.sel[j] = 0; p.base[j] = f / 2; p.stride[j] = pt;
+            p.base[j] = f / 2; p.mt[j] = pt;
         } else if (f < r.dt + r.dh) {
-            p.sel[j] = 1; p.base[j] = offH + (f - r.dt) / 2; p.stride[j] = ph;
+            p.base[j] = offH + (f - r.dt) / 2; p.mh[j] = ph;
         } else if (f < r.dt + r.dh + r.dw) {
-            p.sel[j] = 2; p.base[j] = offW + (f - r.dt - r.dh) / 2; p.stride[j] = pw;
+            p.base[j] = offW + (f - r.dt - r.dh) / 2; p.mw[j] = pw;
         } else {
-            p.sel[j] = 3; p.base[j] = 0; p.stride[j] = 0;
+            p.base[j] = rope_entries(r, nf);       // the identity entry
         }
     }
     return p;
 }
 
-// Rotate x[2j], x[2j+1] of token p (call position) by its angles;
-// frame_lo = p_lo / (gh*gw) of the table's first frame.
-template <int PAIRS>
-__device__ __forceinline__ void rope_rotate(float *x, uint32_t p, uint32_t frame_lo,
-                                            const RopeK &r, const RopePairs<PAIRS> &pp,
-                                            const float2 *tab)
+// Position of call token p: frame offset from the table's first frame, grid
+// row, grid column.
+struct RopePos {
+    int fr, row, col;
+};
+
+__device__ __forceinline__ RopePos rope_pos(uint32_t p, uint32_t frame_lo, const RopeK &r)
 {
-    uint32_t fr = fdiv(p, r.div_hw);
-    uint32_t rem = p - fr * (uint32_t)(r.gh * r.gw);
-    uint32_t row = fdiv(rem, r.div_w);
-    uint32_t col = rem - row * (uint32_t)r.gw;
-    int pos[4] = {(int)(fr - frame_lo), (int)row, (int)col, 0};
+    const uint32_t fr = fdiv(p, r.div_hw);
+    const uint32_t rem = p - fr * (uint32_t)(r.gh * r.gw);
+    const uint32_t row = fdiv(rem, r.div_w);
+    return RopePos{(int)(fr - frame_lo), (int)row, (int)(rem - row * (uint32_t)r.gw)};
+}
+
+// Rotate x[2j], x[2j+1] by the angles of the token at `pos`.
+template <int PAIRS>
+__device__ __forceinline__ void rope_rotate(float *x, const RopePos &pos,
+                                            const RopePairs<PAIRS> &pp, const float2 *tab)
+{
 #pragma unroll
     for (int j = 0; j < PAIRS; ++j) {
-        if (pp.sel[j] == 3) continue;
-        float2 cs = tab[pp.base[j] + pos[pp.sel[j]] * pp.stride[j]];
-        float x0 = x[2 * j], x1 = x[2 * j + 1];
+        const int idx = pp.base[j] + pos.fr * pp.mt[j] + pos.row * pp.mh[j] + pos.col * pp.mw[j];
+        const float2 cs = tab[idx];
+        const float x0 = x[2 * j], x1 = x[2 * j + 1];
         x[2 * j] = x0 * cs.x - x1 * cs.y;
         x[2 * j + 1] = x0 * cs.y + x1 * cs.x;
     }
@@ -320,6 +343,7 @@ struct BuildArgs {
     const void *K, *V;
     float *S_part, *z_part;        // [BH*nb*splits][d*d], [BH*nb*splits][d]
     int N, n, nb, splits, chunk;   // chunk: tokens per split (multiple of the stage)
+    long BH;
     RopeK rope;
     unsigned long long *counters;  // [BH] arrival counters of the fused scan
     unsigned epoch;                // distinct per call (see arrive())
@@ -627,6 +651,19 @@ svla_state_build_bf16(const BuildArgs a)
     const int m = lane & 31, g = lane >> 5;
     const int mt0 = SPLITK ? 0 : (wave >> 1) * TPW;
     const int nt0 = SPLITK ? 0 : (wave & 1) * TPW;
+    constexpr int GPW = SPLITK ? GPS / 4 : GPS;  // 16-token groups per wave per stage
+    // lane part of a fragment element's LDS index (k-slot i reads row 16 gi + g + 2 i)
+    int kl[TPW], vl[TPW];
+#pragma unroll
+    for (int tm = 0; tm < TPW; ++tm) {
+        const int f = 32 * (mt0 + tm) + m;
+        kl[tm] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
+    }
+#pragma unroll
+    for (int tn = 0; tn < TPW; ++tn) {
+        const int f = 32 * (nt0 + tn) + m;
+        vl[tn] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
+    }
 
     for (int it0 = 0; it0 < nstages; it0 += PF) {
 #pragma unroll
@@ -651,7 +688,7 @@ svla_state_build_bf16(const BuildArgs a)
                 for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
                 const int cpos = swz16<D>(r, q);
                 if constexpr (ROPE) {
-                    rope_rotate<4>(kf, (uint32_t)tok, frame_lo, a.rope, pp, tab);
+                    rope_rotate<4>(kf, rope_pos((uint32_t)tok, frame_lo, a.rope), pp, tab);
                     u32x4_t hi, lo;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -682,32 +719,28 @@ svla_state_build_bf16(const BuildArgs a)
             const unsigned short *Kl = (const unsigned short *)(st + TILEB);
             const unsigned short *Vs = (const unsigned short *)(st + NK * TILEB);
 #pragma unroll
-            for (int gi = 0; gi < GPS; ++gi) {
-                if (SPLITK && (gi & 3) != wave) continue;   // d = 32: waves split the groups
-                int t[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) t[i] = 16 * gi + 2 * i + g;
+            for (int gg = 0; gg < GPW; ++gg) {
+                const int gi = SPLITK ? wave + 4 * gg : gg;
                 bf16x8_t av[TPW], al[TPW], bv[TPW];
 #pragma unroll
                 for (int tm = 0; tm < TPW; ++tm) {
-                    const int f = 32 * (mt0 + tm) + m;
+                    const unsigned short *ph = Kh + 16 * gi * D + kl[tm];
+                    const unsigned short *pl = Kl + 16 * gi * D + kl[tm];
                     u16x8_t x, y;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const int idx = t[i] * D + swz16<D>(t[i], f >> 3) * 8 + (f & 7);
-                        x[i] = Kh[idx];
-                        if constexpr (ROPE) y[i] = Kl[idx];
+                        x[i] = ph[2 * i * D];
+                        if constexpr (ROPE) y[i] = pl[2 * i * D];
                     }
                     av[tm] = __builtin_bit_cast(bf16x8_t, x);
                     if constexpr (ROPE) al[tm] = __builtin_bit_cast(bf16x8_t, y);
                 }
 #pragma unroll
                 for (int tn = 0; tn < TPW; ++tn) {
-                    const int f = 32 * (nt0 + tn) + m;
+                    const unsigned short *pv = Vs + 16 * gi * D + vl[tn];
                     u16x8_t x;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        x[i] = Vs[t[i] * D + swz16<D>(t[i], f >> 3) * 8 + (f & 7)];
+                    for (int i = 0; i < 8; ++i) x[i] = pv[2 * i * D];
                     bv[tn] = __builtin_bit_cast(bf16x8_t, x);
                 }
 #pragma unroll
@@ -796,10 +829,13 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int D, int U, int R>
+template <int D, int U, int R, int DG>
 __global__ void __launch_bounds__(kThreads)
 svla_state_build_dma(const BuildArgs a)
 {
+    // D: width of the tile this workgroup contracts; DG: feature count of the
+    // data.  DG == 2 D is the quadrant split for d = 128: four workgroups per
+    // (b,h,block,split), each computing one 64 x 64 quadrant of S.
     constexpr int CPR = D / 8;            // 16-byte chunks per token row
     constexpr int RPW = 64 / CPR;         // rows one wave instruction covers
     constexpr int RPS = kThreads / CPR;   // rows one pass of the 4 waves covers
@@ -811,8 +847,10 @@ svla_state_build_dma(const BuildArgs a)
     constexpr int TPW = SPLITK ? 1 : D / 64;
     constexpr int GPS = TT / 16;
     constexpr int L = 2 * U;              // loads per thread per stage
+    constexpr bool QUAD = DG != D;
     static_assert(R >= 3 && R <= 4, "ring depth");
     static_assert(!SPLITK || STAGEB >= 8192, "epilogue reuses two stage buffers");
+    static_assert(!QUAD || (DG == 128 && D == 64), "quadrant split is for d = 128");
 
     __shared__ __attribute__((aligned(16))) unsigned char b0[STAGEB];
     __shared__ __attribute__((aligned(16))) unsigned char b1[STAGEB];
@@ -821,16 +859,30 @@ svla_state_build_dma(const BuildArgs a)
     __shared__ float zred[4 * D];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Quadrants of one unit get workgroup ids 8 apart, so the round-robin
+    // dispatch puts all four on the same XCD and its L2 serves the shared
+    // K/V half-rows.
+    long wid = blockIdx.x;
+    int qm = 0, qn = 0;
+    if constexpr (QUAD) {
+        const long x = wid % 8, r = wid / 8;
+        const int q = (int)(r % 4);
+        qm = q >> 1;
+        qn = q & 1;
+        wid = (r / 4) * 8 + x;
+        if (wid >= (long)a.nb * a.splits * a.BH) return;
+    }
     const unsigned per_bh = (unsigned)(a.splits * a.nb);
-    const long bh = blockIdx.x / per_bh;
-    const int rest = (int)(blockIdx.x - bh * per_bh);
+    const long bh = wid / per_bh;
+    const int rest = (int)(wid - bh * per_bh);
     const int c = rest / a.splits, s = rest % a.splits;
     const int tok_lo = c * a.n + s * a.chunk;
     const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
 
-    const uint32_t slice = (uint32_t)a.N * D * 2;
+    const uint32_t slice = (uint32_t)a.N * DG * 2;
     const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
     const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
+    const int kcol = 64 * qm, vcol = 64 * qn;   // first feature of this tile in K / V
 
     auto buf = [&](int j) -> unsigned char * {
         return j == 0 ? b0 : j == 1 ? b1 : j == 2 ? b2 : b3;
@@ -843,16 +895,24 @@ svla_state_build_dma(const BuildArgs a)
             const int r = (u * 4 + wave) * RPW + lane / CPR;
             const int t = tok_lo + st * TT + r;
             const int cg = swz16<D>(r, lane % CPR);
-            const uint32_t off = t < tok_hi ? (uint32_t)(t * D + cg * 8) * 2u : kOOB;
+            const bool in = t < tok_hi;
+            const uint32_t offk = in ? (uint32_t)(t * DG + kcol + cg * 8) * 2u : kOOB;
+            const uint32_t offv = in ? (uint32_t)(t * DG + vcol + cg * 8) * 2u : kOOB;
             unsigned char *kd = dst + (u * 4 + wave) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)kd, 16, off, 0, 0, SVLA_KV_AUX);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(kd + TILEB), 16, off, 0, 0, SVLA_KV_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)kd, 16, offk, 0, 0, SVLA_KV_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(kd + TILEB), 16, offv, 0, 0, SVLA_KV_AUX);
         }
     };
 
-    float zacc[TPW];
+    f32x16_t zt[TPW];                     // phi(K) x ones: every column holds z
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) zacc[i] = 0.f;
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zt[i][r] = 0.f;
+    u16x8_t ones16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones16[i] = 0x3F80;   // bf16 1.0
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones16);
     f32x16_t acc[TPW][TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i)
@@ -890,46 +950,48 @@ svla_state_build_dma(const BuildArgs a)
         for (int j = 0; j < R; ++j) {
             const int it = it0 + j;
             wait_vmcnt<(R - 2) * L>();     // this wave's loads of stage `it` have landed
+            // Rows past the range (only in a workgroup's last stages): the lane
+            // that loaded a slot overwrites it with zeros, so they add nothing
+            // whatever an out-of-range load left there.
+            if (tok_lo + (it + 1) * TT > tok_hi) {
+                const int vrows = tok_hi - (tok_lo + it * TT);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int r = (u * 4 + wave) * RPW + lane / CPR;
+                    if (r >= vrows) {
+                        unsigned char *slot = buf(j) + (u * 4 + wave) * 1024 + lane * 16;
+                        *(u32x4_t *)slot = (u32x4_t){0u, 0u, 0u, 0u};
+                        *(u32x4_t *)(slot + TILEB) = (u32x4_t){0u, 0u, 0u, 0u};
+                    }
+                }
+            }
             lds_barrier();                 // ... everyone's have; stage it-1 is consumed
             issue(buf((j + R - 1) % R), it + R - 1);
-            // Stages past the range are computed too, fully masked (they add
-            // zero), so the stage body has no branch around the accumulators.
             const unsigned short *Ks = (const unsigned short *)buf(j);
             const unsigned short *Vs = Ks + TT * D;
-            const int vrows = tok_hi - (tok_lo + it * TT);   // valid rows of this stage
 #pragma unroll
             for (int gg = 0; gg < GPW; ++gg) {
                 const int gi = SPLITK ? wave + 4 * gg : gg;
-                const int tb = 16 * gi + g;            // k-slot i reads token row tb + 2 i
                 bf16x8_t av[TPW], bv[TPW];
 #pragma unroll
                 for (int tm = 0; tm < TPW; ++tm) {
                     const unsigned short *pk = Ks + 16 * gi * D + kl[tm];
                     u16x8_t x;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const unsigned short v = pk[2 * i * D];
-                        x[i] = tb + 2 * i < vrows ? v : (unsigned short)0;
-                    }
+                    for (int i = 0; i < 8; ++i) x[i] = pk[2 * i * D];
                     u32x4_t w = __builtin_bit_cast(u32x4_t, x);
-                    float zs = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        w[e] = relu_bf16x2(w[e]);
-                        zs += bf16lo(w[e]) + bf16hi(w[e]);
-                    }
-                    if (zwave) zacc[tm] += zs;
+                    for (int e = 0; e < 4; ++e) w[e] = relu_bf16x2(w[e]);
                     av[tm] = __builtin_bit_cast(bf16x8_t, w);
+                    // z on the matrix cores: phi(K) times a ones operand
+                    if (zwave) zt[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], ones, zt[tm], 0, 0, 0);
                 }
 #pragma unroll
                 for (int tn = 0; tn < TPW; ++tn) {
                     const unsigned short *pv = Vs + 16 * gi * D + vl[tn];
                     u16x8_t x;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const unsigned short v = pv[2 * i * D];
-                        x[i] = tb + 2 * i < vrows ? v : (unsigned short)0;
-                    }
+                    for (int i = 0; i < 8; ++i) x[i] = pv[2 * i * D];
                     bv[tn] = __builtin_bit_cast(bf16x8_t, x);
                 }
 #pragma unroll
@@ -945,19 +1007,23 @@ svla_state_build_dma(const BuildArgs a)
 
     // ---- epilogue: S_part (row-major [k][v]) and z_part
     const long unit = (bh * a.nb + c) * a.splits + s;
-    const auto rS = make_rsrc(a.S_part + unit * D * D, D * D * 4);
-    const auto rz = make_rsrc(a.z_part + unit * D, D * 4);
-#pragma unroll
-    for (int tm = 0; tm < TPW; ++tm) zacc[tm] += __shfl_xor(zacc[tm], 32);
+    const auto rS = make_rsrc(a.S_part + unit * DG * DG, DG * DG * 4);
+    const auto rz = make_rsrc(a.z_part + unit * DG, DG * 4);
+    // z: column 0 of each zt tile, held by lanes 0 (rows 8q + r, r < 4) and 32 (rows 8q + 4 + r)
     if constexpr (SPLITK) {
         float *red = (float *)(wave < 2 ? b0 : b1);   // 2 waves x 16 x 64 floats each
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[((wave & 1) * 16 + r) * 64 + lane] = acc[0][0][r];
-        if (lane < 32) zred[wave * 32 + lane] = zacc[0];
-    } else {
-        if (zwave && lane < 32) {
+        if ((lane & 31) == 0) {
 #pragma unroll
-            for (int tm = 0; tm < TPW; ++tm) zred[32 * (mt0 + tm) + lane] = zacc[tm];
+            for (int r = 0; r < 16; ++r) zred[wave * 32 + 8 * (r >> 2) + 4 * g + (r & 3)] = zt[0][r];
+        }
+    } else {
+        if (zwave && (lane & 31) == 0) {
+#pragma unroll
+            for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) zred[32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3)] = zt[tm][r];
         }
     }
     __syncthreads();
@@ -990,11 +1056,11 @@ svla_state_build_dma(const BuildArgs a)
             for (int tn = 0; tn < TPW; ++tn)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int rr = 32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const int cc = 32 * (nt0 + tn) + m;
-                    store4(rS, (uint32_t)(rr * D + cc) * 4u, acc[tm][tn][r]);
+                    const int rr = kcol + 32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const int cc = vcol + 32 * (nt0 + tn) + m;
+                    store4(rS, (uint32_t)(rr * DG + cc) * 4u, acc[tm][tn][r]);
                 }
-        if (tid < D) store4(rz, (uint32_t)tid * 4u, zred[tid]);
+        if (tid < D && qn == 0) store4(rz, (uint32_t)(kcol + tid) * 4u, zred[tid]);
     }
 }
 
@@ -1069,7 +1135,7 @@ svla_state_build_f32(const BuildArgs a)
             kf[e] = fmaxf(as_f32(kreg[e]), 0.f);
             zacc[e] += kf[e];
         }
-        if constexpr (ROPE) rope_rotate<2>(kf, (uint32_t)tok, frame_lo, a.rope, pp, tab);
+        if constexpr (ROPE) rope_rotate<2>(kf, rope_pos((uint32_t)tok, frame_lo, a.rope), pp, tab);
         u32x4_t kw;
 #pragma unroll
         for (int e = 0; e < 4; ++e) kw[e] = as_u32(kf[e]);
@@ -1244,6 +1310,8 @@ svla_apply_bf16(const ApplyArgs a)
         const u32x4_t *qr = qb[j];
         float den = 0.f;
         bf16x8_t qf[KS];
+        RopePos rp{0, 0, 0};
+        if constexpr (ROPE) rp = rope_pos((uint32_t)tok, frame_lo, a.rope);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4_t p;
@@ -1258,7 +1326,7 @@ svla_apply_bf16(const ApplyArgs a)
 #pragma unroll
             for (int e = 0; e < 8; ++e) den = fmaf(pf[e], zf[ks][e], den);
             if constexpr (ROPE) {
-                rope_rotate<4>(pf, (uint32_t)tok, frame_lo, a.rope, pp[ks], tab);
+                rope_rotate<4>(pf, rp, pp[ks], tab);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) p[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
             }
@@ -1357,6 +1425,8 @@ svla_apply_f32(const ApplyArgs a)
         const bool valid = tok < t_hi;
         float qv[KQ][4];
         float den = 0.f;
+        RopePos rp{0, 0, 0};
+        if constexpr (ROPE) rp = rope_pos((uint32_t)tok, frame_lo, a.rope);
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
             u32x4_t r = load16(rQ, valid ? (uint32_t)(tok * D + 4 * (4 * kq + kg)) * 4u : kOOB);
@@ -1365,7 +1435,7 @@ svla_apply_f32(const ApplyArgs a)
                 qv[kq][e] = fmaxf(as_f32(r[e]), 0.f);
                 den = fmaf(qv[kq][e], zf[kq][e], den);
             }
-            if constexpr (ROPE) rope_rotate<2>(qv[kq], (uint32_t)tok, frame_lo, a.rope, pp[kq], tab);
+            if constexpr (ROPE) rope_rotate<2>(qv[kq], rp, pp[kq], tab);
         }
         den += __shfl_xor(den, 16);
         den += __shfl_xor(den, 32);
@@ -1405,10 +1475,27 @@ enum Slot { SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2 };
 // Every kernel goes through here.  With timing events set, the launch
 // carries a start/stop event pair that the runtime records around the
 // kernel's own execution.
+// svla_describe: while set, launch() records what it would launch instead.
+struct LaunchDesc {
+    char name[3][96];
+    unsigned grid[3], block[3];
+    size_t lds[3];
+    bool used[3];
+};
+thread_local LaunchDesc *t_desc = nullptr;
+
 template <typename Arg>
 void launch(void (*kernel)(Arg), unsigned grid, size_t lds, hipStream_t s, Slot slot, const Arg &a,
-            unsigned threads = kThreads)
+            const char *name, unsigned threads = kThreads)
 {
+    if (t_desc) {
+        snprintf(t_desc->name[slot], sizeof t_desc->name[slot], "%s", name);
+        t_desc->grid[slot] = grid;
+        t_desc->block[slot] = threads;
+        t_desc->lds[slot] = lds;
+        t_desc->used[slot] = true;
+        return;
+    }
     const int e = 2 * (int)slot;
     if (t_events && e + 1 < t_nev)
         hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(threads), (uint32_t)lds, s,
@@ -1547,7 +1634,7 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     } else {
         p->splits = pick_splits(p->BH * nb, n, d, &p->chunk);
     }
-    p->tile = d == 128 ? 128 : 256;
+    p->tile = d == 128 ? SVLA_APPLY_TILE128 : (p->rope.on ? SVLA_APPLY_TILE_ROPE : SVLA_APPLY_TILE32);
     p->tiles = n > 0 ? (n + p->tile - 1) / p->tile : 0;
 
     // LDS: [RoPE table][stage buffers | epilogue]
@@ -1562,13 +1649,13 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
                         (long)p->rope.gh * (p->rope.dh / 2) + (long)p->rope.gw * (p->rope.dw / 2);
         const long ea = (long)frames_spanned_max(p->tile, hw) * (p->rope.dt / 2) +
                         (long)p->rope.gh * (p->rope.dh / 2) + (long)p->rope.gw * (p->rope.dw / 2);
-        if (eb > kMaxRopeEntries || ea > kMaxRopeEntries)
+        if (eb >= kMaxRopeEntries || ea >= kMaxRopeEntries)
             return fail(SVLA_ERR_UNSUPPORTED, fn,
                         "RoPE table of %ld entries exceeds %d (grid %dx%d too large)",
                         eb > ea ? eb : ea, kMaxRopeEntries, p->rope.gh, p->rope.gw);
         // the table takes only what the largest range of this call needs
         // (build and apply share it: the larger of the two)
-        const long e = eb > ea ? eb : ea;
+        const long e = (eb > ea ? eb : ea) + 1;   // + the identity entry
         p->rope.tab_bytes = (int)((e * 8 + 255) & ~255L);
         p->lds_build += (size_t)p->rope.tab_bytes;
         p->lds_apply = (size_t)p->rope.tab_bytes;
@@ -1602,22 +1689,38 @@ template <int D, bool FUSE>
 void launch_build_f(const Plan &p, const BuildArgs &a, hipStream_t s)
 {
     const unsigned grid = (unsigned)(p.BH * p.nb * p.splits);
+    const char *fz = FUSE ? "true" : "false";
+    char nm[96];
     if (SVLA_USE_DMA && p.esize == 2 && !p.rope.on && !FUSE) {
         constexpr int U = D == 32 ? SVLA_DMA_U32 : SVLA_DMA_U;
         constexpr int R = D == 32 ? SVLA_DMA_R32 : SVLA_DMA_R;
-        launch(svla_state_build_dma<D, U, R>, grid, 0, s, SLOT_BUILD, a);
+        if constexpr (D == 128 && SVLA_QUAD128) {
+            const unsigned qgrid = (unsigned)((grid + 7) / 8 * 8 * 4);
+            snprintf(nm, sizeof nm, "void svla_state_build_dma<64, %d, %d, 128>", U, R);
+            launch(svla_state_build_dma<64, U, R, 128>, qgrid, 0, s, SLOT_BUILD, a, nm);
+        } else {
+            snprintf(nm, sizeof nm, "void svla_state_build_dma<%d, %d, %d, %d>", D, U, R, D);
+            launch(svla_state_build_dma<D, U, R, D>, grid, 0, s, SLOT_BUILD, a, nm);
+        }
         return;
     }
     if (p.esize == 2) {
-        if (p.rope.on)
+        if (p.rope.on) {
+            snprintf(nm, sizeof nm, "void svla_state_build_bf16<%d, true, %d, %d, %s>", D,
+                     build_pf(true), build_u(true), fz);
             launch(svla_state_build_bf16<D, true, build_pf(true), build_u(true), FUSE>, grid,
-                   p.lds_build, s, SLOT_BUILD, a);
-        else
+                   p.lds_build, s, SLOT_BUILD, a, nm);
+        } else {
+            snprintf(nm, sizeof nm, "void svla_state_build_bf16<%d, false, %d, %d, %s>", D,
+                     build_pf(false), build_u(false), fz);
             launch(svla_state_build_bf16<D, false, build_pf(false), build_u(false), FUSE>, grid,
-                   p.lds_build, s, SLOT_BUILD, a);
+                   p.lds_build, s, SLOT_BUILD, a, nm);
+        }
     } else {
-        if (p.rope.on) launch(svla_state_build_f32<D, true, FUSE>, grid, p.lds_build, s, SLOT_BUILD, a);
-        else launch(svla_state_build_f32<D, false, FUSE>, grid, p.lds_build, s, SLOT_BUILD, a);
+        snprintf(nm, sizeof nm, "void svla_state_build_f32<%d, %s, %s>", D,
+                 p.rope.on ? "true" : "false", fz);
+        if (p.rope.on) launch(svla_state_build_f32<D, true, FUSE>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
+        else launch(svla_state_build_f32<D, false, FUSE>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
     }
 }
 
@@ -1634,20 +1737,25 @@ template <int D, int MODE>
 void launch_scan_d(const Plan &p, const ScanArgs &a, hipStream_t s)
 {
     const unsigned grid = (unsigned)(p.BH * (D * D / (kScanThreads * 4) + 1));
-    if (p.esize == 2) launch(svla_state_scan_k<D, MODE, true>, grid, 0, s, SLOT_SCAN, a, kScanThreads);
-    else launch(svla_state_scan_k<D, MODE, false>, grid, 0, s, SLOT_SCAN, a, kScanThreads);
+    char nm[96];
+    snprintf(nm, sizeof nm, "void svla_state_scan_k<%d, %d, %s>", D, MODE, p.esize == 2 ? "true" : "false");
+    if (p.esize == 2) launch(svla_state_scan_k<D, MODE, true>, grid, 0, s, SLOT_SCAN, a, nm, kScanThreads);
+    else launch(svla_state_scan_k<D, MODE, false>, grid, 0, s, SLOT_SCAN, a, nm, kScanThreads);
 }
 
 template <int D>
 void launch_apply(const Plan &p, const ApplyArgs &a, hipStream_t s)
 {
     const unsigned grid = (unsigned)(p.BH * p.nb * p.tiles);
+    char nm[96];
+    snprintf(nm, sizeof nm, "void svla_apply_%s<%d, %s>", p.esize == 2 ? "bf16" : "f32", D,
+             p.rope.on ? "true" : "false");
     if (p.esize == 2) {
-        if (p.rope.on) launch(svla_apply_bf16<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a);
-        else launch(svla_apply_bf16<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a);
+        if (p.rope.on) launch(svla_apply_bf16<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+        else launch(svla_apply_bf16<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
     } else {
-        if (p.rope.on) launch(svla_apply_f32<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a);
-        else launch(svla_apply_f32<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a);
+        if (p.rope.on) launch(svla_apply_f32<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+        else launch(svla_apply_f32<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
     }
 }
 
@@ -1727,6 +1835,7 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
         ba.S_part = (float *)(w + p.off_spart);
         ba.z_part = (float *)(w + p.off_zpart);
         ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = p.splits; ba.chunk = p.chunk;
+        ba.BH = p.BH;
         ba.rope = p.rope;
         if (p.fuse) {
             ba.counters = (unsigned long long *)(w + p.off_ctr);
@@ -1783,6 +1892,46 @@ svla_status svla_set_timing_events(void *const *events, int n)
     if (events && n < 0) return fail(SVLA_ERR_VALUE, "svla_set_timing_events", "n must be >= 0");
     t_events = (events && n > 0) ? events : nullptr;
     t_nev = t_events ? n : 0;
+    return SVLA_OK;
+}
+
+svla_status svla_describe(svla_op op, svla_dtype dt, int B, int H, int nb, int n, int d,
+                          const svla_rope *rope, char *buf, size_t len)
+{
+    const char *fn = "svla_describe";
+    if (!buf || len == 0) return fail(SVLA_ERR_NULL, fn, "buf is NULL or empty");
+    if (op != SVLA_OP_NONCAUSAL && op != SVLA_OP_BLOCK_CAUSAL && op != SVLA_OP_BLOCK_STEP)
+        return fail(SVLA_ERR_VALUE, fn, "only the fused calls are described (op %d)", (int)op);
+    Plan p;
+    svla_status st = make_plan(fn, op, dt, B, H, nb, n, d, rope, &p);
+    if (st) return st;
+    LaunchDesc desc;
+    memset(&desc, 0, sizeof desc);
+    t_desc = &desc;
+    BuildArgs ba;
+    memset(&ba, 0, sizeof ba);
+    ScanArgs sa;
+    memset(&sa, 0, sizeof sa);
+    ApplyArgs aa;
+    memset(&aa, 0, sizeof aa);
+    if (p.BH > 0) {
+        if (p.splits > 0 && nb > 0) build_any(p, ba, nullptr);
+        if (!p.fuse) scan_any<SCAN_FUSED>(p, sa, nullptr);
+        if ((long)nb * n > 0) apply_any(p, aa, nullptr);
+    }
+    t_desc = nullptr;
+    static const char *slot_name[3] = {"build", "scan", "apply"};
+    int w = snprintf(buf, len, "{\"splits\": %d, \"chunk\": %d, \"apply_tile\": %d, \"workspace\": %zu, \"kernels\": [",
+                     p.splits, p.chunk, p.tile, p.total);
+    bool first = true;
+    for (int k = 0; k < 3; ++k) {
+        if (!desc.used[k] || w < 0 || (size_t)w >= len) continue;
+        w += snprintf(buf + w, len - w, "%s{\"slot\": \"%s\", \"name\": \"%s\", \"grid\": %u, \"block\": %u, \"lds\": %zu}",
+                      first ? "" : ", ", slot_name[k], desc.name[k], desc.grid[k], desc.block[k], desc.lds[k]);
+        first = false;
+    }
+    if (w >= 0 && (size_t)w < len) w += snprintf(buf + w, len - w, "]}");
+    if (w < 0 || (size_t)w >= len) return fail(SVLA_ERR_VALUE, fn, "buffer of %zu bytes too small", len);
     return SVLA_OK;
 }
 
@@ -1881,6 +2030,7 @@ svla_status svla_state_build(svla_dtype dt, int B, int H, int nb, int n, int d, 
     memset(&ba, 0, sizeof ba);
     ba.K = K; ba.V = V; ba.S_part = S_local; ba.z_part = z_local;
     ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = 1; ba.chunk = p.chunk; ba.rope = p.rope;
+    ba.BH = p.BH;
     build_any(p, ba, s);
     return check_launch(fn);
 }

@@ -123,6 +123,15 @@ const char *svla_last_error(void);                /* thread-local; "" if none */
 svla_status svla_workspace_size(svla_op op, svla_dtype dt, int B, int H,
                                 int nb, int n, int d, size_t *bytes);
 
+/* The launch plan of a fused call (SVLA_OP_NONCAUSAL, _BLOCK_CAUSAL,
+ * _BLOCK_STEP) for these sizes, as a JSON object written to buf (host
+ * memory, `len` bytes including the terminating zero): split count, tokens
+ * per split, apply tile, workspace bytes, and for each kernel its name (as
+ * profilers report it), grid, block and dynamic LDS.  Launches nothing.
+ * SVLA_ERR_VALUE if the text does not fit. */
+svla_status svla_describe(svla_op op, svla_dtype dt, int B, int H, int nb, int n, int d,
+                          const svla_rope *rope, char *buf, size_t len);
+
 /* ---- the method ------------------------------------------------------------ */
 
 /* Non-causal linear attention over one block of N tokens (the base Linear
