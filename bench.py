@@ -256,7 +256,7 @@ def cpu_baseline(w: Workload, budget_s: float = 10.0) -> dict:
     threads = len(os.sched_getaffinity(0))
     reps, secs, used = 0, 0.0, threads
     kw = dict(g=x["g"], rope=w.cfg.rope, eps=x["eps"], threads=threads)
-    while secs < budget_s and reps < 20:
+    while secs < budget_s and reps < 1000:
         r = oracle.forward(Q, K, V, w.cfg.nb, **kw)
         secs += r["seconds"]
         used = r["threads"]
