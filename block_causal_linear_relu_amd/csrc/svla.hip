@@ -36,20 +36,11 @@
 #include "../../include/svla.h"
 
 // Tuning knobs (compile-time; the defaults are the measured choices).
-#ifndef SVLA_BUILD_PF
-#define SVLA_BUILD_PF 2            // stages of K/V loads in flight in the state build
-#endif
-#ifndef SVLA_BUILD_U
-#define SVLA_BUILD_U 2             // 16-byte K and V chunks per thread per stage
-#endif
-#ifndef SVLA_BUILD_PF_ROPE
-#define SVLA_BUILD_PF_ROPE 2       // the same two knobs for the RoPE build
-#endif
-#ifndef SVLA_BUILD_U_ROPE
-#define SVLA_BUILD_U_ROPE 1
+#ifndef SVLA_DMA_WGS
+#define SVLA_DMA_WGS 420           // state build without RoPE: workgroups wanted per launch
 #endif
 #ifndef SVLA_DMA_U32
-#define SVLA_DMA_U32 1             // direct-to-LDS build, d = 32: chunks per thread per stage
+#define SVLA_DMA_U32 1             // ... d = 32: 16-byte loads per thread per tensor per stage
 #endif
 #ifndef SVLA_DMA_R32
 #define SVLA_DMA_R32 3             // ... and LDS ring depth
@@ -60,25 +51,42 @@
 #ifndef SVLA_DMA_R
 #define SVLA_DMA_R 4
 #endif
-#ifndef SVLA_QUAD128
-#define SVLA_QUAD128 1             // d = 128 build: one workgroup per 64 x 64 quadrant of S
+#ifndef SVLA_ROPE_PF
+#define SVLA_ROPE_PF 2             // state build with RoPE: stages in flight per wave
+#endif
+#ifndef SVLA_ROPE_U
+#define SVLA_ROPE_U 2              // ... 16-byte loads per lane per tensor per stage
+#endif
+#ifndef SVLA_ROPE_WGS
+#define SVLA_ROPE_WGS 2048         // ... (and fp32 builds): workgroups wanted per launch
+#endif
+#ifndef SVLA_MIN_SPLIT_PER_D
+#define SVLA_MIN_SPLIT_PER_D 8     // tokens per build workgroup and block >= this * d
+#endif
+#ifndef SVLA_SCAN_LA
+#define SVLA_SCAN_LA 16            // partial-state loads in flight per scan thread
 #endif
 #ifndef SVLA_APPLY_TILE32
-#define SVLA_APPLY_TILE32 256      // apply: tokens per workgroup for d = 32, 64
+#define SVLA_APPLY_TILE32 256      // apply: tokens per workgroup for bf16 d = 32 and fp32 d = 32, 64
 #endif
 #ifndef SVLA_APPLY_TILE_ROPE
 #define SVLA_APPLY_TILE_ROPE 512   // ... with RoPE (amortises the per-workgroup angle table)
 #endif
 #ifndef SVLA_APPLY_TILE128
-#define SVLA_APPLY_TILE128 128     // ... and for d = 128
+#define SVLA_APPLY_TILE128 128     // ... fp32, d = 128
 #endif
-#ifndef SVLA_USE_DMA
-#define SVLA_USE_DMA 1             // non-RoPE bf16 builds load straight to LDS
+#ifndef SVLA_APPLY_TILE_LDS
+#define SVLA_APPLY_TILE_LDS 256    // bf16 apply with the state in LDS (d >= 64): tokens per workgroup
+#endif
+#ifndef SVLA_APPLY_PF
+#define SVLA_APPLY_PF 4            // ... 16-token groups of Q loads in flight per wave
+#endif
+#ifndef SVLA_APPLY_XCD
+#define SVLA_APPLY_XCD 1           // apply: the token tiles of one block on one XCD
 #endif
 // Cache-policy bits of the streaming accesses (gfx950 buffer instructions:
 // bit 1 = nt, non-temporal).  Measured: nt pays for K/V (read once by the
-// state build) and for Q when every element is read once (d <= 64); the
-// d = 128 apply re-reads Q from four waves and wants it cached.
+// state build), for Q (read once by the apply) and not for O.
 #ifndef SVLA_KV_AUX
 #define SVLA_KV_AUX 2
 #endif
@@ -87,18 +95,6 @@
 #endif
 #ifndef SVLA_O_AUX
 #define SVLA_O_AUX 0
-#endif
-#ifndef SVLA_SCAN_LA
-#define SVLA_SCAN_LA 16            // partial-state loads in flight per scan thread
-#endif
-#ifndef SVLA_TARGET_WGS
-#define SVLA_TARGET_WGS 2048       // state-build workgroups wanted per launch
-#endif
-#ifndef SVLA_MIN_SPLIT_PER_D
-#define SVLA_MIN_SPLIT_PER_D 8     // tokens per split >= this * d
-#endif
-#ifndef SVLA_FUSE_MAX_D
-#define SVLA_FUSE_MAX_D 0          // fuse the scan into the build for d <= this
 #endif
 
 // ---------------------------------------------------------------------------
@@ -114,7 +110,7 @@ typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 namespace {
 
 constexpr int kThreads = 256;                 // build and apply: 4 waves of 64
-constexpr int kScanThreads = 64;              // scan: one wave, 256 state elements per workgroup
+constexpr int kScanLongChain = 16;            // scan: blocks from which the chain is cut four ways
 constexpr uint32_t kOOB = 0x80000000u;        // an offset past every resource
 constexpr int kMaxRopeEntries = 4096;         // (cos, sin) pairs per workgroup
 
@@ -177,9 +173,12 @@ __device__ __forceinline__ unsigned short f2bf(float x)
     return __builtin_bit_cast(unsigned short, (__bf16)x);
 }
 
+// two fp32 -> packed bf16 pair (lo in bits 0-15), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ unsigned int pack_bf16(float lo, float hi)
 {
-    return (unsigned int)f2bf(lo) | ((unsigned int)f2bf(hi) << 16);
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // Barrier for LDS hand-offs inside a workgroup.  __syncthreads() also
@@ -190,6 +189,15 @@ __device__ __forceinline__ unsigned int pack_bf16(float lo, float hi)
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Unsigned division by a divisor fixed per launch (multiply-high method of
@@ -242,7 +250,7 @@ __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
         turns_per_pos[a * kMaxRopePairs + m] =
             pow((double)r.base, -2.0 * (double)m / (double)width) * (0.5 / M_PI);
     }
-    __syncthreads();
+    lds_barrier();
     const int nT = nf * pt, nH = r.gh * ph, total = rope_entries(r, nf);
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
         int pos, m, a;
@@ -325,6 +333,20 @@ __device__ __forceinline__ void rope_rotate(float *x, const RopePos &pos,
     }
 }
 
+// Workgroup w of a launch is dispatched to XCD w % 8 (round-robin over the
+// eight XCDs, each with its own L2).  Logical id (w % 8) * ceil(G / 8) + w / 8
+// gives each XCD one contiguous range of the G logical ids, so neighbouring
+// logical workgroups (the token tiles of one block, which read the same
+// block state) share an L2.  The grid is G rounded up to a multiple of 8;
+// a logical id >= G has no work.
+__device__ __forceinline__ long xcd_logical(long G)
+{
+    const long w = blockIdx.x;
+    return SVLA_APPLY_XCD ? (w % 8) * ((G + 7) / 8) + w / 8 : w;
+}
+
+inline unsigned xcd_grid(long G) { return (unsigned)(SVLA_APPLY_XCD ? (G + 7) / 8 * 8 : G); }
+
 // ---------------------------------------------------------------------------
 // kernel arguments
 // ---------------------------------------------------------------------------
@@ -336,18 +358,16 @@ struct ScanArgs {
     float *z_pre;                  // [BH*nb][d]
     float *S_pre;                  // fp32 prefix states [BH*nb][d*d] (export mode)
     float *S_fin, *z_fin;          // final state or null
-    int nb, splits;
+    int nb, splits;                // blocks, partial states per block
 };
 
 struct BuildArgs {
     const void *K, *V;
-    float *S_part, *z_part;        // [BH*nb*splits][d*d], [BH*nb*splits][d]
-    int N, n, nb, splits, chunk;   // chunk: tokens per split (multiple of the stage)
+    float *S_part, *z_part;        // [BH*nb][splits][d*d], [BH*nb][splits][d]
+    int N, n, nb;
+    int splits, chunk;             // workgroups per block, tokens per workgroup
     long BH;
     RopeK rope;
-    unsigned long long *counters;  // [BH] arrival counters of the fused scan
-    unsigned epoch;                // distinct per call (see arrive())
-    ScanArgs scan;                 // what the last workgroup of a (b,h) runs
 };
 
 struct ApplyArgs {
@@ -356,17 +376,19 @@ struct ApplyArgs {
     const void *S_op;              // packed operand [BH*nb][d*d]
     const float *z_pre;            // [BH*nb][d]
     int N, n, nb, tile, tiles;     // tile: tokens per workgroup; tiles per block
+    long groups;                   // logical workgroups: B*H*nb*tiles
     float eps;
     RopeK rope;
 };
 
-enum ScanMode { SCAN_FUSED = 0, SCAN_EXPORT = 1, SCAN_PACK = 2 };
+// SCAN_FORWARD: partials -> packed operands, prefix z and the final state;
+// SCAN_EXPORT: local states -> fp32 prefix states; SCAN_PACK: prefix states
+// -> packed operands.
+enum ScanMode { SCAN_FORWARD = 0, SCAN_EXPORT = 1, SCAN_PACK = 2 };
 
 // ---------------------------------------------------------------------------
-// The scan of one (bh, tile): tile < d*d/1024 is a 1024-element slice of S
-// (each thread owns 4 consecutive elements of S[k][v]), tile == d*d/1024 is
-// z.  Blocks are walked in order, acc = g_c * acc + sum over splits, with the
-// splits added in index order, so the result repeats bit for bit.
+// svla_state_scan: per (bh, element tile), the inclusive, optionally decayed
+// prefix over blocks, S_c = g_c S_{c-1} + (sum of block c's split partials).
 //
 // Packed operand layout read by svla_apply (per (bh, block), d*d entries):
 // bf16: fragment (m, ks) = 64 lanes x 8 values; lane (rho + 16 kg), value i
@@ -375,196 +397,240 @@ enum ScanMode { SCAN_FUSED = 0, SCAN_EXPORT = 1, SCAN_PACK = 2 };
 //       holds S[16 kq + 4 kg + i][f(m, rho)]
 // with f(m, rho) = (d/4) (rho / 4) + 4 m + rho % 4: the output rows of the
 // MFMA land so that each lane ends up with consecutive O features.
+//
+// Element tiles: lane -> column v0 + lane % CW and RL consecutive rows
+// k0 + RL (lane / CW) of an 8-row x CW-column tile, so each lane's values
+// are contiguous in the packed operand (one store per block) and every
+// load instruction reads whole row segments.  The last tile of a (bh) is z.
+// For long chains of blocks the NSEG waves of a workgroup take the same
+// tile and 1/NSEG of the blocks each, which cuts the serial chain NSEG ways
+// (the prefix over blocks is associative: (G1, P1) then (G2, P2) is
+// (G1 G2, G2 P1 + P2)):
+//   1. each wave sums its blocks from a zero state: its product of gates G
+//      and its partial prefix P;
+//   2. through LDS, each wave composes the (G, P) of the waves before it
+//      onto the incoming state (S_in or 0), in wave order;
+//   3. each wave walks its blocks again from that state and writes every
+//      block's prefix; the last wave's state is the final state.
+// With NSEG = 1 the one wave skips steps 1 and 2.
+// The partials of a wave's blocks are read in chunks of LA, all loads of a
+// chunk issued before any is used.  Everything is summed in a fixed order,
+// so the result repeats bit for bit.
 // ---------------------------------------------------------------------------
-template <int D, int MODE, bool OPBF16, int NT>
-__device__ __forceinline__ void scan_tile(const ScanArgs &a, long bh, int tile, int tid)
+template <int D>
+struct ScanShape {
+    static constexpr int RL = D == 32 ? 2 : 4;          // rows per lane
+    static constexpr int CW = 8 * RL;                   // columns per tile
+    static constexpr int STILES = (D / 8) * (D / CW);   // S tiles per (bh)
+};
+
+// Walk partials [lo, hi) of one (bh) (block-major, split-minor) in chunks
+// of LA: fetch(idx, values) loads one (idx clamped into [lo, hi), so every
+// load is in bounds; a value past hi is never used), consume(values) adds it.
+template <int LA, int W, typename Fetch, typename Consume>
+__device__ __forceinline__ void scan_walk(int lo, int hi, Fetch fetch, Consume consume)
 {
-    constexpr int STILES = D * D / (NT * 4);
-    if (tile < STILES) {
-        const int e0 = tile * (NT * 4) + tid * 4;
-        const int k = e0 / D, v = e0 % D;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (MODE != SCAN_PACK && a.S_in) acc = *(const f32x4_t *)(a.S_in + bh * D * D + e0);
-        // operand positions of the 4 elements (k, v..v+3)
-        const int m = (v % (D / 4)) / 4, rho0 = 4 * (v / (D / 4));
-        int opos[4];
+    static_assert(LA * W < 64, "the loads of a chunk must fit the vmcnt counter");
+    for (int base = lo; base < hi; base += LA) {
+        float buf[LA][W];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (OPBF16) {
-                const int ks = k / 32, kg = (k % 32) / 8, i = k % 8;
-                opos[j] = (((m * (D / 32) + ks) * 64 + rho0 + j + 16 * kg) * 8 + i);
-            } else {
-                const int kq = k / 16, kg = (k % 16) / 4, i = k % 4;
-                opos[j] = (((m * (D / 16) + kq) * 64 + rho0 + j + 16 * kg) * 4 + i);
-            }
-        }
-        // The partials of (block c, split sp) form one stream, idx = c*splits + sp,
-        // read through a ring of LA loads in flight; a refill past the end
-        // re-reads the last partial (always in bounds) and is never used.
-        constexpr int LA = SVLA_SCAN_LA;
-        const int total = a.nb * a.splits;
-        const float *base = a.S_part + bh * (long)total * D * D + e0;
-        f32x4_t ring[LA];
+        for (int j = 0; j < LA; ++j) fetch(min(base + j, hi - 1), buf[j]);
+        wait_vmcnt<0>();      // once per chunk: the stores of consume() then wait for nothing
 #pragma unroll
         for (int j = 0; j < LA; ++j)
-            ring[j] = total > 0 ? *(const f32x4_t *)(base + (long)min(j, total - 1) * D * D)
-                                : (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        int c = 0, sp = 0;
-        if (a.splits == 0) {
-            // no tokens: each block only decays the carried state
-            for (; c < a.nb; ++c) {
-                const long unit = bh * a.nb + c;
-                if (a.g) acc *= a.g[unit];
-                if (MODE == SCAN_EXPORT) *(f32x4_t *)(a.S_pre + unit * D * D + e0) = acc;
-            }
-        }
-        for (int idx0 = 0; idx0 < total; idx0 += LA) {
-#pragma unroll
-            for (int j = 0; j < LA; ++j) {
-                const int idx = idx0 + j;
-                if (idx < total) {
-                    const long unit = bh * a.nb + c;
-                    if (sp == 0) {
-                        if (MODE == SCAN_PACK) acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                        else if (a.g) acc *= a.g[unit];
-                    }
-                    acc += ring[j];
-                    if (sp == a.splits - 1) {
-                        if (MODE == SCAN_EXPORT) {
-                            *(f32x4_t *)(a.S_pre + unit * D * D + e0) = acc;
-                        } else if constexpr (OPBF16) {
-                            unsigned short *op = (unsigned short *)a.S_op + unit * D * D;
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) op[opos[jj]] = f2bf(acc[jj]);
-                        } else {
-                            float *op = (float *)a.S_op + unit * D * D;
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) op[opos[jj]] = acc[jj];
-                        }
-                        sp = 0;
-                        ++c;
-                    } else {
-                        ++sp;
-                    }
-                }
-                ring[j] = *(const f32x4_t *)(base + (long)min(idx + LA, total - 1) * D * D);
-            }
-        }
-        if (MODE != SCAN_PACK && a.S_fin) *(f32x4_t *)(a.S_fin + bh * D * D + e0) = acc;
-    } else if (MODE != SCAN_PACK && tid < D / 4) {
-        const int e0 = tid * 4;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (a.z_in) acc = *(const f32x4_t *)(a.z_in + bh * D + e0);
-        constexpr int LA = SVLA_SCAN_LA;   // same look-ahead ring as for S
-        const int total = a.nb * a.splits;
-        const float *base = a.z_part + bh * (long)total * D + e0;
-        f32x4_t ring[LA];
-#pragma unroll
-        for (int j = 0; j < LA; ++j)
-            ring[j] = total > 0 ? *(const f32x4_t *)(base + (long)min(j, total - 1) * D)
-                                : (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        int c = 0, sp = 0;
-        if (a.splits == 0) {
-            for (; c < a.nb; ++c) {
-                const long unit = bh * a.nb + c;
-                if (a.g) acc *= a.g[unit];
-                *(f32x4_t *)(a.z_pre + unit * D + e0) = acc;
-            }
-        }
-        for (int idx0 = 0; idx0 < total; idx0 += LA) {
-#pragma unroll
-            for (int j = 0; j < LA; ++j) {
-                const int idx = idx0 + j;
-                if (idx < total) {
-                    const long unit = bh * a.nb + c;
-                    if (sp == 0 && a.g) acc *= a.g[unit];
-                    acc += ring[j];
-                    if (sp == a.splits - 1) {
-                        *(f32x4_t *)(a.z_pre + unit * D + e0) = acc;
-                        sp = 0;
-                        ++c;
-                    } else {
-                        ++sp;
-                    }
-                }
-                ring[j] = *(const f32x4_t *)(base + (long)min(idx + LA, total - 1) * D);
-            }
-        }
-        if (a.z_fin) *(f32x4_t *)(a.z_fin + bh * D + e0) = acc;
+            if (base + j < hi) consume(buf[j]);
     }
 }
 
-template <int D, int MODE, bool OPBF16>
-__global__ void __launch_bounds__(kScanThreads)
+// The segmented scan of W values per lane.  fetch(idx, values) loads
+// partial idx of this (bh); emit(c, values) writes block c's prefix;
+// `acc` holds the incoming state on entry and, in the last wave, the final
+// state on exit.  red: LDS of NSEG * W * 64 + NSEG floats.
+template <int W, int MODE, int NSEG, typename Fetch, typename Emit>
+__device__ __forceinline__ void scan_blocks(const ScanArgs &a, long bh, float *acc, float *red,
+                                            Fetch fetch, Emit emit)
+{
+    constexpr int LA = 63 / W;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int per = (a.nb + NSEG - 1) / NSEG;
+    const int c0 = min(wave * per, a.nb), c1 = min(c0 + per, a.nb);
+    const int lo = c0 * a.splits, hi = c1 * a.splits;
+    const float *g = a.g ? a.g + bh * a.nb : nullptr;
+
+    if constexpr (MODE != SCAN_PACK && NSEG > 1) {
+        // 1. this wave's (G, P) from a zero state
+        float P[W], G = 1.f;
+#pragma unroll
+        for (int r = 0; r < W; ++r) P[r] = 0.f;
+        int c = c0, sp = 0;
+        scan_walk<LA, W>(lo, hi, fetch, [&](const float *x) {
+            if (sp == 0 && g) {
+                const float gc = g[c];
+                G *= gc;
+#pragma unroll
+                for (int r = 0; r < W; ++r) P[r] *= gc;
+            }
+#pragma unroll
+            for (int r = 0; r < W; ++r) P[r] += x[r];
+            if (++sp == a.splits) { sp = 0; ++c; }
+        });
+        if (a.splits == 0 && g) {   // no tokens: the blocks only decay
+            for (int cc = c0; cc < c1; ++cc) G *= g[cc];
+        }
+#pragma unroll
+        for (int r = 0; r < W; ++r) red[(wave * W + r) * 64 + lane] = P[r];
+        if (lane == 0) red[NSEG * W * 64 + wave] = G;
+        __syncthreads();
+        // 2. compose the earlier waves onto the incoming state
+        for (int w = 0; w < wave; ++w) {
+            const float gw = red[NSEG * W * 64 + w];
+#pragma unroll
+            for (int r = 0; r < W; ++r) acc[r] = gw * acc[r] + red[(w * W + r) * 64 + lane];
+        }
+    }
+    // 3. this wave's blocks from its incoming state
+    int c = c0, sp = 0;
+    if (a.splits == 0) {
+        for (; c < c1; ++c) {
+            if (g) {
+#pragma unroll
+                for (int r = 0; r < W; ++r) acc[r] *= g[c];
+            }
+            emit(c, acc);
+        }
+    } else {
+        scan_walk<LA, W>(lo, hi, fetch, [&](const float *x) {
+            if (sp == 0) {
+                const float gc = MODE == SCAN_PACK ? 0.f : (g ? g[c] : 1.f);
+#pragma unroll
+                for (int r = 0; r < W; ++r) acc[r] *= gc;
+            }
+#pragma unroll
+            for (int r = 0; r < W; ++r) acc[r] += x[r];
+            if (++sp == a.splits) {
+                emit(c, acc);
+                sp = 0;
+                ++c;
+            }
+        });
+    }
+}
+
+template <int D, int MODE, bool OPBF16, int NSEG>
+__device__ __forceinline__ void scan_s_tile(const ScanArgs &a, long bh, int tile, float *red)
+{
+    using SH = ScanShape<D>;
+    constexpr int RL = SH::RL, CW = SH::CW;
+    const int lane = threadIdx.x & 63;
+    const int v = (tile % (D / CW)) * CW + lane % CW;
+    const int k = (tile / (D / CW)) * 8 + RL * (lane / CW);
+    // operand position of (k .. k + RL - 1, v)
+    const int m = (v % (D / 4)) / 4, rho = 4 * (v / (D / 4)) + v % 4;
+    long opos;
+    if constexpr (OPBF16)
+        opos = ((long)((m * (D / 32) + k / 32) * 64 + rho + 16 * ((k % 32) / 8)) * 8 + k % 8);
+    else
+        opos = ((long)((m * (D / 16) + k / 16) * 64 + rho + 16 * ((k % 16) / 4)) * 4 + k % 4);
+
+    float acc[RL];
+#pragma unroll
+    for (int r = 0; r < RL; ++r)
+        acc[r] = (MODE != SCAN_PACK && a.S_in) ? a.S_in[bh * D * D + (k + r) * D + v] : 0.f;
+    const float *part = a.S_part + bh * (long)a.nb * a.splits * D * D + k * D + v;
+    auto fetch = [&](int idx, float *dst) {
+        const float *src = part + (long)idx * D * D;
+#pragma unroll
+        for (int r = 0; r < RL; ++r) dst[r] = src[r * D];
+    };
+    auto emit = [&](int c, const float *x) {
+        const long unit = bh * a.nb + c;
+        if constexpr (MODE == SCAN_EXPORT) {
+#pragma unroll
+            for (int r = 0; r < RL; ++r) a.S_pre[unit * D * D + (k + r) * D + v] = x[r];
+        } else if constexpr (OPBF16) {
+            unsigned short *op = (unsigned short *)a.S_op + unit * D * D + opos;
+            if constexpr (RL == 2) *(unsigned int *)op = pack_bf16(x[0], x[1]);
+            else *(uint2 *)op = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+        } else {
+            float *op = (float *)a.S_op + unit * D * D + opos;
+            if constexpr (RL == 2) *(float2 *)op = make_float2(x[0], x[1]);
+            else *(float4 *)op = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    };
+    scan_blocks<RL, MODE, NSEG>(a, bh, acc, red, fetch, emit);
+    if (MODE != SCAN_PACK && a.S_fin && (threadIdx.x >> 6) == NSEG - 1) {
+#pragma unroll
+        for (int r = 0; r < RL; ++r) a.S_fin[bh * D * D + (k + r) * D + v] = acc[r];
+    }
+}
+
+// z of one (bh): lane -> z[lane], z[lane + 64]
+template <int D, int MODE, int NSEG>
+__device__ __forceinline__ void scan_z_tile(const ScanArgs &a, long bh, float *red)
+{
+    constexpr int ZL = (D + 63) / 64;
+    const int lane = threadIdx.x & 63;
+    const int e0 = min(lane, D - 1);    // lanes past d read a valid element and write nothing
+    float acc[ZL];
+#pragma unroll
+    for (int r = 0; r < ZL; ++r) acc[r] = (a.z_in && lane + 64 * r < D) ? a.z_in[bh * D + e0 + 64 * r] : 0.f;
+    const float *part = a.z_part + bh * (long)a.nb * a.splits * D + e0;
+    auto fetch = [&](int idx, float *dst) {
+        const float *src = part + (long)idx * D;
+#pragma unroll
+        for (int r = 0; r < ZL; ++r) dst[r] = src[64 * r];
+    };
+    auto emit = [&](int c, const float *x) {
+#pragma unroll
+        for (int r = 0; r < ZL; ++r)
+            if (lane + 64 * r < D) a.z_pre[(bh * a.nb + c) * D + lane + 64 * r] = x[r];
+    };
+    scan_blocks<ZL, MODE, NSEG>(a, bh, acc, red, fetch, emit);
+    if (a.z_fin && (threadIdx.x >> 6) == NSEG - 1) {
+#pragma unroll
+        for (int r = 0; r < ZL; ++r)
+            if (lane + 64 * r < D) a.z_fin[bh * D + lane + 64 * r] = acc[r];
+    }
+}
+
+template <int D, int MODE, bool OPBF16, int NSEG>
+__global__ void __launch_bounds__(64 * NSEG)
 svla_state_scan_k(const ScanArgs a)
 {
-    constexpr int STILES = D * D / (kScanThreads * 4);
+    constexpr int STILES = ScanShape<D>::STILES;
+    __shared__ float red[NSEG > 1 ? NSEG * 4 * 64 + NSEG : 1];
     const long bh = blockIdx.x / (STILES + 1);
-    scan_tile<D, MODE, OPBF16, kScanThreads>(a, bh, blockIdx.x % (STILES + 1), threadIdx.x);
-}
-
-// Arrival of one workgroup at a (b,h) counter; true for the last of `total`.
-// The counter holds (epoch << 32 | count).  A count left by any other call
-// (a different epoch), or whatever an unused workspace held, is restarted,
-// so the workspace needs no initialisation; the last arrival rewinds the
-// count to 0 under the same epoch, so replaying a captured launch works too.
-// The loop ends: a failed compare-and-swap means another workgroup's swap
-// succeeded, and at most `total` workgroups arrive per launch.
-__device__ bool arrive(unsigned long long *ctr, unsigned epoch, unsigned total)
-{
-    const unsigned long long tag = (unsigned long long)epoch << 32;
-    unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {
-        const unsigned long long nw = ((old >> 32) == epoch) ? old + 1 : (tag | 1ull);
-        const unsigned long long prev = atomicCAS(ctr, old, nw);
-        if (prev == old) {
-            if ((unsigned)(nw & 0xffffffffull) == total) {
-                __hip_atomic_store(ctr, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return true;
-            }
-            return false;
-        }
-        old = prev;
-    }
-}
-
-// After a build workgroup has written its partials: the last workgroup of the
-// (b,h) runs the scan of every tile of that (b,h) (the inclusive prefix over
-// blocks, the packed operands, the final state).
-template <int D, bool OPBF16>
-__device__ __forceinline__ void fused_scan(const BuildArgs &a, long bh, int tid)
-{
-    __shared__ int s_last;
-    __threadfence();                 // release this workgroup's partial stores
-    __syncthreads();
-    if (tid == 0) s_last = arrive(a.counters + bh, a.epoch, (unsigned)(a.nb * a.splits));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();                 // acquire every other workgroup's partials
-#pragma unroll 1
-    for (int tile = 0; tile <= D * D / 1024; ++tile) scan_tile<D, SCAN_FUSED, OPBF16, kThreads>(a.scan, bh, tile, tid);
+    const int tile = (int)(blockIdx.x % (STILES + 1));
+    if (tile < STILES) scan_s_tile<D, MODE, OPBF16, NSEG>(a, bh, tile, red);
+    else if (MODE != SCAN_PACK) scan_z_tile<D, MODE, NSEG>(a, bh, red);
 }
 
 // ---------------------------------------------------------------------------
-// svla_state_build, bf16 inputs.
+// svla_state_build, bf16 inputs without RoPE, loads straight to LDS.
 //
-// Workgroup = (bh, block c, split s); it walks its token range in stages of
-// TT tokens.  Per stage every thread loads one 16-byte chunk of K and of V
-// (8 features of one token), applies phi to K, adds phi(k) to its running z,
-// and writes both chunks to LDS rows.  PF stages of loads are in flight while
-// the current stage is contracted.  The MFMA v_mfma_f32_32x32x16_bf16
-// contracts over tokens, so each lane gathers 8 tokens of one feature from
-// the staged rows.  Which token feeds which k-slot does not matter for a
-// sum over tokens, as long as A and B use the same assignment; lanes 32-63
-// take the odd tokens so the two half-waves hit disjoint LDS banks.
+// Workgroup = (bh, block c, split s[, quadrant]): it walks its token range in
+// stages of TT tokens.  K and V travel from global memory into an R-deep
+// ring of LDS stages with buffer_load ... lds (16 bytes per lane, one
+// kilobyte per wave instruction), so R - 1 stages of loads stay in flight
+// without holding registers.  The contraction S = phi(K)^T V runs on
+// v_mfma_f32_32x32x16_bf16 over tokens: each lane gathers 8 tokens of one
+// feature from the staged rows (which token feeds which k-slot does not
+// matter for a sum over tokens, as long as A and B agree; lanes 32-63 take
+// the odd tokens so the two half-waves read disjoint banks).  phi is applied
+// to the K fragments, and z comes out of the same matrix cores as phi(K)
+// times a ones operand.  Rows of the last stage past the range are
+// overwritten with zeros by the lanes that loaded them.  Each stage buffer
+// is its own LDS object, which lets the compiler tell the loads of
+// different stages apart instead of waiting for all of them.
 //   d = 32 : one 32x32 output tile; the 4 waves split the stage's tokens and
-//            their accumulators are summed through LDS at the end.
-//   d = 64 : 2x2 tiles, one per wave, every wave sees every token.
-//   d = 128: 4x4 tiles, 2x2 per wave.
-// With RoPE the rotated phi(k) is split into bf16 hi + lo parts, two MFMAs,
-// so the state keeps ~16 bits of the rotated key.
-// FUSE: the last workgroup of each (b,h) also runs the scan (fused_scan).
+//            their tiles are summed through LDS at the end.
+//   d = 64 : 2x2 tiles, one per wave; every wave sees every token.
+//   d = 128: DG = 128, D = 64: four workgroups per (bh, block, split), one
+//            64 x 64 quadrant of S each, from K and V half-rows.
 // ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
 template <int D>
 __device__ __forceinline__ int swz16(int t, int chunk)
 {
@@ -573,269 +639,10 @@ __device__ __forceinline__ int swz16(int t, int chunk)
     return (D >= 64) ? (chunk ^ ((t & 1) << 2)) : chunk;
 }
 
-template <int D, bool ROPE, int PF, int U, bool FUSE>
-__global__ void __launch_bounds__(kThreads)
-svla_state_build_bf16(const BuildArgs a)
-{
-    constexpr int CPR = D / 8;            // 16-byte chunks per token row
-    constexpr int RPS = kThreads / CPR;   // token rows one pass of the threads covers
-    constexpr int TT = U * RPS;           // tokens per stage (U chunks per thread per tensor)
-    constexpr int ROWB = D * 2;
-    constexpr int TILEB = TT * ROWB;      // U * 4096 bytes
-    constexpr int NK = ROPE ? 2 : 1;
-    constexpr int STAGEB = (NK + 1) * TILEB;
-    constexpr bool SPLITK = (D == 32);
-    constexpr int TPW = SPLITK ? 1 : D / 64;
-    constexpr int GPS = TT / 16;          // 16-token groups per stage
-
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const unsigned per_bh = (unsigned)(a.splits * a.nb);
-    const long bh = blockIdx.x / per_bh;
-    const int rest = (int)(blockIdx.x - bh * per_bh);
-    const int c = rest / a.splits, s = rest % a.splits;
-    const int tok_lo = c * a.n + s * a.chunk;
-    const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
-
-    const uint32_t slice = (uint32_t)a.N * D * 2;
-    const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
-    const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
-
-    // RoPE table (lives before the stage buffers)
-    float2 *tab = (float2 *)lds;
-    uint32_t frame_lo = 0;
-    RopePairs<4> pp;
-    const int row = tid / CPR, q = tid % CPR;
-    if constexpr (ROPE) {
-        frame_lo = tok_lo < tok_hi ? fdiv((uint32_t)tok_lo, a.rope.div_hw) : 0;
-        uint32_t frame_hi = tok_lo < tok_hi ? fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw) : 0;
-        int nf = (int)(frame_hi - frame_lo) + 1;
-        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
-        pp = rope_pairs<4>(a.rope, q * 8, nf);
-        __syncthreads();
-    }
-    unsigned char *stage = lds + (ROPE ? a.rope.tab_bytes : 0);
-
-    float zacc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
-
-    f32x16_t acc[TPW][TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i)
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    // The stage loop is kept regular so the compiler can count the loads in
-    // flight: the stage count is rounded up to a multiple of PF (extra stages
-    // load nothing and add zeros) and every slot is refilled unconditionally
-    // (a refill past the range gets the out-of-range offset).
-    const int ntiles = tok_hi > tok_lo ? (tok_hi - tok_lo + TT - 1) / TT : 0;
-    const int nstages = (ntiles + PF - 1) / PF * PF;
-    auto offset = [&](int t) -> uint32_t {
-        return t < tok_hi ? (uint32_t)(t * D + q * 8) * 2u : kOOB;
-    };
-    u32x4_t kreg[PF][U], vreg[PF][U];
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t off = offset(tok_lo + row + u * RPS + p * TT);
-            kreg[p][u] = load16p<SVLA_KV_AUX>(rK, off);
-            vreg[p][u] = load16p<SVLA_KV_AUX>(rV, off);
-        }
-
-    const int m = lane & 31, g = lane >> 5;
-    const int mt0 = SPLITK ? 0 : (wave >> 1) * TPW;
-    const int nt0 = SPLITK ? 0 : (wave & 1) * TPW;
-    constexpr int GPW = SPLITK ? GPS / 4 : GPS;  // 16-token groups per wave per stage
-    // lane part of a fragment element's LDS index (k-slot i reads row 16 gi + g + 2 i)
-    int kl[TPW], vl[TPW];
-#pragma unroll
-    for (int tm = 0; tm < TPW; ++tm) {
-        const int f = 32 * (mt0 + tm) + m;
-        kl[tm] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
-    }
-#pragma unroll
-    for (int tn = 0; tn < TPW; ++tn) {
-        const int f = 32 * (nt0 + tn) + m;
-        vl[tn] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
-    }
-
-    for (int it0 = 0; it0 < nstages; it0 += PF) {
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int it = it0 + p;
-            unsigned char *st = stage + (it & 1) * STAGEB;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int r = row + u * RPS;              // row within the stage
-                const int tok = tok_lo + r + it * TT;
-                // phi(k), z, (rotation), stage to LDS
-                u32x4_t kr;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) kr[e] = relu_bf16x2(kreg[p][u][e]);
-                float kf[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kf[2 * e] = bf16lo(kr[e]);
-                    kf[2 * e + 1] = bf16hi(kr[e]);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
-                const int cpos = swz16<D>(r, q);
-                if constexpr (ROPE) {
-                    rope_rotate<4>(kf, rope_pos((uint32_t)tok, frame_lo, a.rope), pp, tab);
-                    u32x4_t hi, lo;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        unsigned short h0 = f2bf(kf[2 * e]), h1 = f2bf(kf[2 * e + 1]);
-                        float r0 = kf[2 * e] - as_f32((unsigned int)h0 << 16);
-                        float r1 = kf[2 * e + 1] - as_f32((unsigned int)h1 << 16);
-                        hi[e] = (unsigned int)h0 | ((unsigned int)h1 << 16);
-                        lo[e] = pack_bf16(r0, r1);
-                    }
-                    *(u32x4_t *)(st + r * ROWB + cpos * 16) = hi;
-                    *(u32x4_t *)(st + TILEB + r * ROWB + cpos * 16) = lo;
-                } else {
-                    *(u32x4_t *)(st + r * ROWB + cpos * 16) = kr;
-                }
-                *(u32x4_t *)(st + NK * TILEB + r * ROWB + cpos * 16) = vreg[p][u];
-            }
-            lds_barrier();
-
-            // refill this register slot with the stage PF ahead
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t off = offset(tok_lo + row + u * RPS + (it + PF) * TT);
-                kreg[p][u] = load16p<SVLA_KV_AUX>(rK, off);
-                vreg[p][u] = load16p<SVLA_KV_AUX>(rV, off);
-            }
-
-            const unsigned short *Kh = (const unsigned short *)st;
-            const unsigned short *Kl = (const unsigned short *)(st + TILEB);
-            const unsigned short *Vs = (const unsigned short *)(st + NK * TILEB);
-#pragma unroll
-            for (int gg = 0; gg < GPW; ++gg) {
-                const int gi = SPLITK ? wave + 4 * gg : gg;
-                bf16x8_t av[TPW], al[TPW], bv[TPW];
-#pragma unroll
-                for (int tm = 0; tm < TPW; ++tm) {
-                    const unsigned short *ph = Kh + 16 * gi * D + kl[tm];
-                    const unsigned short *pl = Kl + 16 * gi * D + kl[tm];
-                    u16x8_t x, y;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        x[i] = ph[2 * i * D];
-                        if constexpr (ROPE) y[i] = pl[2 * i * D];
-                    }
-                    av[tm] = __builtin_bit_cast(bf16x8_t, x);
-                    if constexpr (ROPE) al[tm] = __builtin_bit_cast(bf16x8_t, y);
-                }
-#pragma unroll
-                for (int tn = 0; tn < TPW; ++tn) {
-                    const unsigned short *pv = Vs + 16 * gi * D + vl[tn];
-                    u16x8_t x;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] = pv[2 * i * D];
-                    bv[tn] = __builtin_bit_cast(bf16x8_t, x);
-                }
-#pragma unroll
-                for (int tm = 0; tm < TPW; ++tm)
-#pragma unroll
-                    for (int tn = 0; tn < TPW; ++tn) {
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
-                        if constexpr (ROPE)
-                            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[tm], bv[tn], acc[tm][tn], 0, 0, 0);
-                    }
-            }
-        }
-    }
-    __syncthreads();   // every wave is done with the stage buffers
-
-    // ---- epilogue: write S_part (row-major [k][v]) and z_part
-    const long unit = (bh * a.nb + c) * a.splits + s;
-    const auto rS = make_rsrc(a.S_part + unit * D * D, D * D * 4);
-    const auto rz = make_rsrc(a.z_part + unit * D, D * 4);
-    float *red = (float *)stage;
-    float *zred = (float *)(stage + (SPLITK ? 4 * 16 * 64 * 4 : 0));
-    if constexpr (SPLITK) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[0][0][r];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zred[tid * 8 + e] = zacc[e];
-    __syncthreads();
-    if constexpr (SPLITK) {
-        // thread -> 4 consecutive columns of one row; fixed summation order
-        const int e0 = tid * 4, rr = e0 / 32, c0 = e0 % 32;
-        u32x4_t out;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ln = (c0 + j) + 32 * ((rr >> 2) & 1);
-            const int r = 4 * (rr >> 3) + (rr & 3);
-            float v = red[(0 * 16 + r) * 64 + ln];
-            v += red[(1 * 16 + r) * 64 + ln];
-            v += red[(2 * 16 + r) * 64 + ln];
-            v += red[(3 * 16 + r) * 64 + ln];
-            out[j] = as_u32(v);
-        }
-        store16(rS, (uint32_t)(rr * D + c0) * 4u, out);
-    } else {
-#pragma unroll
-        for (int tm = 0; tm < TPW; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < TPW; ++tn)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rr = 32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const int cc = 32 * (nt0 + tn) + m;
-                    store4(rS, (uint32_t)(rr * D + cc) * 4u, acc[tm][tn][r]);
-                }
-    }
-    if (tid < D) {
-        const int qq = tid >> 3, e = tid & 7;
-        float v = 0.f;
-        for (int j = 0; j < kThreads / CPR; ++j) v += zred[(qq + CPR * j) * 8 + e];
-        store4(rz, (uint32_t)tid * 4u, v);
-    }
-    if constexpr (FUSE) fused_scan<D, true>(a, bh, tid);
-    (void)RPS;
-}
-
-// ---------------------------------------------------------------------------
-// svla_state_build, bf16 inputs without RoPE, loads straight to LDS.
-//
-// The same contraction as svla_state_build_bf16, but K and V travel from
-// global memory into an R-deep ring of LDS stages with buffer_load ... lds
-// (16 bytes per lane, one kilobyte per wave instruction), so R - 1 stages of
-// loads stay in flight without holding registers.  phi is applied to the
-// K fragments after they are read from LDS, and z is summed from those
-// fragments.  Rows past the end of the range are masked when fragments are
-// read, so whatever an out-of-range load leaves in LDS never enters a sum.
-// Each stage buffer is its own LDS object, which lets the compiler tell the
-// loads of different stages apart instead of waiting for all of them.
-// ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 template <int D, int U, int R, int DG>
 __global__ void __launch_bounds__(kThreads)
 svla_state_build_dma(const BuildArgs a)
 {
-    // D: width of the tile this workgroup contracts; DG: feature count of the
-    // data.  DG == 2 D is the quadrant split for d = 128: four workgroups per
-    // (b,h,block,split), each computing one 64 x 64 quadrant of S.
     constexpr int CPR = D / 8;            // 16-byte chunks per token row
     constexpr int RPW = 64 / CPR;         // rows one wave instruction covers
     constexpr int RPS = kThreads / CPR;   // rows one pass of the 4 waves covers
@@ -1065,10 +872,252 @@ svla_state_build_dma(const BuildArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// svla_state_build, bf16 inputs with RoPE: wave-private streams.
+//
+// Workgroup = (bh, block c, split s[, quadrant]).  Its token range is cut
+// into wave stages of TW tokens and wave w takes stages w, w + 4, w + 8, ...
+// Each wave keeps PF stages of K/V loads in flight in registers, applies phi,
+// the rotation and the bf16 hi/lo split to its K chunks (one token, 8
+// features per lane), writes the stage into an LDS slot of its own and
+// contracts it from there on v_mfma_f32_32x32x16_bf16, which sums over
+// tokens: each lane gathers 8 tokens of one feature from the slot rows
+// (lanes 32-63 take the odd tokens so the two half-waves read disjoint
+// banks); the hi and lo parts make two MFMAs, so the state keeps about 16
+// bits of the rotated key.  z sums the unrotated phi(k) on the vector ALU.
+// No wave reads another wave's slot, and the LDS operations of one wave
+// execute in program order, so the main loop needs no barrier and the slot
+// can be overwritten by the next stage right after it was read.  Every wave
+// accumulates the whole tile; the four tiles are summed through LDS at the
+// end, in wave order.  Rows past the range load zeros (buffer range
+// check), which add nothing.
+//   D = DG     : the whole d x d state (d = 32, 64).
+//   DG = 128   : D = 64 quadrant split; four workgroups per unit, each
+//                one 64 x 64 quadrant of S from K and V half-rows.
+// ---------------------------------------------------------------------------
+template <int D, int DG, int PF, int U>
+__global__ void __launch_bounds__(kThreads)
+svla_state_build_rope(const BuildArgs a)
+{
+    constexpr int CPR = D / 8;            // 16-byte chunks per (half-)row
+    constexpr int RPW = 64 / CPR;         // rows one wave load instruction covers
+    constexpr int TW = U * RPW;           // tokens per wave stage
+    constexpr int GPW = TW / 16;          // 16-token groups per wave stage
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = TW * ROWB;
+    constexpr int NK = 2;                 // K tiles: rotated hi and lo
+    constexpr int SLOTB = (NK + 1) * TILEB;
+    constexpr int TPW = D / 32;           // 32 x 32 tiles per side
+    constexpr bool QUAD = DG != D;
+    static_assert(TW % 16 == 0, "a wave stage holds whole 16-token groups");
+    static_assert(!QUAD || (DG == 128 && D == 64), "the quadrant split is for d = 128");
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    long wid = blockIdx.x;
+    int qm = 0, qn = 0;
+    if constexpr (QUAD) {
+        // Quadrants of one unit get workgroup ids 8 apart, so the round-robin
+        // dispatch puts all four on one XCD and its L2 serves the K/V
+        // half-rows they share.
+        const long x = wid % 8, r = wid / 8;
+        const int q = (int)(r % 4);
+        qm = q >> 1;
+        qn = q & 1;
+        wid = (r / 4) * 8 + x;
+        if (wid >= (long)a.nb * a.splits * a.BH) return;
+    }
+    const unsigned per_bh = (unsigned)(a.splits * a.nb);
+    const long bh = wid / per_bh;
+    const int rest = (int)(wid - bh * per_bh);
+    const int c = rest / a.splits, s = rest % a.splits;
+    const int tok_lo = c * a.n + s * a.chunk;
+    const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
+
+    const uint32_t slice = (uint32_t)a.N * DG * 2;
+    const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
+    const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
+    const int kcol = 64 * qm, vcol = 64 * qn;   // first feature of this tile in K / V
+
+    // lane -> (row lane / CPR + u RPW of the wave stage, chunk q of the row)
+    const int row = lane / CPR, q = lane % CPR;
+
+    // this wave's stages: st = wave + 4 i, i < nw
+    const int nst = tok_hi > tok_lo ? (tok_hi - tok_lo + TW - 1) / TW : 0;
+    const int nw = nst > wave ? (nst - wave + 3) / 4 : 0;
+    auto offset = [&](int i, int u, int col) -> uint32_t {
+        const int t = tok_lo + (wave + 4 * i) * TW + u * RPW + row;
+        return t < tok_hi ? (uint32_t)(t * DG + col + q * 8) * 2u : kOOB;
+    };
+    // Register slot p holds stage i with i % PF == p.  The scheduling
+    // barriers keep the slots' loads in slot order, the order the loop
+    // consumes them in, so a wait for the oldest slot leaves the younger
+    // slots' loads in flight.
+    u32x4_t kreg[PF][U], vreg[PF][U];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            kreg[p][u] = load16p<SVLA_KV_AUX>(rK, offset(p, u, kcol));
+            vreg[p][u] = load16p<SVLA_KV_AUX>(rV, offset(p, u, vcol));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // the RoPE table is built while the first stages load
+    float2 *tab = (float2 *)lds;
+    const uint32_t frame_lo = tok_lo < tok_hi ? fdiv((uint32_t)tok_lo, a.rope.div_hw) : 0;
+    const uint32_t frame_hi = tok_lo < tok_hi ? fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw) : 0;
+    const int nf = (int)(frame_hi - frame_lo) + 1;
+    rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+    const RopePairs<4> pp = rope_pairs<4>(a.rope, kcol + q * 8, nf);
+    lds_barrier();
+    unsigned char *slot = lds + a.rope.tab_bytes + wave * SLOTB;
+
+    f32x16_t acc[TPW][TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    float zacc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
+
+    const int m = lane & 31, g = lane >> 5;
+    // lane part of a fragment element's LDS index: k-slot i of group gi reads
+    // row 16 gi + g + 2 i; the row's parity (= g) fixes the swizzle
+    int fl[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int f = 32 * t + m;
+        fl[t] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
+    }
+
+    // The loop is kept regular so the compiler can count the loads in flight:
+    // the stage count is rounded up to a multiple of PF (the extra stages
+    // load nothing and add zeros) and every register slot is refilled.
+    const int nwr = (nw + PF - 1) / PF * PF;
+    for (int i0 = 0; i0 < nwr; i0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int i = i0 + p;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = u * RPW + row;              // row within the stage
+                const int cpos = swz16<D>(r, q);
+                u32x4_t kr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) kr[e] = relu_bf16x2(kreg[p][u][e]);
+                float kf[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kf[2 * e] = bf16lo(kr[e]);
+                    kf[2 * e + 1] = bf16hi(kr[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
+                const int tok = tok_lo + (wave + 4 * i) * TW + r;
+                rope_rotate<4>(kf, rope_pos((uint32_t)tok, frame_lo, a.rope), pp, tab);
+                u32x4_t hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = pack_bf16(kf[2 * e], kf[2 * e + 1]);
+                    lo[e] = pack_bf16(kf[2 * e] - bf16lo(hi[e]), kf[2 * e + 1] - bf16hi(hi[e]));
+                }
+                *(u32x4_t *)(slot + r * ROWB + cpos * 16) = hi;
+                *(u32x4_t *)(slot + TILEB + r * ROWB + cpos * 16) = lo;
+                *(u32x4_t *)(slot + NK * TILEB + r * ROWB + cpos * 16) = vreg[p][u];
+            }
+            // refill this register slot with the stage PF ahead
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                kreg[p][u] = load16p<SVLA_KV_AUX>(rK, offset(i + PF, u, kcol));
+                vreg[p][u] = load16p<SVLA_KV_AUX>(rV, offset(i + PF, u, vcol));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const unsigned short *Kh = (const unsigned short *)slot;
+            const unsigned short *Kl = (const unsigned short *)(slot + TILEB);
+            const unsigned short *Vs = (const unsigned short *)(slot + NK * TILEB);
+#pragma unroll
+            for (int gi = 0; gi < GPW; ++gi) {
+                bf16x8_t av[TPW], al[TPW], bv[TPW];
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    u16x8_t x, y, w;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        x[e] = Kh[16 * gi * D + fl[t] + 2 * e * D];
+                        y[e] = Kl[16 * gi * D + fl[t] + 2 * e * D];
+                        w[e] = Vs[16 * gi * D + fl[t] + 2 * e * D];
+                    }
+                    av[t] = __builtin_bit_cast(bf16x8_t, x);
+                    al[t] = __builtin_bit_cast(bf16x8_t, y);
+                    bv[t] = __builtin_bit_cast(bf16x8_t, w);
+                }
+#pragma unroll
+                for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < TPW; ++tn) {
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+                    }
+            }
+        }
+    }
+
+    // ---- epilogue: the four waves' tiles summed in wave order, then
+    // S_part (row-major [k][v], row stride DG) and z_part
+    float *red = (float *)(lds + a.rope.tab_bytes);                // D x D floats
+    float *zred = red + D * D;                                     // 256 x 8 floats
+    __syncthreads();          // every wave is done with its slot
+#pragma unroll 1
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int tm = 0; tm < TPW; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TPW; ++tn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = 32 * tm + 8 * (r >> 2) + 4 * g + (r & 3);
+                        const int cc = 32 * tn + m;
+                        float *p = red + rr * D + cc;
+                        *p = w == 0 ? acc[tm][tn][r] : *p + acc[tm][tn][r];
+                    }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zred[D + tid * 8 + e] = zacc[e];
+    __syncthreads();
+    if (tid < D) {
+        // feature tid = 8 qq + e: summed over the threads that hold chunk qq
+        const int qq = tid >> 3, e = tid & 7;
+        float v = 0.f;
+        for (int j = 0; j < kThreads / CPR; ++j) v += zred[D + (qq + CPR * j) * 8 + e];
+        zred[tid] = v;
+    }
+    __syncthreads();
+    const long unit = (bh * a.nb + c) * a.splits + s;
+    const auto rS = make_rsrc(a.S_part + unit * DG * DG, DG * DG * 4);
+    const auto rz = make_rsrc(a.z_part + unit * DG, DG * 4);
+#pragma unroll
+    for (int e0 = tid * 4; e0 < D * D; e0 += kThreads * 4) {
+        const int rr = e0 / D, c0 = e0 % D;
+        store16(rS, (uint32_t)((kcol + rr) * DG + vcol + c0) * 4u, *(const u32x4_t *)(red + e0));
+    }
+    if (tid < D && qn == 0) store4(rz, (uint32_t)(kcol + tid) * 4u, zred[tid]);
+}
+
+// ---------------------------------------------------------------------------
 // svla_state_build, fp32 inputs: the same walk with fp32 rows staged and
 // v_mfma_f32_32x32x2_f32 (one token per half-wave per instruction).
 // ---------------------------------------------------------------------------
-template <int D, bool ROPE, bool FUSE>
+template <int D, bool ROPE>
 __global__ void __launch_bounds__(kThreads)
 svla_state_build_f32(const BuildArgs a)
 {
@@ -1213,19 +1262,18 @@ svla_state_build_f32(const BuildArgs a)
         for (int j = 0; j < kThreads / CPR; ++j) v += zred[(qq + CPR * j) * 4 + e];
         store4(rz, (uint32_t)tid * 4u, v);
     }
-    if constexpr (FUSE) fused_scan<D, false>(a, bh, tid);
 }
 
 // ---------------------------------------------------------------------------
-// svla_apply, bf16 inputs.  Workgroup = (bh, block c, token tile).
+// svla_apply, bf16 inputs, d = 32.  Workgroup = (bh, block c, token tile);
+// the tiles of one block run on one XCD.
 // O^T = S^T phi~(Q)^T on v_mfma_f32_16x16x32_bf16: the state is the A
 // operand (kept in registers for the whole tile, loaded once from the
 // packed layout), phi~(q) the B operand straight from a 16-byte load per
 // lane (token = lane % 16, 8 features of chunk 4 ks + lane / 16).  The
 // denominator phi(q) . z is a per-lane partial dot product reduced over the
-// 4 lanes that share a token.
-//   d = 32, 64: each wave takes every 4th 16-token group, all output features.
-//   d = 128   : every wave takes every group, for its own 32 output features.
+// 4 lanes that share a token.  Each wave takes every 4th 16-token group,
+// with all output features.
 // ---------------------------------------------------------------------------
 template <int D, bool ROPE>
 __global__ void __launch_bounds__(kThreads)
@@ -1233,15 +1281,16 @@ svla_apply_bf16(const ApplyArgs a)
 {
     constexpr int MT = D / 16;
     constexpr int KS = D / 32;
-    constexpr bool SPLITM = (D == 128);
-    constexpr int MW = SPLITM ? 2 : MT;
+    constexpr int MW = MT;
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tile = blockIdx.x % a.tiles;
-    const int c = (blockIdx.x / a.tiles) % a.nb;
-    const long bh = blockIdx.x / ((long)a.tiles * a.nb);
+    const long lid = xcd_logical(a.groups);
+    if (lid >= a.groups) return;
+    const int tile = (int)(lid % a.tiles);
+    const int c = (int)((lid / a.tiles) % a.nb);
+    const long bh = lid / ((long)a.tiles * a.nb);
     const int t_lo = c * a.n + tile * a.tile;
     const int t_hi = min(t_lo + a.tile, (c + 1) * a.n);
     const long unit = bh * a.nb + c;
@@ -1253,7 +1302,7 @@ svla_apply_bf16(const ApplyArgs a)
     const auto rz = make_rsrc(a.z_pre + unit * D, D * 4);
 
     const int kg = lane >> 4, tl = lane & 15;
-    const int m0 = SPLITM ? 2 * wave : 0;
+    constexpr int m0 = 0;
 
     bf16x8_t sf[MW][KS];
 #pragma unroll
@@ -1289,9 +1338,9 @@ svla_apply_bf16(const ApplyArgs a)
 
     // groups of this wave: g_first, g_first + g_step, ...; the loads of GB
     // groups are issued together before any of them is used.
-    constexpr int GB = SPLITM ? 2 : 4;
+    constexpr int GB = 4;
     const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
-    const int g_first = SPLITM ? 0 : wave, g_step = SPLITM ? 1 : 4;
+    const int g_first = wave, g_step = 4;
     for (int gb = g_first; gb < ngroups; gb += GB * g_step) {
     u32x4_t qb[GB][KS];
 #pragma unroll
@@ -1299,7 +1348,7 @@ svla_apply_bf16(const ApplyArgs a)
         const int tok = t_lo + 16 * (gb + j * g_step) + tl;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qb[j][ks] = load16p<SPLITM ? 0 : SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB);
+            qb[j][ks] = load16p<SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB);
     }
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
@@ -1362,6 +1411,183 @@ svla_apply_bf16(const ApplyArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// svla_apply, bf16 inputs, d = 64 and 128: the block state in LDS.
+//
+// Workgroup = (bh, block c, token tile); the tiles of one block run on one
+// XCD.  The packed state operand of the block (d*d bf16, 1 KB per MFMA
+// fragment) is copied to LDS once per workgroup, and the waves split the
+// tile's 16-token groups (wave w takes groups w, w + 4, ...), so each Q
+// element is loaded and prepared once.  Per group, O^T = S^T phi~(Q)^T on
+// v_mfma_f32_16x16x32_bf16: the A fragments come from LDS, phi~(q) is the
+// B operand straight from a 16-byte load per lane (token = lane % 16,
+// features 8 (4 ks + lane / 16) ...).  The denominator runs on the matrix
+// cores too: one more A tile whose rows 4j and 4j + 1 hold z split into
+// bf16 hi and lo parts (zero elsewhere), against the unrotated phi(q), puts
+// phi(q) . z (to ~16 bits of z) in the first two accumulator values of
+// every lane of the token.  PF groups of Q loads stay in flight per wave.
+// ---------------------------------------------------------------------------
+template <int D, bool ROPE, int PF>
+__global__ void __launch_bounds__(kThreads)
+svla_apply_lds(const ApplyArgs a)
+{
+    constexpr int MT = D / 16;            // 16-feature m-tiles of the output
+    constexpr int KS = D / 32;            // 32-deep k-steps
+    constexpr int NFRAG = MT * KS;        // 1 KB fragments of the packed state
+    static_assert(NFRAG % 4 == 0, "the four waves copy the state in equal shares");
+    __shared__ __attribute__((aligned(16))) unsigned char sS[NFRAG * 1024];
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // RoPE table
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const long lid = xcd_logical(a.groups);
+    if (lid >= a.groups) return;
+    const int tile = (int)(lid % a.tiles);
+    const int c = (int)((lid / a.tiles) % a.nb);
+    const long bh = lid / ((long)a.tiles * a.nb);
+    const int t_lo = c * a.n + tile * a.tile;
+    const int t_hi = min(t_lo + a.tile, (c + 1) * a.n);
+    const long unit = bh * a.nb + c;
+
+    const uint32_t slice = (uint32_t)a.N * D * 2;
+    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
+    const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
+    const auto rS = make_rsrc((const char *)a.S_op + unit * D * D * 2, D * D * 2);
+    const auto rz = make_rsrc(a.z_pre + unit * D, D * 4);
+    const int kg = lane >> 4, tl = lane & 15;
+
+    // 1. the state operand -> LDS, one fragment per wave instruction
+    constexpr int FPW = NFRAG / 4;
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+        const int f = wave + 4 * j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(sS + f * 1024), 16,
+                                                 (uint32_t)(f * 1024 + lane * 16), 0, 0, 0);
+    }
+    // 2. z for this lane's k positions
+    u32x4_t zr[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        zr[ks][0] = load16(rz, (uint32_t)(8 * (4 * ks + kg)) * 4u);
+        zr[ks][1] = load16(rz, (uint32_t)(8 * (4 * ks + kg) + 4) * 4u);
+    }
+    // 3. the first PF groups of Q (slot p holds this wave's group i, i % PF == p;
+    // the scheduling barriers keep the loads in slot order)
+    const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
+    const int nw = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
+    const int nwr = (nw + PF - 1) / PF * PF;
+    auto qoff = [&](int i, int ks) -> uint32_t {
+        const int tok = t_lo + 16 * (wave + 4 * i) + tl;
+        return tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB;
+    };
+    u32x4_t qreg[PF][KS];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(p, ks));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // the z tile: lane (rho + 16 kg), k = 32 ks + 8 kg + i holds z_hi[k] in
+    // rows rho = 4j, z_lo[k] in rows 4j + 1, 0 in the others
+    wait_vmcnt<PF * KS>();
+    bf16x8_t zt[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u16x8_t h;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = as_f32(zr[ks][i >> 2][i & 3]);
+            const unsigned short hi = f2bf(v);
+            const unsigned short lo = f2bf(v - as_f32((unsigned int)hi << 16));
+            h[i] = (tl & 3) == 0 ? hi : (tl & 3) == 1 ? lo : (unsigned short)0;
+        }
+        zt[ks] = __builtin_bit_cast(bf16x8_t, h);
+    }
+
+    float2 *tab = (float2 *)lds;
+    uint32_t frame_lo = 0;
+    RopePairs<4> pp[KS];
+    if constexpr (ROPE) {
+        frame_lo = t_lo < t_hi ? fdiv((uint32_t)t_lo, a.rope.div_hw) : 0;
+        const uint32_t frame_hi = t_lo < t_hi ? fdiv((uint32_t)(t_hi - 1), a.rope.div_hw) : 0;
+        const int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pp[ks] = rope_pairs<4>(a.rope, 8 * (4 * ks + kg), nf);
+    }
+    lds_barrier();         // every wave's state fragments (and the table) are in LDS
+
+    for (int i0 = 0; i0 < nwr; i0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int i = i0 + p;
+            const int tok = t_lo + 16 * (wave + 4 * i) + tl;
+            u32x4_t qr[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qr[ks] = qreg[p][ks];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(i + PF, ks));
+            __builtin_amdgcn_sched_barrier(0);
+
+            bf16x8_t qu[KS], qf[KS];
+            RopePos rp{0, 0, 0};
+            if constexpr (ROPE) rp = rope_pos((uint32_t)tok, frame_lo, a.rope);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4_t pq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[ks][e]);
+                qu[ks] = __builtin_bit_cast(bf16x8_t, pq);
+                if constexpr (ROPE) {
+                    float pf[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pf[2 * e] = bf16lo(pq[e]);
+                        pf[2 * e + 1] = bf16hi(pq[e]);
+                    }
+                    rope_rotate<4>(pf, rp, pp[ks], tab);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pq[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
+                    qf[ks] = __builtin_bit_cast(bf16x8_t, pq);
+                } else {
+                    qf[ks] = qu[ks];
+                }
+            }
+            f32x4_t dz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                dz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zt[ks], qu[ks], dz, 0, 0, 0);
+            f32x4_t acc[MT];
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                acc[mi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8_t sf = *(const bf16x8_t *)(sS + (mi * KS + ks) * 1024 + lane * 16);
+                    acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf, qf[ks], acc[mi], 0, 0, 0);
+                }
+            }
+            const float den = dz[0] + dz[1] + a.eps;
+            const float inv = den != 0.f ? 1.0f / den : 0.f;
+            // lane holds O[tok][(D/4) kg + 4 mi + r]: D/4 consecutive features
+            const bool valid = tok < t_hi;
+#pragma unroll
+            for (int h = 0; h < MT / 2; ++h) {
+                u32x4_t o;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    o[2 * e] = pack_bf16(acc[2 * h + e][0] * inv, acc[2 * h + e][1] * inv);
+                    o[2 * e + 1] = pack_bf16(acc[2 * h + e][2] * inv, acc[2 * h + e][3] * inv);
+                }
+                const int v0 = (D / 4) * kg + 8 * h;
+                store16p<SVLA_O_AUX>(rO, valid ? (uint32_t)(tok * D + v0) * 2u : kOOB, o);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // svla_apply, fp32 inputs: v_mfma_f32_16x16x4_f32, lane chunk = 4 features
 // of chunk 4 kq + lane / 16; the state operand stays fp32.
 // ---------------------------------------------------------------------------
@@ -1377,9 +1603,11 @@ svla_apply_f32(const ApplyArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tile = blockIdx.x % a.tiles;
-    const int c = (blockIdx.x / a.tiles) % a.nb;
-    const long bh = blockIdx.x / ((long)a.tiles * a.nb);
+    const long lid = xcd_logical(a.groups);
+    if (lid >= a.groups) return;
+    const int tile = (int)(lid % a.tiles);
+    const int c = (int)((lid / a.tiles) % a.nb);
+    const long bh = lid / ((long)a.tiles * a.nb);
     const int t_lo = c * a.n + tile * a.tile;
     const int t_hi = min(t_lo + a.tile, (c + 1) * a.n);
     const long unit = bh * a.nb + c;
@@ -1532,38 +1760,35 @@ struct Plan {
     int B, H, nb, n, d;
     long BH;
     int esize;                 // bytes per Q/K/V/O element
-    int splits, chunk;         // build
+    bool dma;                  // build straight to LDS (bf16 without RoPE)
+    int splits, chunk;         // build: workgroups per block, tokens per workgroup
     int tile, tiles;           // apply
-    bool fuse;                 // scan runs in the build's last workgroup per (b,h)
     size_t lds_build, lds_apply;
-    size_t off_ctr, off_spart, off_zpart, off_sop, off_zpre, total;
+    size_t off_spart, off_zpart, off_sop, off_zpre, total;
     RopeK rope;
 };
 
-// A value that differs between any two calls of the process (see arrive()).
-unsigned next_epoch()
-{
-    static std::atomic<unsigned> e{(unsigned)std::chrono::steady_clock::now().time_since_epoch().count()};
-    return e.fetch_add(1, std::memory_order_relaxed);
-}
-
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// bf16 state build: chunks per thread per stage and stages of loads in flight
-constexpr int build_u(bool rope) { return rope ? SVLA_BUILD_U_ROPE : SVLA_BUILD_U; }
-constexpr int build_pf(bool rope) { return rope ? SVLA_BUILD_PF_ROPE : SVLA_BUILD_PF; }
+// RoPE build (svla_state_build_rope): stages in flight per wave and 16-byte
+// loads per lane per tensor per stage (at least one 16-token group per stage:
+// a wave load covers 64 / (d / 8) rows, 8 rows for the 64-feature rows and
+// half-rows of d >= 64)
+constexpr int rope_pf() { return SVLA_ROPE_PF; }
+constexpr int rope_u(int d) { return d == 32 || SVLA_ROPE_U >= 2 ? SVLA_ROPE_U : 2; }
+constexpr int rope_tokens(int d) { return rope_u(d) * 64 / ((d == 128 ? 64 : d) / 8); }
 
-
-// Splits of a block's tokens over workgroups: enough workgroups to fill the
-// chip (about SVLA_TARGET_WGS), but never fewer than SVLA_MIN_SPLIT_PER_D * d
-// tokens per split, so the fp32 partial state (4 d^2 bytes) stays a small
-// fraction of the K/V bytes it summarises (1/8 at the default).
-int pick_splits(long units, int n, int d, int *chunk_out)
+// Splits of a block's tokens over workgroups: about `target` workgroups per
+// launch, but never fewer than SVLA_MIN_SPLIT_PER_D * d tokens per split, so
+// the fp32 partial state (4 d^2 bytes) stays a small fraction of the K/V
+// bytes it summarises (1/8 at the default).  Measured: the build without
+// RoPE runs best with one or two long-lived workgroups per CU, the RoPE
+// build (bound by its vector ALU work) with many.
+int pick_splits(long units, int n, int d, long target, int *chunk_out)
 {
-    constexpr int G = 64;   // chunk granularity; independent of the stage size, so the
-                            // workspace size does not depend on RoPE or tuning
+    constexpr int G = 64;   // chunk granularity; independent of the stage size
     if (n <= 0 || units <= 0) { *chunk_out = G; return 0; }
-    long want = (SVLA_TARGET_WGS + units - 1) / units;
+    long want = (target + units - 1) / units;
     long cap = n / (SVLA_MIN_SPLIT_PER_D * d);
     if (cap < 1) cap = 1;
     long s = want < cap ? want : cap;
@@ -1628,20 +1853,35 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     p->esize = dt == SVLA_BF16 ? 2 : 4;
     st = check_rope(fn, rope, d, &p->rope);
     if (st) return st;
+    p->dma = p->esize == 2 && !p->rope.on;
+    const long units = p->BH * nb;
+    int chunk_dma = 0, chunk_other = 0;
+    const int splits_dma = pick_splits(units, n, d, SVLA_DMA_WGS, &chunk_dma);
+    const int splits_other = pick_splits(units, n, d, SVLA_ROPE_WGS, &chunk_other);
     if (op == SVLA_OP_STATE_BUILD) {
+        // one workgroup per block: its partial is the block's local state
         p->splits = n > 0 ? 1 : 0;
         p->chunk = n > 0 ? n : 1;
     } else {
-        p->splits = pick_splits(p->BH * nb, n, d, &p->chunk);
+        p->splits = p->dma ? splits_dma : splits_other;
+        p->chunk = p->dma ? chunk_dma : chunk_other;
     }
-    p->tile = d == 128 ? SVLA_APPLY_TILE128 : (p->rope.on ? SVLA_APPLY_TILE_ROPE : SVLA_APPLY_TILE32);
+    p->tile = (p->esize == 2 && d >= 64) ? SVLA_APPLY_TILE_LDS
+              : d == 128 ? SVLA_APPLY_TILE128 : (p->rope.on ? SVLA_APPLY_TILE_ROPE : SVLA_APPLY_TILE32);
     p->tiles = n > 0 ? (n + p->tile - 1) / p->tile : 0;
 
-    // LDS: [RoPE table][stage buffers | epilogue]
-    const size_t stage = (size_t)2 * ((p->esize == 2 && p->rope.on) ? 3 : 2) * 4096 *
-                         (p->esize == 2 ? build_u(p->rope.on) : 1);
-    const size_t epi = (d == 32 ? 16384 : 0) + 8192;
-    p->lds_build = stage > epi ? stage : epi;
+    // dynamic LDS: [RoPE table][stage buffers | epilogue] (the direct-to-LDS
+    // build has static LDS only)
+    if (p->esize == 2) {
+        const int td = d == 128 ? 64 : d;                 // tile side (quadrants for d = 128)
+        const size_t slots = (size_t)4 * 3 * rope_tokens(d) * td * 2;
+        const size_t epi = ((size_t)td * td + td + 2048) * 4;
+        p->lds_build = p->dma ? 0 : (slots > epi ? slots : epi);
+    } else {
+        const size_t stage = (size_t)2 * 2 * 4096;
+        const size_t epi = (d == 32 ? 16384 : 0) + 8192;
+        p->lds_build = stage > epi ? stage : epi;
+    }
     p->lds_apply = 0;
     if (p->rope.on) {
         const int hw = p->rope.gh * p->rope.gw;
@@ -1661,21 +1901,20 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
         p->lds_apply = (size_t)p->rope.tab_bytes;
     }
 
-    // workspace
+    // workspace: partial states (as many per block as either build writes,
+    // so the size does not depend on RoPE), packed prefix operands, prefix z
     size_t off = 0;
-    const size_t units = (size_t)p->BH * nb;
     const bool fused = op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP;
-    p->fuse = fused && d <= SVLA_FUSE_MAX_D && p->splits > 0 && nb > 0;
     if (fused) {
-        p->off_ctr = off; off = align256(off + (size_t)p->BH * 8);
-        p->off_spart = off; off = align256(off + units * p->splits * d * d * 4);
-        p->off_zpart = off; off = align256(off + units * p->splits * d * 4);
+        const size_t slots = (size_t)(splits_dma > splits_other ? splits_dma : splits_other);
+        p->off_spart = off; off = align256(off + (size_t)units * slots * d * d * 4);
+        p->off_zpart = off; off = align256(off + (size_t)units * slots * d * 4);
     }
     if (fused || op == SVLA_OP_APPLY) {
-        p->off_sop = off; off = align256(off + units * d * d * p->esize);
+        p->off_sop = off; off = align256(off + (size_t)units * d * d * p->esize);
     }
     if (fused) {
-        p->off_zpre = off; off = align256(off + units * d * 4);
+        p->off_zpre = off; off = align256(off + (size_t)units * d * 4);
     }
     p->total = off;
     return SVLA_OK;
@@ -1685,74 +1924,77 @@ inline bool misaligned(const void *ptr) { return ((uintptr_t)ptr & 15) != 0; }
 
 // ---- launchers ---------------------------------------------------------------
 
-template <int D, bool FUSE>
-void launch_build_f(const Plan &p, const BuildArgs &a, hipStream_t s)
+template <int D>
+void launch_build(const Plan &p, const BuildArgs &args, hipStream_t s)
 {
+    BuildArgs a = args;
+    a.splits = p.splits;
+    a.chunk = p.chunk;
     const unsigned grid = (unsigned)(p.BH * p.nb * p.splits);
-    const char *fz = FUSE ? "true" : "false";
+    const unsigned qgrid = (unsigned)((grid + 7) / 8 * 8 * 4);   // d = 128: four quadrants
     char nm[96];
-    if (SVLA_USE_DMA && p.esize == 2 && !p.rope.on && !FUSE) {
+    if (p.dma) {
         constexpr int U = D == 32 ? SVLA_DMA_U32 : SVLA_DMA_U;
         constexpr int R = D == 32 ? SVLA_DMA_R32 : SVLA_DMA_R;
-        if constexpr (D == 128 && SVLA_QUAD128) {
-            const unsigned qgrid = (unsigned)((grid + 7) / 8 * 8 * 4);
+        if constexpr (D == 128) {
             snprintf(nm, sizeof nm, "void svla_state_build_dma<64, %d, %d, 128>", U, R);
             launch(svla_state_build_dma<64, U, R, 128>, qgrid, 0, s, SLOT_BUILD, a, nm);
         } else {
             snprintf(nm, sizeof nm, "void svla_state_build_dma<%d, %d, %d, %d>", D, U, R, D);
             launch(svla_state_build_dma<D, U, R, D>, grid, 0, s, SLOT_BUILD, a, nm);
         }
-        return;
-    }
-    if (p.esize == 2) {
-        if (p.rope.on) {
-            snprintf(nm, sizeof nm, "void svla_state_build_bf16<%d, true, %d, %d, %s>", D,
-                     build_pf(true), build_u(true), fz);
-            launch(svla_state_build_bf16<D, true, build_pf(true), build_u(true), FUSE>, grid,
-                   p.lds_build, s, SLOT_BUILD, a, nm);
+    } else if (p.esize == 2) {
+        constexpr int PF = rope_pf(), U = rope_u(D);
+        if constexpr (D == 128) {
+            snprintf(nm, sizeof nm, "void svla_state_build_rope<64, 128, %d, %d>", PF, U);
+            launch(svla_state_build_rope<64, 128, PF, U>, qgrid, p.lds_build, s, SLOT_BUILD, a, nm);
         } else {
-            snprintf(nm, sizeof nm, "void svla_state_build_bf16<%d, false, %d, %d, %s>", D,
-                     build_pf(false), build_u(false), fz);
-            launch(svla_state_build_bf16<D, false, build_pf(false), build_u(false), FUSE>, grid,
-                   p.lds_build, s, SLOT_BUILD, a, nm);
+            snprintf(nm, sizeof nm, "void svla_state_build_rope<%d, %d, %d, %d>", D, D, PF, U);
+            launch(svla_state_build_rope<D, D, PF, U>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
         }
     } else {
-        snprintf(nm, sizeof nm, "void svla_state_build_f32<%d, %s, %s>", D,
-                 p.rope.on ? "true" : "false", fz);
-        if (p.rope.on) launch(svla_state_build_f32<D, true, FUSE>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
-        else launch(svla_state_build_f32<D, false, FUSE>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
+        snprintf(nm, sizeof nm, "void svla_state_build_f32<%d, %s>", D, p.rope.on ? "true" : "false");
+        if (p.rope.on) launch(svla_state_build_f32<D, true>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
+        else launch(svla_state_build_f32<D, false>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
     }
-}
-
-template <int D>
-void launch_build(const Plan &p, const BuildArgs &a, hipStream_t s)
-{
-    if constexpr (D <= SVLA_FUSE_MAX_D) {
-        if (p.fuse) { launch_build_f<D, true>(p, a, s); return; }
-    }
-    launch_build_f<D, false>(p, a, s);
 }
 
 template <int D, int MODE>
 void launch_scan_d(const Plan &p, const ScanArgs &a, hipStream_t s)
 {
-    const unsigned grid = (unsigned)(p.BH * (D * D / (kScanThreads * 4) + 1));
+    const unsigned grid = (unsigned)(p.BH * (ScanShape<D>::STILES + 1));
+    const bool bf = p.esize == 2;
     char nm[96];
-    snprintf(nm, sizeof nm, "void svla_state_scan_k<%d, %d, %s>", D, MODE, p.esize == 2 ? "true" : "false");
-    if (p.esize == 2) launch(svla_state_scan_k<D, MODE, true>, grid, 0, s, SLOT_SCAN, a, nm, kScanThreads);
-    else launch(svla_state_scan_k<D, MODE, false>, grid, 0, s, SLOT_SCAN, a, nm, kScanThreads);
+    if (MODE != SCAN_PACK && p.nb >= kScanLongChain) {
+        snprintf(nm, sizeof nm, "void svla_state_scan_k<%d, %d, %s, 4>", D, MODE, bf ? "true" : "false");
+        if (bf) launch(svla_state_scan_k<D, MODE, true, 4>, grid, 0, s, SLOT_SCAN, a, nm, 256);
+        else launch(svla_state_scan_k<D, MODE, false, 4>, grid, 0, s, SLOT_SCAN, a, nm, 256);
+    } else {
+        snprintf(nm, sizeof nm, "void svla_state_scan_k<%d, %d, %s, 1>", D, MODE, bf ? "true" : "false");
+        if (bf) launch(svla_state_scan_k<D, MODE, true, 1>, grid, 0, s, SLOT_SCAN, a, nm, 64);
+        else launch(svla_state_scan_k<D, MODE, false, 1>, grid, 0, s, SLOT_SCAN, a, nm, 64);
+    }
 }
 
 template <int D>
-void launch_apply(const Plan &p, const ApplyArgs &a, hipStream_t s)
+void launch_apply(const Plan &p, const ApplyArgs &args, hipStream_t s)
 {
-    const unsigned grid = (unsigned)(p.BH * p.nb * p.tiles);
+    ApplyArgs a = args;
+    a.groups = p.BH * p.nb * p.tiles;
+    const unsigned grid = xcd_grid(a.groups);
     char nm[96];
     snprintf(nm, sizeof nm, "void svla_apply_%s<%d, %s>", p.esize == 2 ? "bf16" : "f32", D,
              p.rope.on ? "true" : "false");
     if (p.esize == 2) {
-        if (p.rope.on) launch(svla_apply_bf16<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-        else launch(svla_apply_bf16<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+        if constexpr (D >= 64) {
+            constexpr int PF = SVLA_APPLY_PF;
+            snprintf(nm, sizeof nm, "void svla_apply_lds<%d, %s, %d>", D, p.rope.on ? "true" : "false", PF);
+            if (p.rope.on) launch(svla_apply_lds<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            else launch(svla_apply_lds<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+        } else {
+            if (p.rope.on) launch(svla_apply_bf16<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            else launch(svla_apply_bf16<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+        }
     } else {
         if (p.rope.on) launch(svla_apply_f32<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
         else launch(svla_apply_f32<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
@@ -1828,7 +2070,7 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
     sa.z_pre = (float *)(w + p.off_zpre);
     sa.S_fin = S_fin; sa.z_fin = z_fin;
     sa.nb = nb; sa.splits = p.splits;
-    if (p.splits > 0 && nb > 0) {
+    if (tokens) {
         BuildArgs ba;
         memset(&ba, 0, sizeof ba);
         ba.K = K; ba.V = V;
@@ -1837,18 +2079,11 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
         ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = p.splits; ba.chunk = p.chunk;
         ba.BH = p.BH;
         ba.rope = p.rope;
-        if (p.fuse) {
-            ba.counters = (unsigned long long *)(w + p.off_ctr);
-            ba.epoch = next_epoch();
-            ba.scan = sa;
-        }
         build_any(p, ba, s);
         if ((st = check_launch(fn))) return st;
     }
-    if (!p.fuse) {
-        scan_any<SCAN_FUSED>(p, sa, s);
-        if ((st = check_launch(fn))) return st;
-    }
+    scan_any<SCAN_FORWARD>(p, sa, s);
+    if ((st = check_launch(fn))) return st;
     if (tokens) {
         ApplyArgs aa;
         aa.Q = Q; aa.O = O; aa.S_op = w + p.off_sop; aa.z_pre = (const float *)(w + p.off_zpre);
@@ -1915,8 +2150,8 @@ svla_status svla_describe(svla_op op, svla_dtype dt, int B, int H, int nb, int n
     ApplyArgs aa;
     memset(&aa, 0, sizeof aa);
     if (p.BH > 0) {
-        if (p.splits > 0 && nb > 0) build_any(p, ba, nullptr);
-        if (!p.fuse) scan_any<SCAN_FUSED>(p, sa, nullptr);
+        if ((long)nb * n > 0) build_any(p, ba, nullptr);
+        scan_any<SCAN_FORWARD>(p, sa, nullptr);
         if ((long)nb * n > 0) apply_any(p, aa, nullptr);
     }
     t_desc = nullptr;
@@ -2022,14 +2257,14 @@ svla_status svla_state_build(svla_dtype dt, int B, int H, int nb, int n, int d, 
         ScanArgs sa;
         memset(&sa, 0, sizeof sa);
         sa.nb = nb; sa.splits = 0; sa.S_pre = S_local; sa.z_pre = z_local;
-        // an export scan over zero splits writes a zero state for every block
+        // an export scan over zero partials writes a zero state for every block
         scan_any<SCAN_EXPORT>(p, sa, s);
         return check_launch(fn);
     }
     BuildArgs ba;
     memset(&ba, 0, sizeof ba);
     ba.K = K; ba.V = V; ba.S_part = S_local; ba.z_part = z_local;
-    ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = 1; ba.chunk = p.chunk; ba.rope = p.rope;
+    ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = p.splits; ba.chunk = p.chunk; ba.rope = p.rope;
     ba.BH = p.BH;
     build_any(p, ba, s);
     return check_launch(fn);
