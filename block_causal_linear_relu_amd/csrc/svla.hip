@@ -75,6 +75,12 @@
 #ifndef SVLA_APPLY_TILE128
 #define SVLA_APPLY_TILE128 128     // ... fp32, d = 128
 #endif
+#ifndef SVLA_APPLY32_PF
+#define SVLA_APPLY32_PF 4          // ... d = 32: 16-token groups of Q loads in flight per wave
+#endif
+#ifndef SVLA_APPLY32_PF_ROPE
+#define SVLA_APPLY32_PF_ROPE 4     // ... and with RoPE
+#endif
 #ifndef SVLA_APPLY_TILE_LDS
 #define SVLA_APPLY_TILE_LDS 256    // bf16 apply with the state in LDS (d >= 64): tokens per workgroup
 #endif
@@ -110,6 +116,7 @@ typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 namespace {
 
 constexpr int kThreads = 256;                 // build and apply: 4 waves of 64
+constexpr int kFoldMaxParts = 6;              // partials a scan folded into the apply sums at most
 constexpr int kScanLongChain = 16;            // scan: blocks from which the chain is cut four ways
 constexpr uint32_t kOOB = 0x80000000u;        // an offset past every resource
 constexpr int kMaxRopeEntries = 4096;         // (cos, sin) pairs per workgroup
@@ -363,12 +370,30 @@ struct ScanArgs {
 
 struct BuildArgs {
     const void *K, *V;
-    float *S_part, *z_part;        // [BH*nb][splits][d*d], [BH*nb][splits][d]
+    float *S_part, *z_part;        // [BH*nb][slots][d*d], [BH*nb][slots][d]
     int N, n, nb;
     int splits, chunk;             // workgroups per block, tokens per workgroup
+    int slots;                     // partials per block: splits (+ 1 for the carried state)
     long BH;
     RopeK rope;
+    // one block whose scan is folded into the apply: split 0 also stores
+    // g * S_in, g * z_in as partial number `splits` (g: [BH] or null)
+    const float *S_in, *z_in, *g;
 };
+
+// Partial number `splits` of a one-block (b,h): the carried state, scaled
+// by its gate, so the apply never reads S_in (which the final state may
+// overwrite in place).
+__device__ __forceinline__ void carry_in(const BuildArgs &a, long bh, int D)
+{
+    const float gb = a.g ? a.g[bh] : 1.f;
+    float *dS = a.S_part + (bh * a.slots + a.splits) * D * D;
+    float *dz = a.z_part + (bh * a.slots + a.splits) * D;
+    for (int e = threadIdx.x * 4; e < D * D; e += kThreads * 4)
+        *(f32x4_t *)(dS + e) = gb * *(const f32x4_t *)(a.S_in + bh * D * D + e);
+    for (int e = threadIdx.x * 4; e < D; e += kThreads * 4)
+        *(f32x4_t *)(dz + e) = gb * *(const f32x4_t *)(a.z_in + bh * D + e);
+}
 
 struct ApplyArgs {
     const void *Q;
@@ -379,6 +404,12 @@ struct ApplyArgs {
     long groups;                   // logical workgroups: B*H*nb*tiles
     float eps;
     RopeK rope;
+    // one block with the scan folded in (svla_apply_bf16<.., true>): the
+    // state is the sum of the build's partials (the last one the carried,
+    // decayed state when there is one)
+    const float *S_part, *z_part;  // [BH][splits][d*d], [BH][splits][d]
+    int splits;
+    float *S_fin, *z_fin;          // final state or null (written by tile 0)
 };
 
 // SCAN_FORWARD: partials -> packed operands, prefix z and the final state;
@@ -456,7 +487,22 @@ __device__ __forceinline__ void scan_blocks(const ScanArgs &a, long bh, float *a
     const int per = (a.nb + NSEG - 1) / NSEG;
     const int c0 = min(wave * per, a.nb), c1 = min(c0 + per, a.nb);
     const int lo = c0 * a.splits, hi = c1 * a.splits;
+    const int hi0 = min(hi, lo + LA);      // the first chunk, loaded once for both passes
     const float *g = a.g ? a.g + bh * a.nb : nullptr;
+
+    float first[LA][W];
+    if (lo < hi) {
+#pragma unroll
+        for (int j = 0; j < LA; ++j) fetch(min(lo + j, hi - 1), first[j]);
+        wait_vmcnt<0>();
+    }
+    // walk this wave's partials: the first chunk from registers, the rest loaded
+    auto walk = [&](auto consume) {
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            if (lo + j < hi0) consume(first[j]);
+        scan_walk<LA, W>(hi0, hi, fetch, consume);
+    };
 
     if constexpr (MODE != SCAN_PACK && NSEG > 1) {
         // 1. this wave's (G, P) from a zero state
@@ -464,7 +510,7 @@ __device__ __forceinline__ void scan_blocks(const ScanArgs &a, long bh, float *a
 #pragma unroll
         for (int r = 0; r < W; ++r) P[r] = 0.f;
         int c = c0, sp = 0;
-        scan_walk<LA, W>(lo, hi, fetch, [&](const float *x) {
+        walk([&](const float *x) {
             if (sp == 0 && g) {
                 const float gc = g[c];
                 G *= gc;
@@ -500,7 +546,7 @@ __device__ __forceinline__ void scan_blocks(const ScanArgs &a, long bh, float *a
             emit(c, acc);
         }
     } else {
-        scan_walk<LA, W>(lo, hi, fetch, [&](const float *x) {
+        walk([&](const float *x) {
             if (sp == 0) {
                 const float gc = MODE == SCAN_PACK ? 0.f : (g ? g[c] : 1.f);
 #pragma unroll
@@ -813,7 +859,7 @@ svla_state_build_dma(const BuildArgs a)
     __syncthreads();
 
     // ---- epilogue: S_part (row-major [k][v]) and z_part
-    const long unit = (bh * a.nb + c) * a.splits + s;
+    const long unit = (bh * a.nb + c) * a.slots + s;
     const auto rS = make_rsrc(a.S_part + unit * DG * DG, DG * DG * 4);
     const auto rz = make_rsrc(a.z_part + unit * DG, DG * 4);
     // z: column 0 of each zt tile, held by lanes 0 (rows 8q + r, r < 4) and 32 (rows 8q + 4 + r)
@@ -868,6 +914,9 @@ svla_state_build_dma(const BuildArgs a)
                     store4(rS, (uint32_t)(rr * DG + cc) * 4u, acc[tm][tn][r]);
                 }
         if (tid < D && qn == 0) store4(rz, (uint32_t)(kcol + tid) * 4u, zred[tid]);
+    }
+    if constexpr (!QUAD) {
+        if (a.S_in && s == 0) carry_in(a, bh, D);
     }
 }
 
@@ -1102,7 +1151,7 @@ svla_state_build_rope(const BuildArgs a)
         zred[tid] = v;
     }
     __syncthreads();
-    const long unit = (bh * a.nb + c) * a.splits + s;
+    const long unit = (bh * a.nb + c) * a.slots + s;
     const auto rS = make_rsrc(a.S_part + unit * DG * DG, DG * DG * 4);
     const auto rz = make_rsrc(a.z_part + unit * DG, DG * 4);
 #pragma unroll
@@ -1111,6 +1160,9 @@ svla_state_build_rope(const BuildArgs a)
         store16(rS, (uint32_t)((kcol + rr) * DG + vcol + c0) * 4u, *(const u32x4_t *)(red + e0));
     }
     if (tid < D && qn == 0) store4(rz, (uint32_t)(kcol + tid) * 4u, zred[tid]);
+    if constexpr (!QUAD) {
+        if (a.S_in && s == 0) carry_in(a, bh, D);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1218,7 +1270,7 @@ svla_state_build_f32(const BuildArgs a)
     }
     __syncthreads();
 
-    const long unit = (bh * a.nb + c) * a.splits + s;
+    const long unit = (bh * a.nb + c) * a.slots + s;
     const auto rS = make_rsrc(a.S_part + unit * D * D, D * D * 4);
     const auto rz = make_rsrc(a.z_part + unit * D, D * 4);
     float *red = (float *)stage;
@@ -1268,24 +1320,31 @@ svla_state_build_f32(const BuildArgs a)
 // svla_apply, bf16 inputs, d = 32.  Workgroup = (bh, block c, token tile);
 // the tiles of one block run on one XCD.
 // O^T = S^T phi~(Q)^T on v_mfma_f32_16x16x32_bf16: the state is the A
-// operand (kept in registers for the whole tile, loaded once from the
-// packed layout), phi~(q) the B operand straight from a 16-byte load per
-// lane (token = lane % 16, 8 features of chunk 4 ks + lane / 16).  The
-// denominator phi(q) . z is a per-lane partial dot product reduced over the
-// 4 lanes that share a token.  Each wave takes every 4th 16-token group,
-// with all output features.
+// operand (kept in registers for the whole tile), phi~(q) the B operand
+// straight from a 16-byte load per lane (token = lane % 16, 8 features of
+// chunk lane / 16).  The denominator phi(q) . z is a per-lane partial dot
+// product reduced over the 4 lanes that share a token.  Each wave takes
+// every 4th 16-token group, with all output features, and keeps PF groups
+// of Q loads in flight.
+// FOLD (one block, no scan kernel): the state is the sum of the build's
+// partials, formed in LDS by every workgroup of the (b,h) while its first
+// Q loads are in flight; tile 0 also writes it out as the final state.
+// Otherwise the state comes from the scan's packed operand and prefix z.
 // ---------------------------------------------------------------------------
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool FOLD>
 __global__ void __launch_bounds__(kThreads)
 svla_apply_bf16(const ApplyArgs a)
 {
     constexpr int MT = D / 16;
     constexpr int KS = D / 32;
-    constexpr int MW = MT;
+    constexpr int PF = ROPE ? SVLA_APPLY32_PF_ROPE : SVLA_APPLY32_PF;
+    constexpr int MAXP = kFoldMaxParts;
+    static_assert(D == 32, "laid out for d = 32");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const long lid = xcd_logical(a.groups);
     if (lid >= a.groups) return;
     const int tile = (int)(lid % a.tiles);
@@ -1298,29 +1357,110 @@ svla_apply_bf16(const ApplyArgs a)
     const uint32_t slice = (uint32_t)a.N * D * 2;
     const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
     const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
-    const auto rS = make_rsrc((const char *)a.S_op + unit * D * D * 2, D * D * 2);
-    const auto rz = make_rsrc(a.z_pre + unit * D, D * 4);
-
     const int kg = lane >> 4, tl = lane & 15;
-    constexpr int m0 = 0;
 
-    bf16x8_t sf[MW][KS];
+    // 1. the state's loads: this thread's four floats of S (and of z for
+    // threads < d / 4) from every partial, or the packed operand and z
+    f32x4_t part[FOLD ? MAXP : 1][2];
+    u32x4_t sop[MT][KS], zr[KS][2];
+    const int e0 = tid * 4;
+    if constexpr (FOLD) {
+        const float *pS = a.S_part + bh * a.splits * D * D + e0;
+        const float *pz = a.z_part + bh * a.splits * D + min(e0, D - 4);
 #pragma unroll
-    for (int mi = 0; mi < MW; ++mi)
+        for (int sp = 0; sp < MAXP; ++sp) {
+            const int q = min(sp, a.splits - 1);     // in bounds; used only below a.splits
+            part[sp][0] = *(const f32x4_t *)(pS + q * D * D);
+            part[sp][1] = *(const f32x4_t *)(pz + q * D);
+        }
+    } else {
+        const auto rS = make_rsrc((const char *)a.S_op + unit * D * D * 2, D * D * 2);
+        const auto rz = make_rsrc(a.z_pre + unit * D, D * 4);
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sop[mi][ks] = load16(rS, (uint32_t)(((mi * KS + ks) * 64 + lane) * 16));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            zr[ks][0] = load16(rz, (uint32_t)(8 * (4 * ks + kg)) * 4u);
+            zr[ks][1] = load16(rz, (uint32_t)(8 * (4 * ks + kg) + 4) * 4u);
+        }
+    }
+
+    // 2. without RoPE, the first PF groups of Q (slot p holds this wave's
+    // group i, i % PF == p; the scheduling barriers keep the loads in slot
+    // order)
+    const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
+    const int nw = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
+    auto qoff = [&](int i, int ks) -> uint32_t {
+        const int tok = t_lo + 16 * (wave + 4 * i) + tl;
+        return tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB;
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t qreg[PF][KS];
+    if constexpr (!ROPE) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(p, ks));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // 3. the state in registers: A fragments sf (lane (rho + 16 kg), value i
+    // = S[32 ks + 8 kg + i][f(mi, rho)], f(m, rho) = (d/4)(rho/4) + 4m + rho%4)
+    // and z for this lane's features
+    bf16x8_t sf[MT][KS];
+    float zf[KS][8];
+    unsigned char *lds_free = lds;
+    if constexpr (ROPE) lds_free += a.rope.tab_bytes;
+    if constexpr (FOLD) {
+        // summed in partial order, so every workgroup of the (b,h) gets the same bits
+        float *st = (float *)lds_free;      // S[k][v] at [0, d*d), z at [d*d, d*d + d)
+        f32x4_t vs = part[0][0], vz = part[0][1];
+#pragma unroll
+        for (int sp = 1; sp < MAXP; ++sp) {
+            if (sp < a.splits) {
+                vs += part[sp][0];
+                vz += part[sp][1];
+            }
+        }
+        *(f32x4_t *)(st + e0) = vs;
+        if (e0 < D) *(f32x4_t *)(st + D * D + e0) = vz;
+        if (tile == 0 && a.S_fin) {
+            *(f32x4_t *)(a.S_fin + bh * D * D + e0) = vs;
+            if (e0 < D) *(f32x4_t *)(a.z_fin + bh * D + e0) = vz;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int f = (D / 4) * (tl / 4) + 4 * mi + tl % 4;
+                u32x4_t w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = pack_bf16(st[(32 * ks + 8 * kg + 2 * e) * D + f],
+                                     st[(32 * ks + 8 * kg + 2 * e + 1) * D + f]);
+                sf[mi][ks] = __builtin_bit_cast(bf16x8_t, w);
+            }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            sf[mi][ks] = __builtin_bit_cast(bf16x8_t,
-                load16(rS, (uint32_t)((((m0 + mi) * KS + ks) * 64 + lane) * 16)));
-    float zf[KS][8];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t z0 = load16(rz, (uint32_t)(8 * (4 * ks + kg)) * 4u);
-        u32x4_t z1 = load16(rz, (uint32_t)(8 * (4 * ks + kg) + 4) * 4u);
+            for (int e = 0; e < 8; ++e) zf[ks][e] = st[D * D + 8 * (4 * ks + kg) + e];
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            zf[ks][e] = as_f32(z0[e]);
-            zf[ks][4 + e] = as_f32(z1[e]);
-        }
+        for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sf[mi][ks] = __builtin_bit_cast(bf16x8_t, sop[mi][ks]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                zf[ks][e] = as_f32(zr[ks][0][e]);
+                zf[ks][4 + e] = as_f32(zr[ks][1][e]);
+            }
     }
 
     float2 *tab = (float2 *)lds;
@@ -1328,85 +1468,102 @@ svla_apply_bf16(const ApplyArgs a)
     RopePairs<4> pp[KS];
     if constexpr (ROPE) {
         frame_lo = t_lo < t_hi ? fdiv((uint32_t)t_lo, a.rope.div_hw) : 0;
-        uint32_t frame_hi = t_lo < t_hi ? fdiv((uint32_t)(t_hi - 1), a.rope.div_hw) : 0;
-        int nf = (int)(frame_hi - frame_lo) + 1;
+        const uint32_t frame_hi = t_lo < t_hi ? fdiv((uint32_t)(t_hi - 1), a.rope.div_hw) : 0;
+        const int nf = (int)(frame_hi - frame_lo) + 1;
         rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) pp[ks] = rope_pairs<4>(a.rope, 8 * (4 * ks + kg), nf);
-        __syncthreads();
+        lds_barrier();
     }
 
-    // groups of this wave: g_first, g_first + g_step, ...; the loads of GB
-    // groups are issued together before any of them is used.
-    constexpr int GB = 4;
-    const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
-    const int g_first = wave, g_step = 4;
-    for (int gb = g_first; gb < ngroups; gb += GB * g_step) {
-    u32x4_t qb[GB][KS];
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-        const int tok = t_lo + 16 * (gb + j * g_step) + tl;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qb[j][ks] = load16p<SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB);
-    }
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-        const int gi = gb + j * g_step;
-        if (gi >= ngroups) break;
-        const int tok = t_lo + 16 * gi + tl;
+    // 4. the groups: wave group i covers tokens t_lo + 16 (wave + 4 i) ...
+    auto group = [&](int i, const u32x4_t *qr) {
+        const int tok = t_lo + 16 * (wave + 4 * i) + tl;
         const bool valid = tok < t_hi;
-        const u32x4_t *qr = qb[j];
         float den = 0.f;
         bf16x8_t qf[KS];
         RopePos rp{0, 0, 0};
         if constexpr (ROPE) rp = rope_pos((uint32_t)tok, frame_lo, a.rope);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4_t p;
+            u32x4_t pq;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = relu_bf16x2(qr[ks][e]);
+            for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[ks][e]);
             float pf[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                pf[2 * e] = bf16lo(p[e]);
-                pf[2 * e + 1] = bf16hi(p[e]);
+                pf[2 * e] = bf16lo(pq[e]);
+                pf[2 * e + 1] = bf16hi(pq[e]);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) den = fmaf(pf[e], zf[ks][e], den);
             if constexpr (ROPE) {
                 rope_rotate<4>(pf, rp, pp[ks], tab);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
+                for (int e = 0; e < 4; ++e) pq[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
             }
-            qf[ks] = __builtin_bit_cast(bf16x8_t, p);
+            qf[ks] = __builtin_bit_cast(bf16x8_t, pq);
         }
         den += __shfl_xor(den, 16);
         den += __shfl_xor(den, 32);
         den += a.eps;
         const float inv = den != 0.f ? 1.0f / den : 0.f;
 
-        f32x4_t acc[MW];
+        f32x4_t acc[MT];
 #pragma unroll
-        for (int mi = 0; mi < MW; ++mi) {
+        for (int mi = 0; mi < MT; ++mi) {
             acc[mi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mi][ks], qf[ks], acc[mi], 0, 0, 0);
         }
-        // lane holds O[tok][4 MT kg + 4 (m0 + mi) + r], consecutive in (mi, r)
+        // lane holds O[tok][4 MT kg + 4 mi + r], consecutive in (mi, r)
 #pragma unroll
-        for (int h = 0; h < MW / 2; ++h) {
+        for (int h = 0; h < MT / 2; ++h) {
             u32x4_t o;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 o[2 * e] = pack_bf16(acc[2 * h + e][0] * inv, acc[2 * h + e][1] * inv);
                 o[2 * e + 1] = pack_bf16(acc[2 * h + e][2] * inv, acc[2 * h + e][3] * inv);
             }
-            const int v0 = 4 * MT * kg + 4 * (m0 + 2 * h);
+            const int v0 = 4 * MT * kg + 8 * h;
             store16p<SVLA_O_AUX>(rO, valid ? (uint32_t)(tok * D + v0) * 2u : kOOB, o);
         }
-    }
+    };
+    if constexpr (ROPE) {
+        // the rotation makes this loop bound by the vector ALU: batches of PF
+        // groups, loaded together, keep the register count (and occupancy) up
+        for (int i0 = 0; i0 < nw; i0 += PF) {
+            u32x4_t qb[PF][KS];
+#pragma unroll
+            for (int p = 0; p < PF; ++p)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) qb[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(i0 + p, ks));
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                if (i0 + p >= nw) break;
+                group(i0 + p, qb[p]);
+            }
+        }
+    } else {
+        // a ring of PF groups in flight; the count is rounded up to a multiple
+        // of PF (the extra groups load nothing and store nothing) so the loop
+        // stays regular for the wait counts
+        const int nwr = (nw + PF - 1) / PF * PF;
+        for (int i0 = 0; i0 < nwr; i0 += PF) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                const int i = i0 + p;
+                u32x4_t qr[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) qr[ks] = qreg[p][ks];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(i + PF, ks));
+                __builtin_amdgcn_sched_barrier(0);
+                group(i, qr);
+            }
+        }
     }
 }
 
@@ -1761,6 +1918,7 @@ struct Plan {
     long BH;
     int esize;                 // bytes per Q/K/V/O element
     bool dma;                  // build straight to LDS (bf16 without RoPE)
+    bool fold;                 // one block, bf16, d = 32: the apply sums the partials (no scan)
     int splits, chunk;         // build: workgroups per block, tokens per workgroup
     int tile, tiles;           // apply
     size_t lds_build, lds_apply;
@@ -1866,6 +2024,8 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
         p->splits = p->dma ? splits_dma : splits_other;
         p->chunk = p->dma ? chunk_dma : chunk_other;
     }
+    p->fold = (op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP) &&
+              p->esize == 2 && d == 32 && nb == 1 && n > 0 && p->splits + 1 <= kFoldMaxParts;
     p->tile = (p->esize == 2 && d >= 64) ? SVLA_APPLY_TILE_LDS
               : d == 128 ? SVLA_APPLY_TILE128 : (p->rope.on ? SVLA_APPLY_TILE_ROPE : SVLA_APPLY_TILE32);
     p->tiles = n > 0 ? (n + p->tile - 1) / p->tile : 0;
@@ -1900,13 +2060,16 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
         p->lds_build += (size_t)p->rope.tab_bytes;
         p->lds_apply = (size_t)p->rope.tab_bytes;
     }
+    if (p->fold) p->lds_apply += (size_t)(d * d + d) * 4;   // the summed state
 
     // workspace: partial states (as many per block as either build writes,
     // so the size does not depend on RoPE), packed prefix operands, prefix z
     size_t off = 0;
     const bool fused = op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP;
     if (fused) {
-        const size_t slots = (size_t)(splits_dma > splits_other ? splits_dma : splits_other);
+        // (+ 1: a one-block call whose scan is folded into the apply keeps
+        // the carried state there)
+        const size_t slots = (size_t)(splits_dma > splits_other ? splits_dma : splits_other) + 1;
         p->off_spart = off; off = align256(off + (size_t)units * slots * d * d * 4);
         p->off_zpart = off; off = align256(off + (size_t)units * slots * d * 4);
     }
@@ -1930,6 +2093,7 @@ void launch_build(const Plan &p, const BuildArgs &args, hipStream_t s)
     BuildArgs a = args;
     a.splits = p.splits;
     a.chunk = p.chunk;
+    a.slots = p.splits + (a.S_in ? 1 : 0);
     const unsigned grid = (unsigned)(p.BH * p.nb * p.splits);
     const unsigned qgrid = (unsigned)((grid + 7) / 8 * 8 * 4);   // d = 128: four quadrants
     char nm[96];
@@ -1992,8 +2156,15 @@ void launch_apply(const Plan &p, const ApplyArgs &args, hipStream_t s)
             if (p.rope.on) launch(svla_apply_lds<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
             else launch(svla_apply_lds<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
         } else {
-            if (p.rope.on) launch(svla_apply_bf16<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-            else launch(svla_apply_bf16<D, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            if (p.fold) {
+                snprintf(nm, sizeof nm, "void svla_apply_bf16<%d, %s, true>", D, p.rope.on ? "true" : "false");
+                if (p.rope.on) launch(svla_apply_bf16<D, true, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else launch(svla_apply_bf16<D, false, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            } else {
+                snprintf(nm, sizeof nm, "void svla_apply_bf16<%d, %s, false>", D, p.rope.on ? "true" : "false");
+                if (p.rope.on) launch(svla_apply_bf16<D, true, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else launch(svla_apply_bf16<D, false, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            }
         }
     } else {
         if (p.rope.on) launch(svla_apply_f32<D, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
@@ -2079,16 +2250,24 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
         ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = p.splits; ba.chunk = p.chunk;
         ba.BH = p.BH;
         ba.rope = p.rope;
+        if (p.fold && S0) { ba.S_in = S0; ba.z_in = z0; ba.g = g; }
         build_any(p, ba, s);
         if ((st = check_launch(fn))) return st;
     }
-    scan_any<SCAN_FORWARD>(p, sa, s);
-    if ((st = check_launch(fn))) return st;
+    if (!p.fold) {
+        scan_any<SCAN_FORWARD>(p, sa, s);
+        if ((st = check_launch(fn))) return st;
+    }
     if (tokens) {
         ApplyArgs aa;
+        memset(&aa, 0, sizeof aa);
         aa.Q = Q; aa.O = O; aa.S_op = w + p.off_sop; aa.z_pre = (const float *)(w + p.off_zpre);
         aa.N = nb * n; aa.n = n; aa.nb = nb; aa.tile = p.tile; aa.tiles = p.tiles; aa.eps = eps;
         aa.rope = p.rope;
+        if (p.fold) {
+            aa.S_part = sa.S_part; aa.z_part = sa.z_part; aa.splits = p.splits + (S0 ? 1 : 0);
+            aa.S_fin = S_fin; aa.z_fin = z_fin;
+        }
         apply_any(p, aa, s);
         if ((st = check_launch(fn))) return st;
     }
@@ -2151,7 +2330,7 @@ svla_status svla_describe(svla_op op, svla_dtype dt, int B, int H, int nb, int n
     memset(&aa, 0, sizeof aa);
     if (p.BH > 0) {
         if ((long)nb * n > 0) build_any(p, ba, nullptr);
-        scan_any<SCAN_FORWARD>(p, sa, nullptr);
+        if (!p.fold) scan_any<SCAN_FORWARD>(p, sa, nullptr);
         if ((long)nb * n > 0) apply_any(p, aa, nullptr);
     }
     t_desc = nullptr;
@@ -2321,6 +2500,7 @@ svla_status svla_apply(svla_dtype dt, int B, int H, int nb, int n, int d, const 
     scan_any<SCAN_PACK>(p, sa, s);
     if ((st = check_launch(fn))) return st;
     ApplyArgs aa;
+    memset(&aa, 0, sizeof aa);
     aa.Q = Q; aa.O = O; aa.S_op = ws; aa.z_pre = z_prefix;
     aa.N = nb * n; aa.n = n; aa.nb = nb; aa.tile = p.tile; aa.tiles = p.tiles; aa.eps = eps;
     aa.rope = p.rope;
