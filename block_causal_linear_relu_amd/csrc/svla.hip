@@ -207,6 +207,13 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Output feature of row 4 (rho / 4) + rho % 4 of m-tile m in the apply's
+// O^T MFMA (the column of S that packed-operand row (m, rho) holds).
+__host__ __device__ constexpr int op_col(int m, int rho)
+{
+    return 32 * (m / 2) + 8 * (rho / 4) + 4 * (m % 2) + rho % 4;
+}
+
 // Unsigned division by a divisor fixed per launch (multiply-high method of
 // Granlund and Montgomery): q = (t + ((x - t) >> s1)) >> s2, t = mulhi(x, mul).
 struct FastDiv {
@@ -426,8 +433,10 @@ enum ScanMode { SCAN_FORWARD = 0, SCAN_EXPORT = 1, SCAN_PACK = 2 };
 //       holds S[32 ks + 8 kg + i][f(m, rho)]
 // fp32: fragment (m, kq) = 64 lanes x 4 values; lane (rho + 16 kg), value i
 //       holds S[16 kq + 4 kg + i][f(m, rho)]
-// with f(m, rho) = (d/4) (rho / 4) + 4 m + rho % 4: the output rows of the
-// MFMA land so that each lane ends up with consecutive O features.
+// with f(m, rho) = op_col(m, rho) = 32 (m / 2) + 8 (rho / 4) + 4 (m % 2) + rho % 4:
+// the output rows of the MFMA land so that the lanes of one token hold
+// O features 32 h + 8 kg + [0, 8) in m-tiles 2h and 2h + 1, and each store
+// instruction of the apply writes whole 64-byte row segments.
 //
 // Element tiles: lane -> column v0 + lane % CW and RL consecutive rows
 // k0 + RL (lane / CW) of an 8-row x CW-column tile, so each lane's values
@@ -572,7 +581,7 @@ __device__ __forceinline__ void scan_s_tile(const ScanArgs &a, long bh, int tile
     const int v = (tile % (D / CW)) * CW + lane % CW;
     const int k = (tile / (D / CW)) * 8 + RL * (lane / CW);
     // operand position of (k .. k + RL - 1, v)
-    const int m = (v % (D / 4)) / 4, rho = 4 * (v / (D / 4)) + v % 4;
+    const int m = 2 * (v / 32) + (v % 8) / 4, rho = 4 * ((v % 32) / 8) + v % 4;   // op_col(m, rho) == v
     long opos;
     if constexpr (OPBF16)
         opos = ((long)((m * (D / 32) + k / 32) * 64 + rho + 16 * ((k % 32) / 8)) * 8 + k % 8);
@@ -1409,7 +1418,7 @@ svla_apply_bf16(const ApplyArgs a)
     }
 
     // 3. the state in registers: A fragments sf (lane (rho + 16 kg), value i
-    // = S[32 ks + 8 kg + i][f(mi, rho)], f(m, rho) = (d/4)(rho/4) + 4m + rho%4)
+    // = S[32 ks + 8 kg + i][op_col(mi, rho)])
     // and z for this lane's features
     bf16x8_t sf[MT][KS];
     float zf[KS][8];
@@ -1437,7 +1446,7 @@ svla_apply_bf16(const ApplyArgs a)
         for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int f = (D / 4) * (tl / 4) + 4 * mi + tl % 4;
+                const int f = op_col(mi, tl);
                 u32x4_t w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -1517,7 +1526,7 @@ svla_apply_bf16(const ApplyArgs a)
             for (int ks = 0; ks < KS; ++ks)
                 acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mi][ks], qf[ks], acc[mi], 0, 0, 0);
         }
-        // lane holds O[tok][4 MT kg + 4 mi + r], consecutive in (mi, r)
+        // m-tiles 2h, 2h + 1 hold O[tok][op_col(2h, 4 kg) + 0 .. 7]
 #pragma unroll
         for (int h = 0; h < MT / 2; ++h) {
             u32x4_t o;
@@ -1526,7 +1535,7 @@ svla_apply_bf16(const ApplyArgs a)
                 o[2 * e] = pack_bf16(acc[2 * h + e][0] * inv, acc[2 * h + e][1] * inv);
                 o[2 * e + 1] = pack_bf16(acc[2 * h + e][2] * inv, acc[2 * h + e][3] * inv);
             }
-            const int v0 = 4 * MT * kg + 8 * h;
+            const int v0 = op_col(2 * h, 4 * kg);
             store16p<SVLA_O_AUX>(rO, valid ? (uint32_t)(tok * D + v0) * 2u : kOOB, o);
         }
     };
@@ -1715,19 +1724,24 @@ svla_apply_lds(const ApplyArgs a)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 dz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zt[ks], qu[ks], dz, 0, 0, 0);
+            // k-step outer: the MT fragment reads of a step go out together and
+            // its MT MFMAs are independent
             f32x4_t acc[MT];
 #pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                acc[mi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            for (int mi = 0; mi < MT; ++mi) acc[mi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8_t sf = *(const bf16x8_t *)(sS + (mi * KS + ks) * 1024 + lane * 16);
-                    acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf, qf[ks], acc[mi], 0, 0, 0);
-                }
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8_t sf[MT];
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi)
+                    sf[mi] = *(const bf16x8_t *)(sS + (mi * KS + ks) * 1024 + lane * 16);
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi)
+                    acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mi], qf[ks], acc[mi], 0, 0, 0);
             }
             const float den = dz[0] + dz[1] + a.eps;
             const float inv = den != 0.f ? 1.0f / den : 0.f;
-            // lane holds O[tok][(D/4) kg + 4 mi + r]: D/4 consecutive features
+            // m-tiles 2h, 2h + 1 hold O[tok][op_col(2h, 4 kg) + 0 .. 7]
             const bool valid = tok < t_hi;
 #pragma unroll
             for (int h = 0; h < MT / 2; ++h) {
@@ -1737,7 +1751,7 @@ svla_apply_lds(const ApplyArgs a)
                     o[2 * e] = pack_bf16(acc[2 * h + e][0] * inv, acc[2 * h + e][1] * inv);
                     o[2 * e + 1] = pack_bf16(acc[2 * h + e][2] * inv, acc[2 * h + e][3] * inv);
                 }
-                const int v0 = (D / 4) * kg + 8 * h;
+                const int v0 = op_col(2 * h, 4 * kg);
                 store16p<SVLA_O_AUX>(rO, valid ? (uint32_t)(tok * D + v0) * 2u : kOOB, o);
             }
         }
@@ -1841,7 +1855,7 @@ svla_apply_f32(const ApplyArgs a)
             u32x4_t o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = as_u32(acc[mi][r] * inv);
-            const int v0 = 4 * MT * kg + 4 * (m0 + mi);
+            const int v0 = op_col(m0 + mi, 4 * kg);
             store16(rO, valid ? (uint32_t)(tok * D + v0) * 4u : kOOB, o);
         }
     }
