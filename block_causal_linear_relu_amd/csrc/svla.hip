@@ -240,7 +240,9 @@ struct RopeK {
     int tab_bytes;           // LDS reserved for the table in front of the stage buffers
 };
 
-// Table layout: [frames nf x dt/2][rows gh x dh/2][cols gw x dw/2] of float2.
+// Table layout (float2 cos, sin), position fastest: [dt/2 pairs][nf frames],
+// then [dh/2 pairs][gh rows], then [dw/2 pairs][gw columns], then one
+// identity entry (cos 1, sin 0) for the unrotated dims.
 __device__ __forceinline__ int rope_entries(const RopeK &r, int nf)
 {
     return nf * (r.dt / 2) + r.gh * (r.dh / 2) + r.gw * (r.dw / 2);
@@ -269,11 +271,11 @@ __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
         int pos, m, a;
         if (e < nT) {
-            pos = f0 + e / pt; m = e % pt; a = 0;
+            m = e / nf; pos = f0 + (e - m * nf); a = 0;
         } else if (e < nT + nH) {
-            int x = e - nT; pos = x / ph; m = x % ph; a = 1;
+            const int x = e - nT; m = x / r.gh; pos = x - m * r.gh; a = 1;
         } else {
-            int x = e - nT - nH; pos = x / pw; m = x % pw; a = 2;
+            const int x = e - nT - nH; m = x / r.gw; pos = x - m * r.gw; a = 2;
         }
         double turns = (double)pos * turns_per_pos[a * kMaxRopePairs + m];
         turns -= floor(turns);
@@ -286,10 +288,10 @@ __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
 
 // Per-thread description of the 4 (bf16 chunk) or 2 (fp32 chunk) pairs of
 // its fixed feature chunk.  A pair's table index for a token at (frame
-// offset fr, row, col) is base + fr * mt + row * mh + col * mw, with exactly
-// one multiplier non-zero for a rotated pair; a pair outside the three
-// slices points at the identity entry (cos 1, sin 0) that ends the table, so
-// the rotation has no branches.
+// offset fr, row, col) is base + (fr & mt) + (row & mh) + (col & mw): the
+// mask of the pair's axis is all ones and the other two are zero (no
+// multiply on the way); a pair outside the three slices has three zero
+// masks and points at the identity entry, so the rotation has no branches.
 template <int PAIRS>
 struct RopePairs {
     int base[PAIRS], mt[PAIRS], mh[PAIRS], mw[PAIRS];
@@ -299,18 +301,18 @@ template <int PAIRS>
 __device__ __forceinline__ RopePairs<PAIRS> rope_pairs(const RopeK &r, int first_feature, int nf)
 {
     RopePairs<PAIRS> p;
-    const int pt = r.dt / 2, ph = r.dh / 2, pw = r.dw / 2;
+    const int pt = r.dt / 2, ph = r.dh / 2;
     const int offH = nf * pt, offW = offH + r.gh * ph;
 #pragma unroll
     for (int j = 0; j < PAIRS; ++j) {
-        int f = first_feature + 2 * j;
+        const int f = first_feature + 2 * j;
         p.mt[j] = p.mh[j] = p.mw[j] = 0;
         if (f < r.dt) {
-            p.base[j] = f / 2; p.mt[j] = pt;
+            p.base[j] = (f / 2) * nf; p.mt[j] = -1;
         } else if (f < r.dt + r.dh) {
-            p.base[j] = offH + (f - r.dt) / 2; p.mh[j] = ph;
+            p.base[j] = offH + ((f - r.dt) / 2) * r.gh; p.mh[j] = -1;
         } else if (f < r.dt + r.dh + r.dw) {
-            p.base[j] = offW + (f - r.dt - r.dh) / 2; p.mw[j] = pw;
+            p.base[j] = offW + ((f - r.dt - r.dh) / 2) * r.gw; p.mw[j] = -1;
         } else {
             p.base[j] = rope_entries(r, nf);       // the identity entry
         }
@@ -339,7 +341,7 @@ __device__ __forceinline__ void rope_rotate(float *x, const RopePos &pos,
 {
 #pragma unroll
     for (int j = 0; j < PAIRS; ++j) {
-        const int idx = pp.base[j] + pos.fr * pp.mt[j] + pos.row * pp.mh[j] + pos.col * pp.mw[j];
+        const int idx = pp.base[j] + (pos.fr & pp.mt[j]) + (pos.row & pp.mh[j]) + (pos.col & pp.mw[j]);
         const float2 cs = tab[idx];
         const float x0 = x[2 * j], x1 = x[2 * j + 1];
         x[2 * j] = x0 * cs.x - x1 * cs.y;
