@@ -2,13 +2,14 @@
 """Benchmark of block-causal ReLU linear attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5]
-                    [--c4-mode stream|oneshot] [--rotate R] [--no-cpu-baseline]
+                    [--c4-mode stream|oneshot] [--rotate R] [--settle S] [--no-cpu-baseline]
 
 A step is one pass of the whole path (state build -> scan -> apply) over one
 batch of the workload's synthetic input, with inputs resident in HBM.  R
 copies of the inputs and outputs rotate so that consecutive steps do not hit
-in the 256 MB Infinity Cache.  W untimed steps, then K timed steps between two
-device synchronisations; one JSON line on stdout.
+in the 256 MB Infinity Cache.  About S seconds of untimed steps let the
+clocks settle, then W untimed steps, then K timed steps between two device
+synchronisations; one JSON line on stdout.
 
 Also:
   --copy-calibration           time a plain device copy of known size (run it
@@ -53,6 +54,8 @@ def parse():
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--c4-mode", default="stream", choices=["stream", "oneshot"])
     ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup (clock settling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4,
@@ -197,6 +200,21 @@ class Workload:
 # ---------------------------------------------------------------------------
 # measurements
 # ---------------------------------------------------------------------------
+def settle(w: Workload, seconds: float) -> int:
+    """Run the step, untimed, for about `seconds` of wall time so the GPU
+    leaves its idle clock state before the warmup steps (a fresh process's
+    first few hundred milliseconds of work run measurably slower)."""
+    torch = w.torch
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            w.step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def time_steps(w: Workload, steps: int, warmup: int) -> float:
     torch = w.torch
     for i in range(warmup):
@@ -370,6 +388,7 @@ def main():
     w = Workload(args.config, args.rotate, args.c4_mode)
     if w.stream_mode:
         w.capture()
+    settled = settle(w, args.settle) if args.settle > 0 else 0
     ms = time_steps(w, args.steps, args.warmup)
     plan = w.describe_plan()
     used = {k["slot"] for k in plan["kernels"]}
@@ -389,6 +408,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settled,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",

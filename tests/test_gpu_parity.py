@@ -87,6 +87,11 @@ SMALL = [
     ("bf16_d128_rope", "bf16", 1, 2, 2, 300, 128, Rope(40, 44, 44, 6, 10, 0, 1e4), False, True),
     ("bf16_d32_token_causal", "bf16", 1, 2, 40, 1, 32, None, False, False),
     ("bf16_d32_noncausal", "bf16", 2, 3, 1, 1000, 32, None, False, False),
+    # over a thousand short ragged blocks (one-stage and two-stage blocks)
+    ("bf16_d32_many_blocks", "bf16", 1, 40, 30, 37, 32, None, False, False),
+    ("bf16_d32_many_blocks_rope_gate_state", "bf16", 2, 50, 12, 100, 32, Rope(8, 12, 12, 5, 7, 3, 1e4), True, True),
+    # an angle table of over a thousand entries (wide latent grid)
+    ("bf16_d32_rope_wide_grid", "bf16", 1, 2, 3, 300, 32, Rope(8, 12, 12, 100, 100, 0, 1e4), False, False),
 ]
 
 
