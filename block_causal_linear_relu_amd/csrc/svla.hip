@@ -57,6 +57,9 @@
 #ifndef SVLA_ROPE_U
 #define SVLA_ROPE_U 2              // ... 16-byte loads per lane per tensor per stage
 #endif
+#ifndef SVLA_ROPE_TR
+#define SVLA_ROPE_TR 1             // ... gathers by transposing LDS reads
+#endif
 #ifndef SVLA_ROPE_WGS
 #define SVLA_ROPE_WGS 2048         // ... (and fp32 builds): workgroups wanted per launch
 #endif
@@ -696,6 +699,65 @@ __device__ __forceinline__ int swz16(int t, int chunk)
     return (D >= 64) ? (chunk ^ ((t & 1) << 2)) : chunk;
 }
 
+// Token-contraction operand of v_mfma_f32_32x32x16_bf16 from a row-major
+// [token][D] bf16 tile (16-byte chunks swizzled by swz16): lane l needs 8
+// tokens of feature f0 + l % 32.  ds_read_b64_tr_b16 hands lane 4a + k of
+// each 16-lane group element k of the 8-byte pieces addressed by lanes a,
+// a + 4, a + 8, a + 12 of that group, so two such reads, with lane i of the
+// group addressing token 4 r + i / 4 and features 4 (i % 4) .. + 3 of the
+// group's 16-feature half, give lane l tokens 8 (l / 32) + 0 .. 7 of its
+// feature: k-slot 8 (l / 32) + j is token 8 (l / 32) + j of the 16-token group.
+// trb_offset: the lane's byte offset for read r = 0 (r = 1 adds 4 rows).
+template <int D>
+__device__ __forceinline__ int trb_offset(int lane, int f0)
+{
+    const int i = lane & 15, G = lane >> 4;
+    const int row = 8 * (G >> 1) + (i >> 2);
+    const int c = (f0 >> 3) + 2 * (G & 1) + ((i & 3) >> 1);
+    return row * D * 2 + swz16<D>(row, c) * 16 + 8 * (i & 1);
+}
+
+// One operand by the builtin, for kernels with no loads to LDS in flight.
+template <int D>
+__device__ __forceinline__ bf16x8_t trb_load(const unsigned char *grp, int off)
+{
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4_t *lp;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(grp + off));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(grp + off + 4 * D * 2));
+    const u32x4_t x = {__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                       __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
+    return __builtin_bit_cast(bf16x8_t, x);
+}
+
+// Both operands of one 16-token group: four transposing reads in one asm
+// block that also waits for them (the compiler sees no LDS read here, so it
+// adds no wait for the stage loads in flight, which write other buffers;
+// the ring's own waits and barriers order these reads).
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+template <int D>
+__device__ __forceinline__ void trb_load2(const unsigned char *kgrp, int koff, const unsigned char *vgrp,
+                                          int voff, bf16x8_t &av, bf16x8_t &bv)
+{
+    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+    u32x2_t k0, k1, v0, v1;
+    asm volatile("ds_read_b64_tr_b16 %0, %4\n\t"
+                 "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+                 "ds_read_b64_tr_b16 %2, %5\n\t"
+                 "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(k0), "=&v"(k1), "=&v"(v0), "=&v"(v1)
+                 : "v"(lds_addr(kgrp + koff)), "v"(lds_addr(vgrp + voff)), "i"(4 * D * 2));
+    const u32x4_t a = {k0[0], k0[1], k1[0], k1[1]};
+    const u32x4_t b = {v0[0], v0[1], v1[0], v1[1]};
+    av = __builtin_bit_cast(bf16x8_t, a);
+    bv = __builtin_bit_cast(bf16x8_t, b);
+}
+
 template <int D, int U, int R, int DG>
 __global__ void __launch_bounds__(kThreads)
 svla_state_build_dma(const BuildArgs a)
@@ -709,6 +771,7 @@ svla_state_build_dma(const BuildArgs a)
     constexpr int STAGEB = 2 * TILEB;     // K tile, then V tile
     constexpr bool SPLITK = (D == 32);
     constexpr int TPW = SPLITK ? 1 : D / 64;
+    static_assert(TPW == 1, "one 32 x 32 tile per wave (d = 32, or the d = 128 quadrants)");
     constexpr int GPS = TT / 16;
     constexpr int L = 2 * U;              // loads per thread per stage
     constexpr bool QUAD = DG != D;
@@ -790,18 +853,21 @@ svla_state_build_dma(const BuildArgs a)
     const int nt0 = SPLITK ? 0 : (wave & 1) * TPW;
     const bool zwave = SPLITK || nt0 == 0;     // one wave per K fragment sums z
     constexpr int GPW = SPLITK ? GPS / 4 : GPS;  // 16-token groups per wave per stage
-    // Lane part of a fragment element's LDS index: k-slot i of a group reads
-    // row 16 gi + g + 2 i, and the row's parity (= g) fixes the swizzle.
+    // d = 32 (64-byte rows): lane (m, g) gathers k-slot i of a group from row
+    // 16 gi + g + 2 i, 16-bit reads (the row's parity (= g) fixes the
+    // swizzle; these were measured faster here than the transposing reads).
+    // Half-rows of d = 128: the lane's byte offsets of its transposing reads.
+    constexpr bool TR = D >= 64;
     int kl[TPW], vl[TPW];
 #pragma unroll
     for (int tm = 0; tm < TPW; ++tm) {
         const int f = 32 * (mt0 + tm) + m;
-        kl[tm] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
+        kl[tm] = TR ? trb_offset<D>(lane, 32 * (mt0 + tm)) : g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
     }
 #pragma unroll
     for (int tn = 0; tn < TPW; ++tn) {
         const int f = 32 * (nt0 + tn) + m;
-        vl[tn] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
+        vl[tn] = TR ? trb_offset<D>(lane, 32 * (nt0 + tn)) : g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
     }
 
     const int ntiles = tok_hi > tok_lo ? (tok_hi - tok_lo + TT - 1) / TT : 0;
@@ -831,32 +897,34 @@ svla_state_build_dma(const BuildArgs a)
             }
             lds_barrier();                 // ... everyone's have; stage it-1 is consumed
             issue(buf((j + R - 1) % R), it + R - 1);
-            const unsigned short *Ks = (const unsigned short *)buf(j);
-            const unsigned short *Vs = Ks + TT * D;
+            const unsigned char *Ks = buf(j);
+            const unsigned char *Vs = Ks + TILEB;
 #pragma unroll
             for (int gg = 0; gg < GPW; ++gg) {
                 const int gi = SPLITK ? wave + 4 * gg : gg;
                 bf16x8_t av[TPW], bv[TPW];
+                if constexpr (TR) {
+                    trb_load2<D>(Ks + 16 * gi * ROWB, kl[0], Vs + 16 * gi * ROWB, vl[0], av[0], bv[0]);
+                } else {
+                    const unsigned short *pk = (const unsigned short *)Ks + 16 * gi * D + kl[0];
+                    const unsigned short *pv = (const unsigned short *)Vs + 16 * gi * D + vl[0];
+                    u16x8_t x, y;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        x[i] = pk[2 * i * D];
+                        y[i] = pv[2 * i * D];
+                    }
+                    av[0] = __builtin_bit_cast(bf16x8_t, x);
+                    bv[0] = __builtin_bit_cast(bf16x8_t, y);
+                }
 #pragma unroll
                 for (int tm = 0; tm < TPW; ++tm) {
-                    const unsigned short *pk = Ks + 16 * gi * D + kl[tm];
-                    u16x8_t x;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] = pk[2 * i * D];
-                    u32x4_t w = __builtin_bit_cast(u32x4_t, x);
+                    u32x4_t w = __builtin_bit_cast(u32x4_t, av[tm]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = relu_bf16x2(w[e]);
                     av[tm] = __builtin_bit_cast(bf16x8_t, w);
                     // z on the matrix cores: phi(K) times a ones operand
                     if (zwave) zt[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], ones, zt[tm], 0, 0, 0);
-                }
-#pragma unroll
-                for (int tn = 0; tn < TPW; ++tn) {
-                    const unsigned short *pv = Vs + 16 * gi * D + vl[tn];
-                    u16x8_t x;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] = pv[2 * i * D];
-                    bv[tn] = __builtin_bit_cast(bf16x8_t, x);
                 }
 #pragma unroll
                 for (int tm = 0; tm < TPW; ++tm)
@@ -1048,12 +1116,14 @@ svla_state_build_rope(const BuildArgs a)
 
     const int m = lane & 31, g = lane >> 5;
     // lane part of a fragment element's LDS index: k-slot i of group gi reads
-    // row 16 gi + g + 2 i; the row's parity (= g) fixes the swizzle
+    // row 16 gi + g + 2 i; the row's parity (= g) fixes the swizzle.  With
+    // transposing reads: the lane's byte offsets within a 16-token group.
+    constexpr bool TR = SVLA_ROPE_TR != 0;
     int fl[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int f = 32 * t + m;
-        fl[t] = g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
+        fl[t] = TR ? trb_offset<D>(lane, 32 * t) : g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
     }
 
     // The loop is kept regular so the compiler can count the loads in flight:
@@ -1107,16 +1177,22 @@ svla_state_build_rope(const BuildArgs a)
                 bf16x8_t av[TPW], al[TPW], bv[TPW];
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
-                    u16x8_t x, y, w;
+                    if constexpr (TR) {
+                        av[t] = trb_load<D>(slot + 16 * gi * ROWB, fl[t]);
+                        al[t] = trb_load<D>(slot + TILEB + 16 * gi * ROWB, fl[t]);
+                        bv[t] = trb_load<D>(slot + NK * TILEB + 16 * gi * ROWB, fl[t]);
+                    } else {
+                        u16x8_t x, y, w;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        x[e] = Kh[16 * gi * D + fl[t] + 2 * e * D];
-                        y[e] = Kl[16 * gi * D + fl[t] + 2 * e * D];
-                        w[e] = Vs[16 * gi * D + fl[t] + 2 * e * D];
+                        for (int e = 0; e < 8; ++e) {
+                            x[e] = Kh[16 * gi * D + fl[t] + 2 * e * D];
+                            y[e] = Kl[16 * gi * D + fl[t] + 2 * e * D];
+                            w[e] = Vs[16 * gi * D + fl[t] + 2 * e * D];
+                        }
+                        av[t] = __builtin_bit_cast(bf16x8_t, x);
+                        al[t] = __builtin_bit_cast(bf16x8_t, y);
+                        bv[t] = __builtin_bit_cast(bf16x8_t, w);
                     }
-                    av[t] = __builtin_bit_cast(bf16x8_t, x);
-                    al[t] = __builtin_bit_cast(bf16x8_t, y);
-                    bv[t] = __builtin_bit_cast(bf16x8_t, w);
                 }
 #pragma unroll
                 for (int tm = 0; tm < TPW; ++tm)
