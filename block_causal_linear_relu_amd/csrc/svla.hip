@@ -49,7 +49,13 @@
 #define SVLA_DMA_U 1               // the same for d = 64, 128
 #endif
 #ifndef SVLA_DMA_R
-#define SVLA_DMA_R 4
+#define SVLA_DMA_R 4               // ... ring depth for d = 64
+#endif
+#ifndef SVLA_DMA_R128
+#define SVLA_DMA_R128 3            // ... and for d = 128
+#endif
+#ifndef SVLA_MIN_SPLIT_128
+#define SVLA_MIN_SPLIT_128 4       // d = 128 build without RoPE: tokens per split >= this * d
 #endif
 #ifndef SVLA_ROPE_PF
 #define SVLA_ROPE_PF 2             // state build with RoPE: stages in flight per wave
@@ -669,15 +675,15 @@ svla_state_scan_k(const ScanArgs a)
 // ---------------------------------------------------------------------------
 // svla_state_build, bf16 inputs without RoPE, loads straight to LDS.
 //
-// Workgroup = (bh, block c, split s[, quadrant]): it walks its token range in
+// Workgroup = (bh, block c, split s): it walks its token range in
 // stages of TT tokens.  K and V travel from global memory into an R-deep
 // ring of LDS stages with buffer_load ... lds (16 bytes per lane, one
 // kilobyte per wave instruction), so R - 1 stages of loads stay in flight
 // without holding registers.  The contraction S = phi(K)^T V runs on
-// v_mfma_f32_32x32x16_bf16 over tokens: each lane gathers 8 tokens of one
+// v_mfma_f32_32x32x16_bf16 over tokens: each lane needs 8 tokens of one
 // feature from the staged rows (which token feeds which k-slot does not
-// matter for a sum over tokens, as long as A and B agree; lanes 32-63 take
-// the odd tokens so the two half-waves read disjoint banks).  phi is applied
+// matter for a sum over tokens, as long as A and B agree): 16-bit gathers
+// for d = 32, transposing reads (ds_read_b64_tr_b16) for d >= 64.  phi is applied
 // to the K fragments, and z comes out of the same matrix cores as phi(K)
 // times a ones operand.  Rows of the last stage past the range are
 // overwritten with zeros by the lanes that loaded them.  Each stage buffer
@@ -686,8 +692,10 @@ svla_state_scan_k(const ScanArgs a)
 //   d = 32 : one 32x32 output tile; the 4 waves split the stage's tokens and
 //            their tiles are summed through LDS at the end.
 //   d = 64 : 2x2 tiles, one per wave; every wave sees every token.
-//   d = 128: DG = 128, D = 64: four workgroups per (bh, block, split), one
-//            64 x 64 quadrant of S each, from K and V half-rows.
+//   d = 128: 4x4 tiles, 2x2 per wave; every wave sees every token.  (Four
+//            workgroups per unit, one 64 x 64 quadrant each, read the K and
+//            V half-rows twice through L2 and lost more to L2 misses than
+//            the extra split partials of whole rows cost.)
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -758,7 +766,7 @@ __device__ __forceinline__ void trb_load2(const unsigned char *kgrp, int koff, c
     bv = __builtin_bit_cast(bf16x8_t, b);
 }
 
-template <int D, int U, int R, int DG>
+template <int D, int U, int R>
 __global__ void __launch_bounds__(kThreads)
 svla_state_build_dma(const BuildArgs a)
 {
@@ -771,13 +779,11 @@ svla_state_build_dma(const BuildArgs a)
     constexpr int STAGEB = 2 * TILEB;     // K tile, then V tile
     constexpr bool SPLITK = (D == 32);
     constexpr int TPW = SPLITK ? 1 : D / 64;
-    static_assert(TPW == 1, "one 32 x 32 tile per wave (d = 32, or the d = 128 quadrants)");
+    static_assert(TPW <= 2, "at most 2 x 2 tiles of 32 x 32 per wave");
     constexpr int GPS = TT / 16;
     constexpr int L = 2 * U;              // loads per thread per stage
-    constexpr bool QUAD = DG != D;
     static_assert(R >= 3 && R <= 4, "ring depth");
     static_assert(!SPLITK || STAGEB >= 8192, "epilogue reuses two stage buffers");
-    static_assert(!QUAD || (DG == 128 && D == 64), "quadrant split is for d = 128");
 
     __shared__ __attribute__((aligned(16))) unsigned char b0[STAGEB];
     __shared__ __attribute__((aligned(16))) unsigned char b1[STAGEB];
@@ -786,19 +792,7 @@ svla_state_build_dma(const BuildArgs a)
     __shared__ float zred[4 * D];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // Quadrants of one unit get workgroup ids 8 apart, so the round-robin
-    // dispatch puts all four on the same XCD and its L2 serves the shared
-    // K/V half-rows.
-    long wid = blockIdx.x;
-    int qm = 0, qn = 0;
-    if constexpr (QUAD) {
-        const long x = wid % 8, r = wid / 8;
-        const int q = (int)(r % 4);
-        qm = q >> 1;
-        qn = q & 1;
-        wid = (r / 4) * 8 + x;
-        if (wid >= (long)a.nb * a.splits * a.BH) return;
-    }
+    const long wid = blockIdx.x;
     const unsigned per_bh = (unsigned)(a.splits * a.nb);
     const long bh = wid / per_bh;
     const int rest = (int)(wid - bh * per_bh);
@@ -806,10 +800,9 @@ svla_state_build_dma(const BuildArgs a)
     const int tok_lo = c * a.n + s * a.chunk;
     const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
 
-    const uint32_t slice = (uint32_t)a.N * DG * 2;
+    const uint32_t slice = (uint32_t)a.N * D * 2;
     const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
     const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
-    const int kcol = 64 * qm, vcol = 64 * qn;   // first feature of this tile in K / V
 
     auto buf = [&](int j) -> unsigned char * {
         return j == 0 ? b0 : j == 1 ? b1 : j == 2 ? b2 : b3;
@@ -823,11 +816,10 @@ svla_state_build_dma(const BuildArgs a)
             const int t = tok_lo + st * TT + r;
             const int cg = swz16<D>(r, lane % CPR);
             const bool in = t < tok_hi;
-            const uint32_t offk = in ? (uint32_t)(t * DG + kcol + cg * 8) * 2u : kOOB;
-            const uint32_t offv = in ? (uint32_t)(t * DG + vcol + cg * 8) * 2u : kOOB;
+            const uint32_t off = in ? (uint32_t)(t * D + cg * 8) * 2u : kOOB;
             unsigned char *kd = dst + (u * 4 + wave) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)kd, 16, offk, 0, 0, SVLA_KV_AUX);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(kd + TILEB), 16, offv, 0, 0, SVLA_KV_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)kd, 16, off, 0, 0, SVLA_KV_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(kd + TILEB), 16, off, 0, 0, SVLA_KV_AUX);
         }
     };
 
@@ -904,7 +896,9 @@ svla_state_build_dma(const BuildArgs a)
                 const int gi = SPLITK ? wave + 4 * gg : gg;
                 bf16x8_t av[TPW], bv[TPW];
                 if constexpr (TR) {
-                    trb_load2<D>(Ks + 16 * gi * ROWB, kl[0], Vs + 16 * gi * ROWB, vl[0], av[0], bv[0]);
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t)
+                        trb_load2<D>(Ks + 16 * gi * ROWB, kl[t], Vs + 16 * gi * ROWB, vl[t], av[t], bv[t]);
                 } else {
                     const unsigned short *pk = (const unsigned short *)Ks + 16 * gi * D + kl[0];
                     const unsigned short *pv = (const unsigned short *)Vs + 16 * gi * D + vl[0];
@@ -939,8 +933,8 @@ svla_state_build_dma(const BuildArgs a)
 
     // ---- epilogue: S_part (row-major [k][v]) and z_part
     const long unit = (bh * a.nb + c) * a.slots + s;
-    const auto rS = make_rsrc(a.S_part + unit * DG * DG, DG * DG * 4);
-    const auto rz = make_rsrc(a.z_part + unit * DG, DG * 4);
+    const auto rS = make_rsrc(a.S_part + unit * D * D, D * D * 4);
+    const auto rz = make_rsrc(a.z_part + unit * D, D * 4);
     // z: column 0 of each zt tile, held by lanes 0 (rows 8q + r, r < 4) and 32 (rows 8q + 4 + r)
     if constexpr (SPLITK) {
         float *red = (float *)(wave < 2 ? b0 : b1);   // 2 waves x 16 x 64 floats each
@@ -988,15 +982,13 @@ svla_state_build_dma(const BuildArgs a)
             for (int tn = 0; tn < TPW; ++tn)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int rr = kcol + 32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const int cc = vcol + 32 * (nt0 + tn) + m;
-                    store4(rS, (uint32_t)(rr * DG + cc) * 4u, acc[tm][tn][r]);
+                    const int rr = 32 * (mt0 + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const int cc = 32 * (nt0 + tn) + m;
+                    store4(rS, (uint32_t)(rr * D + cc) * 4u, acc[tm][tn][r]);
                 }
-        if (tid < D && qn == 0) store4(rz, (uint32_t)(kcol + tid) * 4u, zred[tid]);
+        if (tid < D) store4(rz, (uint32_t)tid * 4u, zred[tid]);
     }
-    if constexpr (!QUAD) {
-        if (a.S_in && s == 0) carry_in(a, bh, D);
-    }
+    if (a.S_in && s == 0) carry_in(a, bh, D);
 }
 
 // ---------------------------------------------------------------------------
@@ -2029,17 +2021,19 @@ constexpr int rope_u(int d) { return d == 32 || SVLA_ROPE_U >= 2 ? SVLA_ROPE_U :
 constexpr int rope_tokens(int d) { return rope_u(d) * 64 / ((d == 128 ? 64 : d) / 8); }
 
 // Splits of a block's tokens over workgroups: about `target` workgroups per
-// launch, but never fewer than SVLA_MIN_SPLIT_PER_D * d tokens per split, so
-// the fp32 partial state (4 d^2 bytes) stays a small fraction of the K/V
-// bytes it summarises (1/8 at the default).  Measured: the build without
-// RoPE runs best with one or two long-lived workgroups per CU, the RoPE
-// build (bound by its vector ALU work) with many.
-int pick_splits(long units, int n, int d, long target, int *chunk_out)
+// launch, but never fewer than min_per_d * d tokens per split, so the fp32
+// partial state (4 d^2 bytes) stays a small fraction of the K/V bytes it
+// summarises (1/8 at the default, 1/4 for the d = 128 build without RoPE,
+// whose workgroups take whole rows).  Measured: the build without RoPE runs
+// best with one or two long-lived workgroups per CU, the RoPE build with
+// many.
+int pick_splits(long units, int n, int d, long target, int *chunk_out,
+                int min_per_d = SVLA_MIN_SPLIT_PER_D)
 {
     constexpr int G = 64;   // chunk granularity; independent of the stage size
     if (n <= 0 || units <= 0) { *chunk_out = G; return 0; }
     long want = (target + units - 1) / units;
-    long cap = n / (SVLA_MIN_SPLIT_PER_D * d);
+    long cap = n / (min_per_d * d);
     if (cap < 1) cap = 1;
     long s = want < cap ? want : cap;
     if (s < 1) s = 1;
@@ -2106,7 +2100,8 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     p->dma = p->esize == 2 && !p->rope.on;
     const long units = p->BH * nb;
     int chunk_dma = 0, chunk_other = 0;
-    const int splits_dma = pick_splits(units, n, d, SVLA_DMA_WGS, &chunk_dma);
+    const int splits_dma = pick_splits(units, n, d, SVLA_DMA_WGS, &chunk_dma,
+                                       d == 128 ? SVLA_MIN_SPLIT_128 : SVLA_MIN_SPLIT_PER_D);
     const int splits_other = pick_splits(units, n, d, SVLA_ROPE_WGS, &chunk_other);
     if (op == SVLA_OP_STATE_BUILD) {
         // one workgroup per block: its partial is the block's local state
@@ -2191,14 +2186,9 @@ void launch_build(const Plan &p, const BuildArgs &args, hipStream_t s)
     char nm[96];
     if (p.dma) {
         constexpr int U = D == 32 ? SVLA_DMA_U32 : SVLA_DMA_U;
-        constexpr int R = D == 32 ? SVLA_DMA_R32 : SVLA_DMA_R;
-        if constexpr (D == 128) {
-            snprintf(nm, sizeof nm, "void svla_state_build_dma<64, %d, %d, 128>", U, R);
-            launch(svla_state_build_dma<64, U, R, 128>, qgrid, 0, s, SLOT_BUILD, a, nm);
-        } else {
-            snprintf(nm, sizeof nm, "void svla_state_build_dma<%d, %d, %d, %d>", D, U, R, D);
-            launch(svla_state_build_dma<D, U, R, D>, grid, 0, s, SLOT_BUILD, a, nm);
-        }
+        constexpr int R = D == 32 ? SVLA_DMA_R32 : D == 64 ? SVLA_DMA_R : SVLA_DMA_R128;
+        snprintf(nm, sizeof nm, "void svla_state_build_dma<%d, %d, %d>", D, U, R);
+        launch(svla_state_build_dma<D, U, R>, grid, 0, s, SLOT_BUILD, a, nm);
     } else if (p.esize == 2) {
         constexpr int PF = rope_pf(), U = rope_u(D);
         if constexpr (D == 128) {
