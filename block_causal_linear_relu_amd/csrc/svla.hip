@@ -96,6 +96,12 @@
 #ifndef SVLA_APPLY_PF
 #define SVLA_APPLY_PF 4            // ... 16-token groups of Q loads in flight per wave
 #endif
+#ifndef SVLA_APPLY_RING
+#define SVLA_APPLY_RING 1          // ... Q and O staged through LDS as whole rows
+#endif
+#ifndef SVLA_APPLY_RING_PF
+#define SVLA_APPLY_RING_PF 2       // ... groups in flight per wave (LDS slots)
+#endif
 #ifndef SVLA_APPLY_XCD
 #define SVLA_APPLY_XCD 1           // apply: the token tiles of one block on one XCD
 #endif
@@ -1829,6 +1835,222 @@ svla_apply_lds(const ApplyArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// svla_apply, bf16 inputs, d = 64 and 128, Q and O staged through LDS.
+//
+// The same contraction as svla_apply_lds, with whole-row memory accesses:
+// each wave owns a ring of PF slots, one 16-token group each.  A group's Q
+// rows land in its slot straight from memory (buffer_load ... lds, every
+// wave instruction one contiguous kilobyte of whole rows); the 16-byte
+// chunks of row r sit at position chunk ^ (r mod chunks per row), so the
+// MFMA operand reads (16 rows, one chunk each) hit distinct banks.  The
+// output of the group goes back into the same slot in the same layout and
+// leaves it as whole rows, one contiguous kilobyte per store instruction.
+// No wave touches another wave's slots and the LDS operations of one wave
+// execute in program order, so the ring needs no barrier.
+// ---------------------------------------------------------------------------
+template <int D, bool ROPE, int PF>
+__global__ void __launch_bounds__(kThreads)
+svla_apply_ring(const ApplyArgs a)
+{
+    constexpr int MT = D / 16;            // 16-feature m-tiles of the output
+    constexpr int KS = D / 32;            // 32-deep k-steps
+    constexpr int NFRAG = MT * KS;        // 1 KB fragments of the packed state
+    constexpr int CPR = D / 8;            // 16-byte chunks per row
+    constexpr int ROWB = D * 2;
+    constexpr int RPI = 64 / CPR;         // rows one wave instruction covers
+    constexpr int NI = 16 / RPI;          // wave instructions per group
+    constexpr int SLOTB = 16 * ROWB;
+    static_assert(NFRAG % 4 == 0, "the four waves copy the state in equal shares");
+    static_assert(NI == KS, "one kilobyte per k-step");
+    static_assert(PF >= 1 && PF <= 3, "ring depth");
+    __shared__ __attribute__((aligned(16))) unsigned char sS[NFRAG * 1024];
+    // ring position p of the four waves: an LDS object of its own, so the
+    // compiler can tell a slot's reads from the loads in flight into the
+    // other positions
+    __shared__ __attribute__((aligned(16))) unsigned char r0[4 * SLOTB];
+    __shared__ __attribute__((aligned(16))) unsigned char r1[PF > 1 ? 4 * SLOTB : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char r2[PF > 2 ? 4 * SLOTB : 16];
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // RoPE table
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const long lid = xcd_logical(a.groups);
+    if (lid >= a.groups) return;
+    const int tile = (int)(lid % a.tiles);
+    const int c = (int)((lid / a.tiles) % a.nb);
+    const long bh = lid / ((long)a.tiles * a.nb);
+    const int t_lo = c * a.n + tile * a.tile;
+    const int t_hi = min(t_lo + a.tile, (c + 1) * a.n);
+    const long unit = bh * a.nb + c;
+
+    const uint32_t slice = (uint32_t)a.N * D * 2;
+    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
+    const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
+    const auto rS = make_rsrc((const char *)a.S_op + unit * D * D * 2, D * D * 2);
+    const auto rz = make_rsrc(a.z_pre + unit * D, D * 4);
+    const int kg = lane >> 4, tl = lane & 15;
+    auto slot_of = [&](int p) -> unsigned char * {
+        return (p == 0 ? r0 : p == 1 ? r1 : r2) + wave * SLOTB;
+    };
+
+    // 1. the state operand -> LDS, one fragment per wave instruction
+    constexpr int FPW = NFRAG / 4;
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+        const int f = wave + 4 * j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(sS + f * 1024), 16,
+                                                 (uint32_t)(f * 1024 + lane * 16), 0, 0, 0);
+    }
+    // 2. z for this lane's k positions
+    u32x4_t zr[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        zr[ks][0] = load16(rz, (uint32_t)(8 * (4 * ks + kg)) * 4u);
+        zr[ks][1] = load16(rz, (uint32_t)(8 * (4 * ks + kg) + 4) * 4u);
+    }
+    // 3. the first PF groups of Q: this wave's group i -> slot i % PF; lane l
+    // of instruction j brings row RPI j + l / CPR, chunk (l % CPR) ^ (row % CPR)
+    const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
+    const int nw = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
+    const int nwr = (nw + PF - 1) / PF * PF;
+    const int lrow = lane / CPR, lpos = lane % CPR;
+    auto row_off = [&](int i, int j) -> uint32_t {      // global byte offset of lane's chunk, or kOOB
+        const int row = RPI * j + lrow;
+        const int tok = t_lo + 16 * (wave + 4 * i) + row;
+        return tok < t_hi ? (uint32_t)(tok * D + ((lpos ^ (row & (CPR - 1))) * 8)) * 2u : kOOB;
+    };
+    auto issue = [&](int i, unsigned char *slot) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            // (the offset in a variable of its own: with a lambda call as the
+            // builtin's argument this compiler drops the kernel's host stub)
+            const uint32_t off = row_off(i, j);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_ptr_t)(slot + j * 1024), 16, off, 0, 0, SVLA_Q_AUX);
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p) issue(p, slot_of(p));
+
+    // the z tile: lane (rho + 16 kg), k = 32 ks + 8 kg + i holds z_hi[k] in
+    // rows rho = 4j, z_lo[k] in rows 4j + 1, 0 in the others
+    wait_vmcnt<PF * NI>();
+    bf16x8_t zt[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u16x8_t h;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = as_f32(zr[ks][i >> 2][i & 3]);
+            const unsigned short hi = f2bf(v);
+            const unsigned short lo = f2bf(v - as_f32((unsigned int)hi << 16));
+            h[i] = (tl & 3) == 0 ? hi : (tl & 3) == 1 ? lo : (unsigned short)0;
+        }
+        zt[ks] = __builtin_bit_cast(bf16x8_t, h);
+    }
+
+    float2 *tab = (float2 *)lds;
+    uint32_t frame_lo = 0;
+    RopePairs<4> pp[KS];
+    if constexpr (ROPE) {
+        frame_lo = t_lo < t_hi ? fdiv((uint32_t)t_lo, a.rope.div_hw) : 0;
+        const uint32_t frame_hi = t_lo < t_hi ? fdiv((uint32_t)(t_hi - 1), a.rope.div_hw) : 0;
+        const int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pp[ks] = rope_pairs<4>(a.rope, 8 * (4 * ks + kg), nf);
+    }
+    lds_barrier();         // every wave's state fragments (and the table) are in LDS
+
+    // the lane's operand row tl: chunk c sits at position c ^ (tl % CPR)
+    const int rsw = tl & (CPR - 1);
+    for (int i0 = 0; i0 < nwr; i0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int i = i0 + p;
+            unsigned char *slot = slot_of(p);
+            // this group's rows have landed: the loads of the PF - 1 later
+            // groups may still be in flight.  Loads complete in order among
+            // themselves, but the output stores between them may complete
+            // before or after them, so the count admits no store.
+            wait_vmcnt<(PF - 1) * NI>();
+            const int tok = t_lo + 16 * (wave + 4 * i) + tl;
+            u32x4_t qr[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qr[ks] = *(const u32x4_t *)(slot + tl * ROWB + (((4 * ks + kg) ^ rsw) * 16));
+
+            bf16x8_t qu[KS], qf[KS];
+            RopePos rp{0, 0, 0};
+            if constexpr (ROPE) rp = rope_pos((uint32_t)tok, frame_lo, a.rope);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4_t pq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[ks][e]);
+                qu[ks] = __builtin_bit_cast(bf16x8_t, pq);
+                if constexpr (ROPE) {
+                    float pf[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pf[2 * e] = bf16lo(pq[e]);
+                        pf[2 * e + 1] = bf16hi(pq[e]);
+                    }
+                    rope_rotate<4>(pf, rp, pp[ks], tab);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pq[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
+                    qf[ks] = __builtin_bit_cast(bf16x8_t, pq);
+                } else {
+                    qf[ks] = qu[ks];
+                }
+            }
+            f32x4_t dz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                dz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zt[ks], qu[ks], dz, 0, 0, 0);
+            f32x4_t acc[MT];
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) acc[mi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8_t sf[MT];
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi)
+                    sf[mi] = *(const bf16x8_t *)(sS + (mi * KS + ks) * 1024 + lane * 16);
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi)
+                    acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mi], qf[ks], acc[mi], 0, 0, 0);
+            }
+            const float den = dz[0] + dz[1] + a.eps;
+            const float inv = den != 0.f ? 1.0f / den : 0.f;
+            // m-tiles 2h, 2h + 1 hold O[tok][op_col(2h, 4 kg) + 0 .. 7], that is
+            // chunk 4 h + kg of the output row: into the slot, over this group's Q
+#pragma unroll
+            for (int h = 0; h < MT / 2; ++h) {
+                u32x4_t o;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    o[2 * e] = pack_bf16(acc[2 * h + e][0] * inv, acc[2 * h + e][1] * inv);
+                    o[2 * e + 1] = pack_bf16(acc[2 * h + e][2] * inv, acc[2 * h + e][3] * inv);
+                }
+                *(u32x4_t *)(slot + tl * ROWB + (((4 * h + kg) ^ rsw) * 16)) = o;
+            }
+            // whole rows out, then the next group PF ahead into the slot.  The
+            // slot's reads must have returned before its loads are issued: a
+            // load writes LDS when its data arrives, which for a row past the
+            // range (zeros, no memory access) can be almost at once.
+            u32x4_t orow[NI];
+#pragma unroll
+            for (int j = 0; j < NI; ++j) orow[j] = *(const u32x4_t *)(slot + j * 1024 + lane * 16);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < NI; ++j) store16p<SVLA_O_AUX>(rO, row_off(i, j), orow[j]);
+            issue(i + PF, slot);
+        }
+    }
+    wait_vmcnt<0>();      // the trailing out-of-range loads target the ring too
+}
+
+// ---------------------------------------------------------------------------
 // svla_apply, fp32 inputs: v_mfma_f32_16x16x4_f32, lane chunk = 4 features
 // of chunk 4 kq + lane / 16; the state operand stays fp32.
 // ---------------------------------------------------------------------------
@@ -2233,10 +2455,17 @@ void launch_apply(const Plan &p, const ApplyArgs &args, hipStream_t s)
              p.rope.on ? "true" : "false");
     if (p.esize == 2) {
         if constexpr (D >= 64) {
-            constexpr int PF = SVLA_APPLY_PF;
-            snprintf(nm, sizeof nm, "void svla_apply_lds<%d, %s, %d>", D, p.rope.on ? "true" : "false", PF);
-            if (p.rope.on) launch(svla_apply_lds<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-            else launch(svla_apply_lds<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            if constexpr (SVLA_APPLY_RING) {
+                constexpr int PF = SVLA_APPLY_RING_PF;
+                snprintf(nm, sizeof nm, "void svla_apply_ring<%d, %s, %d>", D, p.rope.on ? "true" : "false", PF);
+                if (p.rope.on) launch(svla_apply_ring<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else launch(svla_apply_ring<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            } else {
+                constexpr int PF = SVLA_APPLY_PF;
+                snprintf(nm, sizeof nm, "void svla_apply_lds<%d, %s, %d>", D, p.rope.on ? "true" : "false", PF);
+                if (p.rope.on) launch(svla_apply_lds<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else launch(svla_apply_lds<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            }
         } else {
             if (p.fold) {
                 snprintf(nm, sizeof nm, "void svla_apply_bf16<%d, %s, true>", D, p.rope.on ? "true" : "false");
