@@ -93,14 +93,8 @@
 #ifndef SVLA_APPLY_TILE_LDS
 #define SVLA_APPLY_TILE_LDS 256    // bf16 apply with the state in LDS (d >= 64): tokens per workgroup
 #endif
-#ifndef SVLA_APPLY_PF
-#define SVLA_APPLY_PF 4            // ... 16-token groups of Q loads in flight per wave
-#endif
-#ifndef SVLA_APPLY_RING
-#define SVLA_APPLY_RING 1          // ... Q and O staged through LDS as whole rows
-#endif
 #ifndef SVLA_APPLY_RING_PF
-#define SVLA_APPLY_RING_PF 2       // ... groups in flight per wave (LDS slots)
+#define SVLA_APPLY_RING_PF 2       // bf16 apply, d >= 64: groups of Q in flight per wave (LDS slots)
 #endif
 #ifndef SVLA_APPLY_XCD
 #define SVLA_APPLY_XCD 1           // apply: the token tiles of one block on one XCD
@@ -1653,7 +1647,8 @@ svla_apply_bf16(const ApplyArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// svla_apply, bf16 inputs, d = 64 and 128: the block state in LDS.
+// svla_apply, bf16 inputs, d = 64 and 128: the block state and the token
+// rows in LDS.
 //
 // Workgroup = (bh, block c, token tile); the tiles of one block run on one
 // XCD.  The packed state operand of the block (d*d bf16, 1 KB per MFMA
@@ -1661,184 +1656,14 @@ svla_apply_bf16(const ApplyArgs a)
 // tile's 16-token groups (wave w takes groups w, w + 4, ...), so each Q
 // element is loaded and prepared once.  Per group, O^T = S^T phi~(Q)^T on
 // v_mfma_f32_16x16x32_bf16: the A fragments come from LDS, phi~(q) is the
-// B operand straight from a 16-byte load per lane (token = lane % 16,
-// features 8 (4 ks + lane / 16) ...).  The denominator runs on the matrix
-// cores too: one more A tile whose rows 4j and 4j + 1 hold z split into
-// bf16 hi and lo parts (zero elsewhere), against the unrotated phi(q), puts
-// phi(q) . z (to ~16 bits of z) in the first two accumulator values of
-// every lane of the token.  PF groups of Q loads stay in flight per wave.
-// ---------------------------------------------------------------------------
-template <int D, bool ROPE, int PF>
-__global__ void __launch_bounds__(kThreads)
-svla_apply_lds(const ApplyArgs a)
-{
-    constexpr int MT = D / 16;            // 16-feature m-tiles of the output
-    constexpr int KS = D / 32;            // 32-deep k-steps
-    constexpr int NFRAG = MT * KS;        // 1 KB fragments of the packed state
-    static_assert(NFRAG % 4 == 0, "the four waves copy the state in equal shares");
-    __shared__ __attribute__((aligned(16))) unsigned char sS[NFRAG * 1024];
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];   // RoPE table
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-    const long lid = xcd_logical(a.groups);
-    if (lid >= a.groups) return;
-    const int tile = (int)(lid % a.tiles);
-    const int c = (int)((lid / a.tiles) % a.nb);
-    const long bh = lid / ((long)a.tiles * a.nb);
-    const int t_lo = c * a.n + tile * a.tile;
-    const int t_hi = min(t_lo + a.tile, (c + 1) * a.n);
-    const long unit = bh * a.nb + c;
-
-    const uint32_t slice = (uint32_t)a.N * D * 2;
-    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
-    const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
-    const auto rS = make_rsrc((const char *)a.S_op + unit * D * D * 2, D * D * 2);
-    const auto rz = make_rsrc(a.z_pre + unit * D, D * 4);
-    const int kg = lane >> 4, tl = lane & 15;
-
-    // 1. the state operand -> LDS, one fragment per wave instruction
-    constexpr int FPW = NFRAG / 4;
-#pragma unroll
-    for (int j = 0; j < FPW; ++j) {
-        const int f = wave + 4 * j;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(sS + f * 1024), 16,
-                                                 (uint32_t)(f * 1024 + lane * 16), 0, 0, 0);
-    }
-    // 2. z for this lane's k positions
-    u32x4_t zr[KS][2];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        zr[ks][0] = load16(rz, (uint32_t)(8 * (4 * ks + kg)) * 4u);
-        zr[ks][1] = load16(rz, (uint32_t)(8 * (4 * ks + kg) + 4) * 4u);
-    }
-    // 3. the first PF groups of Q (slot p holds this wave's group i, i % PF == p;
-    // the scheduling barriers keep the loads in slot order)
-    const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
-    const int nw = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
-    const int nwr = (nw + PF - 1) / PF * PF;
-    auto qoff = [&](int i, int ks) -> uint32_t {
-        const int tok = t_lo + 16 * (wave + 4 * i) + tl;
-        return tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB;
-    };
-    u32x4_t qreg[PF][KS];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(p, ks));
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // the z tile: lane (rho + 16 kg), k = 32 ks + 8 kg + i holds z_hi[k] in
-    // rows rho = 4j, z_lo[k] in rows 4j + 1, 0 in the others
-    wait_vmcnt<PF * KS>();
-    bf16x8_t zt[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u16x8_t h;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = as_f32(zr[ks][i >> 2][i & 3]);
-            const unsigned short hi = f2bf(v);
-            const unsigned short lo = f2bf(v - as_f32((unsigned int)hi << 16));
-            h[i] = (tl & 3) == 0 ? hi : (tl & 3) == 1 ? lo : (unsigned short)0;
-        }
-        zt[ks] = __builtin_bit_cast(bf16x8_t, h);
-    }
-
-    float2 *tab = (float2 *)lds;
-    uint32_t frame_lo = 0;
-    RopePairs<4> pp[KS];
-    if constexpr (ROPE) {
-        frame_lo = t_lo < t_hi ? fdiv((uint32_t)t_lo, a.rope.div_hw) : 0;
-        const uint32_t frame_hi = t_lo < t_hi ? fdiv((uint32_t)(t_hi - 1), a.rope.div_hw) : 0;
-        const int nf = (int)(frame_hi - frame_lo) + 1;
-        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) pp[ks] = rope_pairs<4>(a.rope, 8 * (4 * ks + kg), nf);
-    }
-    lds_barrier();         // every wave's state fragments (and the table) are in LDS
-
-    for (int i0 = 0; i0 < nwr; i0 += PF) {
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int i = i0 + p;
-            const int tok = t_lo + 16 * (wave + 4 * i) + tl;
-            u32x4_t qr[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qr[ks] = qreg[p][ks];
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(i + PF, ks));
-            __builtin_amdgcn_sched_barrier(0);
-
-            bf16x8_t qu[KS], qf[KS];
-            RopePos rp{0, 0, 0};
-            if constexpr (ROPE) rp = rope_pos((uint32_t)tok, frame_lo, a.rope);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4_t pq;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[ks][e]);
-                qu[ks] = __builtin_bit_cast(bf16x8_t, pq);
-                if constexpr (ROPE) {
-                    float pf[8];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pf[2 * e] = bf16lo(pq[e]);
-                        pf[2 * e + 1] = bf16hi(pq[e]);
-                    }
-                    rope_rotate<4>(pf, rp, pp[ks], tab);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pq[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
-                    qf[ks] = __builtin_bit_cast(bf16x8_t, pq);
-                } else {
-                    qf[ks] = qu[ks];
-                }
-            }
-            f32x4_t dz = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                dz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zt[ks], qu[ks], dz, 0, 0, 0);
-            // k-step outer: the MT fragment reads of a step go out together and
-            // its MT MFMAs are independent
-            f32x4_t acc[MT];
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) acc[mi] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bf16x8_t sf[MT];
-#pragma unroll
-                for (int mi = 0; mi < MT; ++mi)
-                    sf[mi] = *(const bf16x8_t *)(sS + (mi * KS + ks) * 1024 + lane * 16);
-#pragma unroll
-                for (int mi = 0; mi < MT; ++mi)
-                    acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mi], qf[ks], acc[mi], 0, 0, 0);
-            }
-            const float den = dz[0] + dz[1] + a.eps;
-            const float inv = den != 0.f ? 1.0f / den : 0.f;
-            // m-tiles 2h, 2h + 1 hold O[tok][op_col(2h, 4 kg) + 0 .. 7]
-            const bool valid = tok < t_hi;
-#pragma unroll
-            for (int h = 0; h < MT / 2; ++h) {
-                u32x4_t o;
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    o[2 * e] = pack_bf16(acc[2 * h + e][0] * inv, acc[2 * h + e][1] * inv);
-                    o[2 * e + 1] = pack_bf16(acc[2 * h + e][2] * inv, acc[2 * h + e][3] * inv);
-                }
-                const int v0 = op_col(2 * h, 4 * kg);
-                store16p<SVLA_O_AUX>(rO, valid ? (uint32_t)(tok * D + v0) * 2u : kOOB, o);
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// svla_apply, bf16 inputs, d = 64 and 128, Q and O staged through LDS.
+// B operand (token = lane % 16, features 8 (4 ks + lane / 16) ...).  The
+// denominator runs on the matrix cores too: one more A tile whose rows 4j
+// and 4j + 1 hold z split into bf16 hi and lo parts (zero elsewhere),
+// against the unrotated phi(q), puts phi(q) . z (to ~16 bits of z) in the
+// first two accumulator values of every lane of the token.
 //
-// The same contraction as svla_apply_lds, with whole-row memory accesses:
-// each wave owns a ring of PF slots, one 16-token group each.  A group's Q
+// Memory accesses are whole rows: each wave owns a ring of PF slots, one
+// 16-token group each.  A group's Q
 // rows land in its slot straight from memory (buffer_load ... lds, every
 // wave instruction one contiguous kilobyte of whole rows); the 16-byte
 // chunks of row r sit at position chunk ^ (r mod chunks per row), so the
@@ -2455,17 +2280,10 @@ void launch_apply(const Plan &p, const ApplyArgs &args, hipStream_t s)
              p.rope.on ? "true" : "false");
     if (p.esize == 2) {
         if constexpr (D >= 64) {
-            if constexpr (SVLA_APPLY_RING) {
-                constexpr int PF = SVLA_APPLY_RING_PF;
-                snprintf(nm, sizeof nm, "void svla_apply_ring<%d, %s, %d>", D, p.rope.on ? "true" : "false", PF);
-                if (p.rope.on) launch(svla_apply_ring<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-                else launch(svla_apply_ring<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-            } else {
-                constexpr int PF = SVLA_APPLY_PF;
-                snprintf(nm, sizeof nm, "void svla_apply_lds<%d, %s, %d>", D, p.rope.on ? "true" : "false", PF);
-                if (p.rope.on) launch(svla_apply_lds<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-                else launch(svla_apply_lds<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-            }
+            constexpr int PF = SVLA_APPLY_RING_PF;
+            snprintf(nm, sizeof nm, "void svla_apply_ring<%d, %s, %d>", D, p.rope.on ? "true" : "false", PF);
+            if (p.rope.on) launch(svla_apply_ring<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            else launch(svla_apply_ring<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
         } else {
             if (p.fold) {
                 snprintf(nm, sizeof nm, "void svla_apply_bf16<%d, %s, true>", D, p.rope.on ? "true" : "false");
