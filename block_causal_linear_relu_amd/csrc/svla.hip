@@ -250,6 +250,10 @@ struct RopeK {
     float base;
     FastDiv div_hw, div_w;   // p / (gh*gw), q / gw
     int tab_bytes;           // LDS reserved for the table in front of the stage buffers
+    // per axis (t, h, w): the frequency of pair 0 in turns per position,
+    // 1 / (2 pi), and the ratio base^(-2/width) between successive pairs
+    // (host fp64), so pair m's frequency is freq0 * ratio^m
+    double freq0[3], ratio[3];
 };
 
 // Table layout (float2 cos, sin), position fastest: [dt/2 pairs][nf frames],
@@ -260,25 +264,25 @@ __device__ __forceinline__ int rope_entries(const RopeK &r, int nf)
     return nf * (r.dt / 2) + r.gh * (r.dh / 2) + r.gw * (r.dw / 2);
 }
 
-// Angles pos * theta_m with theta_m = base^(-2m/width): the per-pair
-// frequencies (in turns, theta_m / 2 pi) are computed once per workgroup in
-// fp64, each entry's angle is reduced to a fraction of a turn in fp64 (so
-// large frame indices keep their accuracy) and only then goes through an
-// fp32 sin/cos of pi times that small argument.
-constexpr int kMaxRopePairs = 64;
+// Angles pos * theta_m with theta_m = base^(-2m/width): pair m's frequency
+// in turns per position is freq0 * ratio^m (fp64, by squaring: m < 64), each
+// entry's angle is reduced to a fraction of a turn in fp64 (so large frame
+// indices keep their accuracy) and only then goes through an fp32 sin/cos
+// of pi times that small argument.
+__device__ __forceinline__ double rope_freq(const RopeK &r, int a, int m)
+{
+    double f = r.freq0[a], q = r.ratio[a];
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+        if ((m >> b) & 1) f *= q;
+        q *= q;
+    }
+    return f;
+}
 
 __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
 {
-    __shared__ double turns_per_pos[3 * kMaxRopePairs];
-    const int pt = r.dt / 2, ph = r.dh / 2, pw = r.dw / 2;
-    for (int e = threadIdx.x; e < pt + ph + pw; e += blockDim.x) {
-        const int a = e < pt ? 0 : e < pt + ph ? 1 : 2;
-        const int m = a == 0 ? e : a == 1 ? e - pt : e - pt - ph;
-        const int width = a == 0 ? r.dt : a == 1 ? r.dh : r.dw;
-        turns_per_pos[a * kMaxRopePairs + m] =
-            pow((double)r.base, -2.0 * (double)m / (double)width) * (0.5 / M_PI);
-    }
-    lds_barrier();
+    const int pt = r.dt / 2, ph = r.dh / 2;
     const int nT = nf * pt, nH = r.gh * ph, total = rope_entries(r, nf);
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
         int pos, m, a;
@@ -289,7 +293,7 @@ __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
         } else {
             const int x = e - nT - nH; m = x / r.gw; pos = x - m * r.gw; a = 2;
         }
-        double turns = (double)pos * turns_per_pos[a * kMaxRopePairs + m];
+        double turns = (double)pos * rope_freq(r, a, m);
         turns -= floor(turns);
         float s, c;
         sincospif(2.0f * (float)turns, &s, &c);
@@ -2116,6 +2120,11 @@ svla_status check_rope(const char *fn, const svla_rope *r, int d, RopeK *out)
     out->gh = r->grid_h; out->gw = r->grid_w; out->t0 = r->t0; out->base = r->base;
     out->div_hw = make_fastdiv((uint32_t)(r->grid_h * r->grid_w));
     out->div_w = make_fastdiv((uint32_t)r->grid_w);
+    const int widths[3] = {r->dt_dims, r->dh_dims, r->dw_dims};
+    for (int ax = 0; ax < 3; ++ax) {
+        out->freq0[ax] = 0.5 / M_PI;
+        out->ratio[ax] = widths[ax] > 0 ? pow((double)r->base, -2.0 / widths[ax]) : 1.0;
+    }
     return SVLA_OK;
 }
 
