@@ -1455,9 +1455,12 @@ svla_apply_bf16(const ApplyArgs a)
         const float *pz = a.z_part + bh * a.splits * D + min(e0, D - 4);
 #pragma unroll
         for (int sp = 0; sp < MAXP; ++sp) {
-            const int q = min(sp, a.splits - 1);     // in bounds; used only below a.splits
-            part[sp][0] = *(const f32x4_t *)(pS + q * D * D);
-            part[sp][1] = *(const f32x4_t *)(pz + q * D);
+            if (sp < a.splits) {                     // (uniform)
+                part[sp][0] = *(const f32x4_t *)(pS + sp * D * D);
+                part[sp][1] = *(const f32x4_t *)(pz + sp * D);
+            } else {
+                part[sp][0] = part[sp][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            }
         }
     } else {
         const auto rS = make_rsrc((const char *)a.S_op + unit * D * D * 2, D * D * 2);
