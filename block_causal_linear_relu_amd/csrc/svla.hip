@@ -63,17 +63,11 @@
 #ifndef SVLA_ROPE_U
 #define SVLA_ROPE_U 2              // ... 16-byte loads per lane per tensor per stage
 #endif
-#ifndef SVLA_ROPE_TR
-#define SVLA_ROPE_TR 1             // ... gathers by transposing LDS reads
-#endif
 #ifndef SVLA_ROPE_WGS
 #define SVLA_ROPE_WGS 2048         // ... (and fp32 builds): workgroups wanted per launch
 #endif
 #ifndef SVLA_MIN_SPLIT_PER_D
 #define SVLA_MIN_SPLIT_PER_D 8     // tokens per build workgroup and block >= this * d
-#endif
-#ifndef SVLA_SCAN_LA
-#define SVLA_SCAN_LA 16            // partial-state loads in flight per scan thread
 #endif
 #ifndef SVLA_APPLY_TILE32
 #define SVLA_APPLY_TILE32 256      // apply: tokens per workgroup for bf16 d = 32 and fp32 d = 32, 64
@@ -1007,10 +1001,10 @@ svla_state_build_dma(const BuildArgs a)
 // the rotation and the bf16 hi/lo split to its K chunks (one token, 8
 // features per lane), writes the stage into an LDS slot of its own and
 // contracts it from there on v_mfma_f32_32x32x16_bf16, which sums over
-// tokens: each lane gathers 8 tokens of one feature from the slot rows
-// (lanes 32-63 take the odd tokens so the two half-waves read disjoint
-// banks); the hi and lo parts make two MFMAs, so the state keeps about 16
-// bits of the rotated key.  z sums the unrotated phi(k) on the vector ALU.
+// tokens: each lane takes 8 tokens of one feature from the slot rows with
+// two transposing reads (ds_read_b64_tr_b16, see trb_offset); the hi and lo
+// parts make two MFMAs, so the state keeps about 16 bits of the rotated
+// key.  z sums the unrotated phi(k) on the vector ALU.
 // No wave reads another wave's slot, and the LDS operations of one wave
 // execute in program order, so the main loop needs no barrier and the slot
 // can be overwritten by the next stage right after it was read.  Every wave
@@ -1114,16 +1108,10 @@ svla_state_build_rope(const BuildArgs a)
     for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
 
     const int m = lane & 31, g = lane >> 5;
-    // lane part of a fragment element's LDS index: k-slot i of group gi reads
-    // row 16 gi + g + 2 i; the row's parity (= g) fixes the swizzle.  With
-    // transposing reads: the lane's byte offsets within a 16-token group.
-    constexpr bool TR = SVLA_ROPE_TR != 0;
+    // the lane's byte offsets of its transposing reads within a 16-token group
     int fl[TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int f = 32 * t + m;
-        fl[t] = TR ? trb_offset<D>(lane, 32 * t) : g * D + swz16<D>(g, f >> 3) * 8 + (f & 7);
-    }
+    for (int t = 0; t < TPW; ++t) fl[t] = trb_offset<D>(lane, 32 * t);
 
     // The loop is kept regular so the compiler can count the loads in flight:
     // the stage count is rounded up to a multiple of PF (the extra stages
@@ -1168,30 +1156,14 @@ svla_state_build_rope(const BuildArgs a)
                 vreg[p][u] = load16p<SVLA_KV_AUX>(rV, offset(i + PF, u, vcol));
             }
             __builtin_amdgcn_sched_barrier(0);
-            const unsigned short *Kh = (const unsigned short *)slot;
-            const unsigned short *Kl = (const unsigned short *)(slot + TILEB);
-            const unsigned short *Vs = (const unsigned short *)(slot + NK * TILEB);
 #pragma unroll
             for (int gi = 0; gi < GPW; ++gi) {
                 bf16x8_t av[TPW], al[TPW], bv[TPW];
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
-                    if constexpr (TR) {
-                        av[t] = trb_load<D>(slot + 16 * gi * ROWB, fl[t]);
-                        al[t] = trb_load<D>(slot + TILEB + 16 * gi * ROWB, fl[t]);
-                        bv[t] = trb_load<D>(slot + NK * TILEB + 16 * gi * ROWB, fl[t]);
-                    } else {
-                        u16x8_t x, y, w;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            x[e] = Kh[16 * gi * D + fl[t] + 2 * e * D];
-                            y[e] = Kl[16 * gi * D + fl[t] + 2 * e * D];
-                            w[e] = Vs[16 * gi * D + fl[t] + 2 * e * D];
-                        }
-                        av[t] = __builtin_bit_cast(bf16x8_t, x);
-                        al[t] = __builtin_bit_cast(bf16x8_t, y);
-                        bv[t] = __builtin_bit_cast(bf16x8_t, w);
-                    }
+                    av[t] = trb_load<D>(slot + 16 * gi * ROWB, fl[t]);
+                    al[t] = trb_load<D>(slot + TILEB + 16 * gi * ROWB, fl[t]);
+                    bv[t] = trb_load<D>(slot + NK * TILEB + 16 * gi * ROWB, fl[t]);
                 }
 #pragma unroll
                 for (int tm = 0; tm < TPW; ++tm)
