@@ -54,6 +54,9 @@
 #ifndef SVLA_DMA_R128
 #define SVLA_DMA_R128 3            // ... and for d = 128
 #endif
+#ifndef SVLA_MIN_SPLIT_ROPE
+#define SVLA_MIN_SPLIT_ROPE 5      // builds with RoPE: tokens per split >= this * d
+#endif
 #ifndef SVLA_MIN_SPLIT_128
 #define SVLA_MIN_SPLIT_128 4       // d = 128 build without RoPE: tokens per split >= this * d
 #endif
@@ -123,6 +126,7 @@ namespace {
 
 constexpr int kThreads = 256;                 // build and apply: 4 waves of 64
 constexpr int kFoldMaxParts = 6;              // partials a scan folded into the apply sums at most
+constexpr int kFoldMaxPartsRope = 8;          // ... with RoPE (block steps cut into more splits)
 constexpr int kScanLongChain = 16;            // scan: blocks from which the chain is cut four ways
 constexpr uint32_t kOOB = 0x80000000u;        // an offset past every resource
 constexpr int kMaxRopeEntries = 4096;         // (cos, sin) pairs per workgroup
@@ -1396,7 +1400,7 @@ svla_apply_bf16(const ApplyArgs a)
     constexpr int MT = D / 16;
     constexpr int KS = D / 32;
     constexpr int PF = ROPE ? SVLA_APPLY32_PF_ROPE : SVLA_APPLY32_PF;
-    constexpr int MAXP = kFoldMaxParts;
+    constexpr int MAXP = ROPE ? kFoldMaxPartsRope : kFoldMaxParts;
     static_assert(D == 32, "laid out for d = 32");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -2136,7 +2140,13 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     int chunk_dma = 0, chunk_other = 0;
     const int splits_dma = pick_splits(units, n, d, SVLA_DMA_WGS, &chunk_dma,
                                        d == 128 ? SVLA_MIN_SPLIT_128 : SVLA_MIN_SPLIT_PER_D);
-    const int splits_other = pick_splits(units, n, d, SVLA_ROPE_WGS, &chunk_other);
+    // (the RoPE builds take shorter splits; the workspace holds either plan's
+    // partials, since its size must not depend on RoPE)
+    int chunk_rope = 0;
+    const int splits_plain = pick_splits(units, n, d, SVLA_ROPE_WGS, &chunk_other);
+    const int splits_rope = pick_splits(units, n, d, SVLA_ROPE_WGS, &chunk_rope, SVLA_MIN_SPLIT_ROPE);
+    const int splits_other = p->rope.on ? splits_rope : splits_plain;
+    if (p->rope.on) chunk_other = chunk_rope;
     if (op == SVLA_OP_STATE_BUILD) {
         // one workgroup per block: its partial is the block's local state
         p->splits = n > 0 ? 1 : 0;
@@ -2146,7 +2156,8 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
         p->chunk = p->dma ? chunk_dma : chunk_other;
     }
     p->fold = (op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP) &&
-              p->esize == 2 && d == 32 && nb == 1 && n > 0 && p->splits + 1 <= kFoldMaxParts;
+              p->esize == 2 && d == 32 && nb == 1 && n > 0 &&
+              p->splits + 1 <= (p->rope.on ? kFoldMaxPartsRope : kFoldMaxParts);
     p->tile = (p->esize == 2 && d >= 64) ? SVLA_APPLY_TILE_LDS
               : d == 128 ? SVLA_APPLY_TILE128
               : p->rope.on ? SVLA_APPLY_TILE_ROPE : p->fold ? SVLA_APPLY_TILE_FOLD : SVLA_APPLY_TILE32;
@@ -2191,7 +2202,9 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     if (fused) {
         // (+ 1: a one-block call whose scan is folded into the apply keeps
         // the carried state there)
-        const size_t slots = (size_t)(splits_dma > splits_other ? splits_dma : splits_other) + 1;
+        int most = splits_dma > splits_plain ? splits_dma : splits_plain;
+        if (splits_rope > most) most = splits_rope;
+        const size_t slots = (size_t)most + 1;
         p->off_spart = off; off = align256(off + (size_t)units * slots * d * d * 4);
         p->off_zpart = off; off = align256(off + (size_t)units * slots * d * 4);
     }
@@ -2217,7 +2230,7 @@ void launch_build(const Plan &p, const BuildArgs &args, hipStream_t s)
     a.chunk = p.chunk;
     a.slots = p.splits + (a.S_in ? 1 : 0);
     const unsigned grid = (unsigned)(p.BH * p.nb * p.splits);
-    const unsigned qgrid = (unsigned)((grid + 7) / 8 * 8 * 4);   // d = 128: four quadrants
+    const unsigned qgrid = (unsigned)((grid + 7) / 8 * 8 * 4);   // RoPE build at d = 128: four quadrants
     char nm[96];
     if (p.dma) {
         constexpr int U = D == 32 ? SVLA_DMA_U32 : SVLA_DMA_U;
