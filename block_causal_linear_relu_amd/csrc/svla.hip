@@ -78,6 +78,9 @@
 #ifndef SVLA_APPLY_TILE_FOLD
 #define SVLA_APPLY_TILE_FOLD 512   // ... bf16 d = 32 with the scan folded in (one-block calls)
 #endif
+#ifndef SVLA_APPLY_TILE_FOLD_ROPE
+#define SVLA_APPLY_TILE_FOLD_ROPE 192   // ... and with RoPE (latency-bound block steps: more workgroups)
+#endif
 #ifndef SVLA_APPLY_TILE_ROPE
 #define SVLA_APPLY_TILE_ROPE 512   // ... with RoPE (amortises the per-workgroup angle table)
 #endif
@@ -2160,7 +2163,8 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
               p->splits + 1 <= (p->rope.on ? kFoldMaxPartsRope : kFoldMaxParts);
     p->tile = (p->esize == 2 && d >= 64) ? SVLA_APPLY_TILE_LDS
               : d == 128 ? SVLA_APPLY_TILE128
-              : p->rope.on ? SVLA_APPLY_TILE_ROPE : p->fold ? SVLA_APPLY_TILE_FOLD : SVLA_APPLY_TILE32;
+              : p->rope.on ? (p->fold ? SVLA_APPLY_TILE_FOLD_ROPE : SVLA_APPLY_TILE_ROPE)
+              : p->fold ? SVLA_APPLY_TILE_FOLD : SVLA_APPLY_TILE32;
     p->tiles = n > 0 ? (n + p->tile - 1) / p->tile : 0;
 
     // dynamic LDS: [RoPE table][stage buffers | epilogue] (the direct-to-LDS
