@@ -61,10 +61,10 @@
 #define SVLA_MIN_SPLIT_128 4       // d = 128 build without RoPE: tokens per split >= this * d
 #endif
 #ifndef SVLA_ROPE_PF
-#define SVLA_ROPE_PF 2             // state build with RoPE: stages in flight per wave
+#define SVLA_ROPE_PF 3             // state build with RoPE: stages in flight per wave
 #endif
 #ifndef SVLA_ROPE_U
-#define SVLA_ROPE_U 2              // ... 16-byte loads per lane per tensor per stage
+#define SVLA_ROPE_U 1              // ... 16-byte loads per lane per tensor per stage (2 at d >= 64)
 #endif
 #ifndef SVLA_ROPE_WGS
 #define SVLA_ROPE_WGS 2048         // ... (and fp32 builds): workgroups wanted per launch
