@@ -373,8 +373,8 @@ def main():
         summarize_counters(*args.summarize_counters, config=args.config)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the path shards by (batch, head) "
-              "with no communication; see the design notes); --gpus %d is not supported"
+        print("bench.py: measures one GPU only (the path shards by (batch, head) with no "
+              "communication, so N GPUs run N independent calls); --gpus %d is not supported"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
