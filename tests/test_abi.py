@@ -141,3 +141,32 @@ def test_other_entry_points_validate(lib):
     assert lib.svla_state_scan(1, 2, 2, 32, MIS, A, None, None, None, A, A, None) == 4
     assert lib.svla_apply(_lib.SVLA_BF16, 1, 2, 2, 64, 32, A, A, A, None, 1e-6, A2, A, 8,
                           None) == 6
+
+
+def test_workspace_covers_every_plan():
+    """svla_workspace_size takes no RoPE argument, so the workspace it gives
+    must hold the partials of whichever build the call picks, RoPE or not;
+    the plan the library describes (svla_describe, host logic only) must fit."""
+    import torch
+    import block_causal_linear_relu_amd as svla
+    from workloads import Rope
+    shapes = [
+        ("block_step", 1, 70, 1, 1170, 32), ("block_causal", 1, 70, 80, 1170, 32),
+        ("noncausal", 2, 70, 1, 8190, 32), ("block_causal", 1, 70, 7, 2640, 32),
+        ("block_causal", 1, 20, 8, 1760, 128), ("block_step", 1, 20, 1, 1760, 128),
+        ("block_causal", 1, 3, 3, 333, 32), ("block_step", 2, 5, 1, 77, 64),
+        ("block_causal", 1, 40, 30, 37, 32),
+    ]
+    for op, B, H, nb, n, d in shapes:
+        ws = svla.workspace_size(op, torch.bfloat16, B, H, nb, n, d)
+        rope = Rope(8, 12, 12, 5, 7, 3, 1e4)
+        plain = svla.describe(op, torch.bfloat16, B, H, nb, n, d)
+        rot = svla.describe(op, torch.bfloat16, B, H, nb, n, d, rope=rope)
+        assert plain["workspace"] == ws and rot["workspace"] == ws, (op, B, H, nb, n, d)
+        # one-block bf16 d = 32 calls fold the scan into the apply (with RoPE
+        # as long as the block's splits fit the apply's partial count: the
+        # minute-long block step does)
+        if nb == 1 and d == 32:
+            assert [k["slot"] for k in plain["kernels"]] == ["build", "apply"]
+            if op == "block_step" and n == 1170:
+                assert [k["slot"] for k in rot["kernels"]] == ["build", "apply"]
