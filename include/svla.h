@@ -118,8 +118,9 @@ const char *svla_status_string(svla_status s);    /* static string */
 const char *svla_last_error(void);                /* thread-local; "" if none */
 
 /* Bytes of workspace the call `op` needs for these sizes (nb = 1 for the
- * non-causal call and the block step; N = nb*n).  *bytes is written on
- * SVLA_OK only. */
+ * non-causal call and the block step; N = nb*n), with or without RoPE and
+ * a gate (the size covers every launch plan the call can pick).  *bytes is
+ * written on SVLA_OK only. */
 svla_status svla_workspace_size(svla_op op, svla_dtype dt, int B, int H,
                                 int nb, int n, int d, size_t *bytes);
 
