@@ -123,7 +123,9 @@ def test_noncausal_entry_point(svla):
 
 @pytest.mark.parametrize("dtype,d,rope", [("bf16", 32, Rope(8, 12, 12, 5, 7, 3, 1e4)),
                                           ("bf16", 128, None), ("f32", 64, None),
-                                          ("bf16", 64, Rope(16, 24, 24, 4, 9, 0, 1e4))])
+                                          ("bf16", 64, Rope(16, 24, 24, 4, 9, 0, 1e4)),
+                                          ("bf16", 32, None), ("bf16", 64, None),
+                                          ("bf16", 128, Rope(32, 48, 48, 4, 9, 1, 1e4))])
 def test_state_build(svla, dtype, d, rope):
     x = _small(dtype, 1, 2, 3, 211, d)
     dt = _tdt(x)
@@ -168,15 +170,18 @@ def test_apply(svla, dtype, d, rope):
 
 # --- streaming steps ------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,gate,d", [("f32", False, 32), ("bf16", True, 32), ("bf16", False, 32),
-                                          ("bf16", True, 128), ("bf16", False, 64)])
-def test_chained_steps_equal_one_shot(svla, dtype, gate, d):
+@pytest.mark.parametrize("dtype,gate,d,with_rope", [
+    ("f32", False, 32, True), ("bf16", True, 32, True), ("bf16", False, 32, True),
+    ("bf16", True, 128, True), ("bf16", False, 64, True),
+    ("bf16", True, 32, False), ("bf16", True, 64, False), ("bf16", False, 128, False),
+    ("f32", True, 128, False)])
+def test_chained_steps_equal_one_shot(svla, dtype, gate, d, with_rope):
     """nb block steps with the state carried == the one-shot call (and the oracle)."""
     gh, gw, frames = 5, 6, 2
     n = frames * gh * gw
     nb = 6
     x = _small(dtype, 1, 3, nb, n, d)
-    rope = Rope(8, 12, 12, gh, gw, 0, 1e4)
+    rope = Rope(8, 12, 12, gh, gw, 0, 1e4) if with_rope else None
     rng = np.random.default_rng(3)
     g = rng.uniform(0.5, 1.0, (1, 3, nb)).astype(np.float32) if gate else None
     dt = _tdt(x)
@@ -191,7 +196,7 @@ def test_chained_steps_equal_one_shot(svla, dtype, gate, d):
         gs = None if g is None else gt[:, :, s].contiguous()
         O, S, z = svla.block_step(Q[:, :, sl].contiguous(), K[:, :, sl].contiguous(),
                                   V[:, :, sl].contiguous(), S, z, S_out=S, z_out=z, g=gs,
-                                  rope=Rope(8, 12, 12, gh, gw, frames * s, 1e4))
+                                  rope=Rope(8, 12, 12, gh, gw, frames * s, 1e4) if with_rope else None)
         outs.append(O)
     Oc = torch.cat(outs, dim=2)
     torch.cuda.synchronize()
