@@ -322,3 +322,49 @@ def test_full_size_c4_streaming_and_one_shot(svla):
     ref = oracle.forward(sub(x["Q"]), sub(x["K"]), sub(x["V"]), nb, rope=cfg.rope, eps=x["eps"])
     eo, es, ez = _check(x, (_np(Oc), S.cpu().numpy(), z.cpu().numpy()), ref, heads=hs)
     print("c4 sampled heads %s: O %.2e S %.2e z %.2e" % (hs, eo, es, ez))
+
+
+def test_largest_slice(svla):
+    """The largest call the size check admits at d = 32, bf16: two blocks of
+    2^24 - 1 tokens per (b,h), so one slice is 128 bytes short of 2 GiB and the
+    second head's slice starts 2 GiB into each tensor.  The inputs are sparse:
+    zero rows of K and V add nothing to the state and a zero query gives a zero
+    output, so the rows that are set (at both ends of every block, the slice's
+    last token among them, and random rows between) form a small dense problem
+    with the same block structure, which the oracle solves."""
+    B, H, nb, d = 1, 2, 2, 32
+    n = (1 << 24) - 1
+    N = nb * n
+    assert nb * n * d * 2 < (1 << 31) <= nb * (n + 1) * d * 2
+    rng = np.random.default_rng(29)
+    rows = []
+    for b in range(nb):
+        inner = rng.choice(np.arange(b * n + 1, (b + 1) * n - 1), size=62, replace=False)
+        rows.append(np.sort(np.concatenate([[b * n], inner, [(b + 1) * n - 1]])))
+    m = max(len(r) for r in rows)
+    vals = {k: torch.from_numpy(rng.standard_normal((B, H, nb * m, d)).astype(np.float32))
+            .to(torch.bfloat16) for k in "QKV"}
+    g = rng.uniform(0.5, 1.0, (B, H, nb)).astype(np.float32)
+
+    big = {k: torch.zeros((B, H, N, d), dtype=torch.bfloat16, device=DEV) for k in "QKV"}
+    for b in range(nb):
+        idx = torch.from_numpy(rows[b]).to(DEV)
+        for k in "QKV":
+            big[k][:, :, idx] = vals[k][:, :, b * m:b * m + len(rows[b])].to(DEV)
+    O, S, z = svla.block_causal(big["Q"], big["K"], big["V"], nb, g=_t(g, torch.float32),
+                                return_state=True)
+    torch.cuda.synchronize()
+    del big
+
+    ref = oracle.forward(vals["Q"].float().numpy(), vals["K"].float().numpy(),
+                         vals["V"].float().numpy(), nb, g=g)
+    got = np.concatenate([_np(O[:, :, torch.from_numpy(rows[b]).to(DEV)]) for b in range(nb)], axis=2)
+    want = np.concatenate([ref["O"][:, :, b * m:b * m + len(rows[b])] for b in range(nb)], axis=2)
+    eo = nerr(got, want)
+    es, ez = nerr(S.cpu().numpy(), ref["S"]), nerr(z.cpu().numpy(), ref["z"])
+    assert eo <= TOL_O["bf16"] and es <= TOL_S and ez <= TOL_S, (eo, es, ez)
+    # rows whose query is zero, sampled across the slice (the last rows included)
+    zero = np.setdiff1d(np.concatenate([rng.integers(0, N, 4000), np.arange(N - 200, N)]),
+                        np.concatenate(rows))
+    assert torch.count_nonzero(O[:, :, torch.from_numpy(zero).to(DEV)]).item() == 0
+    print("largest slice: O %.2e S %.2e z %.2e" % (eo, es, ez))
