@@ -324,29 +324,32 @@ def test_full_size_c4_streaming_and_one_shot(svla):
     print("c4 sampled heads %s: O %.2e S %.2e z %.2e" % (hs, eo, es, ez))
 
 
-def test_largest_slice(svla):
-    """The largest call the size check admits at d = 32, bf16: two blocks of
-    2^24 - 1 tokens per (b,h), so one slice is 128 bytes short of 2 GiB and the
-    second head's slice starts 2 GiB into each tensor.  The inputs are sparse:
-    zero rows of K and V add nothing to the state and a zero query gives a zero
-    output, so the rows that are set (at both ends of every block, the slice's
-    last token among them, and random rows between) form a small dense problem
-    with the same block structure, which the oracle solves."""
-    B, H, nb, d = 1, 2, 2, 32
-    n = (1 << 24) - 1
+@pytest.mark.parametrize("dtype,d", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 128)])
+def test_largest_slice(svla, dtype, d):
+    """The largest call the size check admits: two blocks of 2^k - 1 tokens per
+    (b,h), so one slice is two rows short of 2 GiB and the second head's
+    slice starts 2 GiB into each tensor.  The inputs are sparse: zero rows of K
+    and V add nothing to the state and a zero query gives a zero output, so the
+    rows that are set (at both ends of every block, the slice's last token
+    among them, and random rows between) form a small dense problem with the
+    same block structure, which the oracle solves."""
+    B, H, nb = 1, 2, 2
+    es = 2 if dtype == "bf16" else 4
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    n = (1 << 31) // (nb * d * es) - 1
     N = nb * n
-    assert nb * n * d * 2 < (1 << 31) <= nb * (n + 1) * d * 2
+    assert nb * n * d * es < (1 << 31) <= nb * (n + 1) * d * es
     rng = np.random.default_rng(29)
     rows = []
     for b in range(nb):
         inner = rng.choice(np.arange(b * n + 1, (b + 1) * n - 1), size=62, replace=False)
         rows.append(np.sort(np.concatenate([[b * n], inner, [(b + 1) * n - 1]])))
     m = max(len(r) for r in rows)
-    vals = {k: torch.from_numpy(rng.standard_normal((B, H, nb * m, d)).astype(np.float32))
-            .to(torch.bfloat16) for k in "QKV"}
+    vals = {k: torch.from_numpy(rng.standard_normal((B, H, nb * m, d)).astype(np.float32)).to(tdt)
+            for k in "QKV"}
     g = rng.uniform(0.5, 1.0, (B, H, nb)).astype(np.float32)
 
-    big = {k: torch.zeros((B, H, N, d), dtype=torch.bfloat16, device=DEV) for k in "QKV"}
+    big = {k: torch.zeros((B, H, N, d), dtype=tdt, device=DEV) for k in "QKV"}
     for b in range(nb):
         idx = torch.from_numpy(rows[b]).to(DEV)
         for k in "QKV":
@@ -361,10 +364,10 @@ def test_largest_slice(svla):
     got = np.concatenate([_np(O[:, :, torch.from_numpy(rows[b]).to(DEV)]) for b in range(nb)], axis=2)
     want = np.concatenate([ref["O"][:, :, b * m:b * m + len(rows[b])] for b in range(nb)], axis=2)
     eo = nerr(got, want)
-    es, ez = nerr(S.cpu().numpy(), ref["S"]), nerr(z.cpu().numpy(), ref["z"])
-    assert eo <= TOL_O["bf16"] and es <= TOL_S and ez <= TOL_S, (eo, es, ez)
+    es_, ez = nerr(S.cpu().numpy(), ref["S"]), nerr(z.cpu().numpy(), ref["z"])
+    assert eo <= TOL_O[dtype] and es_ <= TOL_S and ez <= TOL_S, (eo, es_, ez)
     # rows whose query is zero, sampled across the slice (the last rows included)
     zero = np.setdiff1d(np.concatenate([rng.integers(0, N, 4000), np.arange(N - 200, N)]),
                         np.concatenate(rows))
     assert torch.count_nonzero(O[:, :, torch.from_numpy(zero).to(DEV)]).item() == 0
-    print("largest slice: O %.2e S %.2e z %.2e" % (eo, es, ez))
+    print("largest slice %s d=%d: O %.2e S %.2e z %.2e" % (dtype, d, eo, es_, ez))
