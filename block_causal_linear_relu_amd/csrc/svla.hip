@@ -1183,6 +1183,52 @@ svla_state_build_rope(const BuildArgs a)
         }
     }
 
+    if constexpr (D == 32 && !QUAD) {
+        // ---- epilogue (d = 32): each wave's tile in an LDS region of its
+        // own, then every thread sums four values in wave order (the same
+        // order as the pass-by-pass sum below); z is summed within each wave
+        // over the 16 lanes that share a chunk, then over the waves
+        float *red = (float *)(lds + a.rope.tab_bytes);            // 4 x D x D floats
+        float *zw = red + 4 * D * D;                               // 4 x D floats
+        __syncthreads();          // every wave is done with its slot
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            red[wave * D * D + (8 * (r >> 2) + 4 * g + (r & 3)) * D + m] = acc[0][0][r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = zacc[e];
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 8);
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            zacc[e] = v;
+        }
+        if (lane < CPR) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zw[wave * D + lane * 8 + e] = zacc[e];
+        }
+        __syncthreads();
+        static_assert(D * D == 4 * kThreads, "four values per thread");
+        const long unit = (bh * a.nb + c) * a.slots + s;
+        const auto rS = make_rsrc(a.S_part + unit * DG * DG, DG * DG * 4);
+        const auto rz = make_rsrc(a.z_part + unit * DG, DG * 4);
+        const int e0 = tid * 4;
+        float t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = red[e0 + i];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] += red[w * D * D + e0 + i];
+        u32x4_t out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = as_u32(t[i]);
+        store16(rS, (uint32_t)e0 * 4u, out);
+        if (tid < D) store4(rz, (uint32_t)tid * 4u, ((zw[tid] + zw[D + tid]) + zw[2 * D + tid]) + zw[3 * D + tid]);
+        if (a.S_in && s == 0) carry_in(a, bh, D);
+        return;
+    }
+
     // ---- epilogue: the four waves' tiles summed in wave order, then
     // S_part (row-major [k][v], row stride DG) and z_part
     float *red = (float *)(lds + a.rope.tab_bytes);                // D x D floats
@@ -2172,7 +2218,8 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     if (p->esize == 2) {
         const int td = d == 128 ? 64 : d;                 // tile side (quadrants for d = 128)
         const size_t slots = (size_t)4 * 3 * rope_tokens(d) * td * 2;
-        const size_t epi = ((size_t)td * td + td + 2048) * 4;
+        const size_t epi = td == 32 && p->rope.on ? ((size_t)4 * td * td + 4 * td) * 4   // one-pass epilogue
+                                                  : ((size_t)td * td + td + 2048) * 4;
         p->lds_build = p->dma ? 0 : (slots > epi ? slots : epi);
     } else {
         const size_t stage = (size_t)2 * 2 * 4096;
