@@ -371,3 +371,54 @@ def test_largest_slice(svla, dtype, d):
                         np.concatenate(rows))
     assert torch.count_nonzero(O[:, :, torch.from_numpy(zero).to(DEV)]).item() == 0
     print("largest slice %s d=%d: O %.2e S %.2e z %.2e" % (dtype, d, eo, es_, ez))
+
+
+@pytest.mark.parametrize("d,with_rope,gate", [(32, True, False), (64, False, True)])
+def test_graph_replay_matches_eager(svla, d, with_rope, gate):
+    """A pass of block steps captured in a HIP graph, as a streaming caller
+    replays it: every replay, with eager work and a synchronization between
+    replays, gives the eager pass's outputs and final state bit for bit."""
+    gh, gw, frames, nb, H = 5, 6, 2, 5, 3
+    n = frames * gh * gw
+    x = _small("bf16", 1, H, nb, n, d, seed=13)
+    Q, K, V = (_t(x[k], torch.bfloat16) for k in "QKV")
+    steps = [tuple(t[:, :, s * n:(s + 1) * n].contiguous() for t in (Q, K, V)) for s in range(nb)]
+    rng = np.random.default_rng(17)
+    gs = ([_t(rng.uniform(0.5, 1.0, (1, H)).astype(np.float32), torch.float32) for _ in range(nb)]
+          if gate else [None] * nb)
+    ropes = [Rope(8, 12, 12, gh, gw, frames * s, 1e4) if with_rope else None for s in range(nb)]
+    S = torch.zeros((1, H, d, d), device=DEV)
+    z = torch.zeros((1, H, d), device=DEV)
+    outs = [torch.empty_like(steps[0][0]) for _ in range(nb)]
+    ws = torch.empty(svla.workspace_size("block_step", torch.bfloat16, 1, H, 1, n, d),
+                     dtype=torch.uint8, device=DEV)
+
+    def run_pass():
+        for s in range(nb):
+            svla.block_step(*steps[s], S if s else None, z if s else None, S_out=S, z_out=z,
+                            g=gs[s], rope=ropes[s], out=outs[s], workspace=ws)
+
+    run_pass()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs] + [S.clone(), z.clone()]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_pass()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        S.fill_(float("nan"))
+        z.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = outs + [S, z]
+        assert all(torch.equal(a, b) for a, b in zip(got, want)), "replay %d differs" % rep
