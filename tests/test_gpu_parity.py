@@ -422,3 +422,26 @@ def test_graph_replay_matches_eager(svla, d, with_rope, gate):
         torch.cuda.synchronize()
         got = outs + [S, z]
         assert all(torch.equal(a, b) for a, b in zip(got, want)), "replay %d differs" % rep
+
+
+def test_side_stream_matches_default_stream(svla):
+    """Every call launches on the caller's current stream: the same calls on a
+    side stream, with inputs produced on that stream, give the same bits."""
+    x = _small("bf16", 1, 4, 3, 330, 32, seed=19)
+    rope = Rope(8, 12, 12, 5, 6, 0, 1e4)
+    Q, K, V = (_t(x[k], torch.bfloat16) for k in "QKV")
+    ref = svla.block_causal(Q, K, V, 3, rope=rope, return_state=True)
+    S0 = torch.randn((1, 4, 32, 32), device=DEV)
+    z0 = torch.rand((1, 4, 32), device=DEV) * 10
+    ref_step = svla.block_step(Q[:, :, :330].contiguous(), K[:, :, :330].contiguous(),
+                               V[:, :, :330].contiguous(), S0, z0, rope=rope)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        Q2, K2, V2 = (t * 1 for t in (Q, K, V))      # produced on the side stream
+        got = svla.block_causal(Q2, K2, V2, 3, rope=rope, return_state=True)
+        got_step = svla.block_step(Q2[:, :, :330].contiguous(), K2[:, :, :330].contiguous(),
+                                   V2[:, :, :330].contiguous(), S0, z0, rope=rope)
+    side.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(got, ref))
+    assert all(torch.equal(a, b) for a, b in zip(got_step, ref_step))
