@@ -352,3 +352,118 @@ def test_generator_is_seeded_and_bf16_exact():
     assert np.all((a["K"].view(np.uint32) & 0xFFFF) == 0)
     g = make_inputs(CONFIGS["c5"], nb=8, n=4, H=2)["g"]
     assert g.shape == (1, 2, 8) and np.all((g > 0) & (g < 1))
+
+
+# --- the error measure behind every parity assertion -------------------------
+# normwise_error(x, ref): per (b,h) slice, max|x - ref| / max|ref| (the scale
+# taken from the reference), then the largest slice value.  Each case below has
+# an answer worked out by hand that a plausible slip in the measure (one global
+# scale, a mean, a scale from the result) gets wrong.
+
+def test_normwise_error_scale_is_per_slice():
+    """Two slices whose scales differ by 12000x, the error in the small one:
+    a per-slice measure reports 0.25; one global scale would report 0.25/12000."""
+    ref = np.zeros((1, 2, 4, 3))
+    ref[0, 0] = 1000.0 * np.arange(1, 13).reshape(4, 3)      # max |ref| = 12000
+    ref[0, 1] = np.arange(1, 13).reshape(4, 3) / 12.0        # max |ref| = 1
+    x = ref.copy()
+    x[0, 1, 2, 1] += 0.25
+    assert normwise_error(x, ref) == pytest.approx(0.25, rel=1e-12)
+    # the same error in the large slice is small at that slice's scale
+    y = ref.copy()
+    y[0, 0, 2, 1] += 0.25
+    assert normwise_error(y, ref) == pytest.approx(0.25 / 12000.0, rel=1e-12)
+
+
+def test_normwise_error_is_a_max_not_a_mean():
+    """One element of eight off by 0.5 at scale 1: 0.5 (a mean would give 0.0625);
+    two slices at 0.1 and 0.3: 0.3 (a mean over slices would give 0.2)."""
+    ref = np.ones((1, 1, 8, 1))
+    x = ref.copy()
+    x[0, 0, 3, 0] = 1.5
+    assert normwise_error(x, ref) == 0.5
+    ref2 = np.ones((2, 1, 5, 2))
+    x2 = ref2.copy()
+    x2[0, 0, 1, 1] += 0.1
+    x2[1, 0, 4, 0] -= 0.3
+    assert normwise_error(x2, ref2) == pytest.approx(0.3, rel=1e-12)
+
+
+def test_normwise_error_scale_comes_from_the_reference():
+    """ref max 1, x max 3: error (3 - 1) / 1 = 2, not (3 - 1) / 3; the measure is
+    not symmetric in its arguments."""
+    ref = np.ones((1, 1, 4, 1))
+    x = ref.copy()
+    x[0, 0, 0, 0] = 3.0
+    assert normwise_error(x, ref) == 2.0
+    assert normwise_error(ref, x) == pytest.approx(2.0 / 3.0, rel=1e-15)
+
+
+def test_normwise_error_zero_reference_and_non_finite():
+    """A slice whose reference is all zero is measured by its absolute error
+    (zero when the result is zero too); any NaN or inf in the result is inf."""
+    ref = np.zeros((1, 2, 3, 2))
+    ref[0, 0] = 2.0
+    assert normwise_error(ref.copy(), ref) == 0.0
+    x = ref.copy()
+    x[0, 1, 1, 1] = -1e-3
+    assert normwise_error(x, ref) == pytest.approx(1e-3, rel=1e-15)
+    for bad in (np.nan, np.inf, -np.inf):
+        y = ref.copy()
+        y[0, 0, 2, 0] = bad
+        assert normwise_error(y, ref) == float("inf")
+    with pytest.raises(ValueError):
+        normwise_error(np.zeros((1, 1, 2)), np.zeros((1, 1, 3)))
+
+
+def test_normwise_error_is_scale_invariant():
+    rng = np.random.default_rng(21)
+    ref = rng.standard_normal((2, 3, 10, 4))
+    x = ref + 1e-3 * rng.standard_normal(ref.shape)
+    e = normwise_error(x, ref)
+    assert 1e-4 < e < 1e-2
+    assert normwise_error(1024.0 * x, 1024.0 * ref) == pytest.approx(e, rel=1e-12)
+
+
+# --- the per-block states the per-kernel parity tests compare against ----------
+
+@pytest.mark.parametrize("variant", ["plain", "gate", "gate_state_in", "rope"])
+def test_block_states_are_the_states_of_truncated_calls(variant):
+    """Exported block state c (inclusive) == the final state of the same call
+    cut after block c; the last one == the call's final state.  Exported local
+    state c == phi(K_c)^T V_c (rotated keys with RoPE) and sum phi(K_c), by
+    matrix products and the brute force's own rotation."""
+    nb, n, d = 5, 12, 32
+    Q, K, V = _tiny(31, N=nb * n)
+    rng = np.random.default_rng(32)
+    g = rng.uniform(0.2, 0.9, (1, 2, nb)) if "gate" in variant else None
+    S0 = z0 = None
+    if "state_in" in variant:
+        S0 = rng.standard_normal((1, 2, d, d)) * 5
+        z0 = np.abs(rng.standard_normal((1, 2, d))) * 20
+    rope = Rope(8, 12, 12, 2, 3, 4, 10000.0) if variant == "rope" else None
+    full = oracle.forward(Q, K, V, nb, g=g, rope=rope, S0=S0, z0=z0, want_blocks=True,
+                          want_local=True)
+    for c in range(nb):
+        cut = slice(0, (c + 1) * n)
+        part = oracle.forward(Q[:, :, cut], K[:, :, cut], V[:, :, cut], c + 1,
+                              g=None if g is None else g[:, :, :c + 1], rope=rope,
+                              S0=S0, z0=z0)
+        assert normwise_error(full["S_blocks"][:, :, c], part["S"]) < 1e-14
+        assert normwise_error(full["z_blocks"][:, :, c], part["z"]) < 1e-14
+        blk = slice(c * n, (c + 1) * n)
+        A = np.maximum(K[:, :, blk], 0.0)
+        if rope is None:
+            Ar = A
+        else:
+            # the brute force rotates call tokens 0 .. N-1: block c's keys sit at c*n ..
+            padded = np.concatenate([np.zeros((1, 2, c * n, d)), A], axis=2)
+            Ar = np.stack([oracle.rope_apply(padded[0, h], rope, d)[c * n:] for h in range(2)])[None]
+        assert normwise_error(full["S_local"][:, :, c], np.swapaxes(Ar, -1, -2) @ V[:, :, blk]) < 1e-13
+        assert normwise_error(full["z_local"][:, :, c], A.sum(axis=2)) < 1e-14
+    assert np.array_equal(full["S_blocks"][:, :, -1], full["S"])
+    assert np.array_equal(full["z_blocks"][:, :, -1], full["z"])
+    if nb > 1 and g is not None:
+        # inclusive, decayed: block 1 = g_1 * block 0 + local 1
+        want = g[:, :, 1, None, None] * full["S_blocks"][:, :, 0] + full["S_local"][:, :, 1]
+        assert normwise_error(full["S_blocks"][:, :, 1], want) < 1e-14
