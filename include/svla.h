@@ -11,13 +11,14 @@
  *     block's KV contribution (ICLR 2026 oral talk, "block KV cache"
  *     review; abstract, design (2) "Constant-Memory KV cache");
  *   - video is generated block by block, causally across blocks and
- *     bidirectionally inside a block (talk, "block by block causally and
- *     diffuse within the block");
+ *     bidirectionally inside a block (talk, the description of the hybrid
+ *     schedule: autoregressive over blocks, diffusion inside each block);
  *   - SANA-Video 2.0 uses gated linear attention layers (SANA-Video 2.0
  *     news page, "Hybrid Linear-Softmax Attention"; comfyui-wiki model page,
  *     2.0 section);
- *   - the linear attention carries 3D RoPE (talk, "3D RoPE for the linear
- *     attention"; comfyui-wiki model page, rotary position embeddings).
+ *   - the linear attention carries 3D RoPE (talk, architecture section on
+ *     the changes made to the linear attention; comfyui-wiki model page,
+ *     rotary position embeddings).
  *
  * Definitions used by every call, per (batch b, head h):
  *   phi(x)  = max(x, 0), elementwise, on Q and K only.
@@ -128,8 +129,11 @@ svla_status svla_workspace_size(svla_op op, svla_dtype dt, int B, int H,
  * _BLOCK_STEP) for these sizes, as a JSON object written to buf (host
  * memory, `len` bytes including the terminating zero): split count, tokens
  * per split, apply tile, workspace bytes, and for each kernel its name (as
- * profilers report it), grid, block and dynamic LDS.  Launches nothing.
- * SVLA_ERR_VALUE if the text does not fit. */
+ * profilers report it), grid, block and dynamic LDS ("kernels").  A one-block
+ * call of bf16 at d = 32 up to 2048 tokens runs as one launch ("fused": true,
+ * "step_tiles" workgroups of "step_tile" tokens per (b,h)) unless its new
+ * state overlaps the state it reads; "in_place_kernels" then lists the launches
+ * of that case.  Launches nothing.  SVLA_ERR_VALUE if the text does not fit. */
 svla_status svla_describe(svla_op op, svla_dtype dt, int B, int H, int nb, int n, int d,
                           const svla_rope *rope, char *buf, size_t len);
 
@@ -171,8 +175,14 @@ svla_status svla_block_causal_gated(svla_dtype dt, int B, int H, int nb, int n, 
  * S_out = S_in + phi(K)^T V, z_out = z_in + sum phi(K); O reads S_out.
  * S_in/z_in nullable (zero state).  S_out/z_out required; S_out may equal
  * S_in (commit in place) or differ (evaluate without committing, as a
- * denoising loop does before a block is final).  With RoPE, rope->t0 is the
- * absolute frame index of this block's first token. */
+ * denoising loop does before a block is final, or commit into the other of
+ * two state buffers).  With RoPE, rope->t0 is the absolute frame index of
+ * this block's first token.
+ * Launches: bf16 at d = 32 with n <= 2048 and S_out/z_out sharing no byte
+ * with S_in/z_in runs as one kernel (every workgroup of a (b,h) builds the
+ * block state itself, nothing waits on another workgroup); otherwise, and
+ * always when the new state overlaps the old one, a state build and a read-out
+ * that folds the scan in (two kernels; three for d >= 64 or fp32). */
 svla_status svla_block_step(svla_dtype dt, int B, int H, int n, int d,
                             const void *Q, const void *K, const void *V, void *O,
                             const float *S_in, const float *z_in,
@@ -222,7 +232,7 @@ svla_status svla_apply(svla_dtype dt, int B, int H, int nb, int n, int d,
 
 /* For benchmarks that time each kernel with HIP events.  While set, every
  * kernel that a call made by this thread launches for slot k (0 = state
- * build, 1 = scan, 2 = apply) is launched with the start/stop pair
+ * build, 1 = scan, 2 = apply, 3 = one-launch block step) is launched with the start/stop pair
  * events[2k], events[2k+1], which the runtime records around that kernel's
  * execution (a kernel a call does not need is not launched and leaves its
  * pair alone; pairs past n are not used).  `events` are hipEvent_t handles

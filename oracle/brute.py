@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE.  No state, no recurrence: every query is compared with
 every key its block may see, with the block mask of the SANA-Video talk
-("generate block by block causally and diffuse within the block") and, for
+(its description of the hybrid schedule: causal over blocks, bidirectional
+diffusion inside each block) and, for
 the gated variant of SANA-Video 2.0, the product of the decays of the blocks
 in between.  For token i in block c(i) and token j in block c(j):
 

@@ -15,12 +15,14 @@
  *   - The state of block i is the previous block's state plus the current
  *     block's KV contribution (same talk, additive update of the cached
  *     state; abstract, design (2) "Constant-Memory KV cache").
- *   - Bidirectional inside a block, causal across blocks (talk, "generate
- *     video block by block causally and diffuse within the block").
+ *   - Bidirectional inside a block, causal across blocks (talk, the
+ *     description of the hybrid schedule: autoregressive over blocks,
+ *     diffusion inside each block).
  *   - Optional per-block decay g of the carried state (SANA-Video 2.0 pages:
  *     "gated" linear attention layers), S_c = g_c * S_{c-1} + local_c.
- *   - Optional 3D RoPE on the numerator only (talk, "3D RoPE for the linear
- *     attention"; comfyui-wiki model page, rotary position embeddings).
+ *   - Optional 3D RoPE on the numerator only (talk, architecture section on
+ *     the changes made to the linear attention; comfyui-wiki model page,
+ *     rotary position embeddings).
  *
  * Readings taken where the pages are silent (all documented in the design
  * notes of the repository):
