@@ -98,13 +98,37 @@ def _rope_arg(rope):
     return (ctypes.byref(s), s) if s is not None else (None, None)
 
 
+def _shape(t, shape, name):
+    """Raise ValueError unless ``t`` (None allowed) has exactly ``shape``.
+
+    The library reads and writes every tensor through a raw pointer with no
+    range check of its own, so the shapes are checked here, before anything
+    else (device, dtype) and before any call into the library."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, list(shape), list(t.shape)))
+
+
+def _qkv_shape(Q, K, V):
+    """(B, H, N, d) of Q, K, V, which must share one 4-d shape."""
+    for t, name in ((Q, "Q"), (K, "K"), (V, "V")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+    if Q.dim() != 4 or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must share one [B,H,N,d] shape")
+    return tuple(Q.shape)
+
+
+def _pair(a, b, na, nb_):
+    if (a is None) != (b is None):
+        raise ValueError("pass both %s and %s, or neither" % (na, nb_))
+
+
 def _qkv(Q, K, V):
+    _qkv_shape(Q, K, V)
     _dev(Q, "Q")
     dt = _dtype(Q)
     _dev(K, "K", Q.dtype)
     _dev(V, "V", Q.dtype)
-    if Q.dim() != 4 or K.shape != Q.shape or V.shape != Q.shape:
-        raise ValueError("Q, K, V must share one [B,H,N,d] shape")
     return dt
 
 
@@ -131,8 +155,9 @@ def set_timing_events(events) -> None:
 def noncausal(Q, K, V, eps: float = 1e-6, return_state: bool = False,
               out: Optional[torch.Tensor] = None, workspace=None):
     """Bidirectional linear attention over all N tokens (one block)."""
+    B, H, N, d = _qkv_shape(Q, K, V)
+    _shape(out, Q.shape, "out")
     dt = _qkv(Q, K, V)
-    B, H, N, d = Q.shape
     lib = library()
     O = torch.empty_like(Q) if out is None else _dev(out, "out", Q.dtype)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=Q.device) if return_state else None
@@ -150,11 +175,16 @@ def block_causal(Q, K, V, nb: int, S0=None, z0=None, g=None, rope=None, eps: flo
     """Block-causal linear attention over nb blocks of N/nb tokens in one call.
 
     ``g`` [B,H,nb] float32 selects the gated variant."""
-    dt = _qkv(Q, K, V)
-    B, H, N, d = Q.shape
+    B, H, N, d = _qkv_shape(Q, K, V)
     if nb <= 0 or N % nb:
         raise ValueError("N=%d is not a multiple of nb=%d" % (N, nb))
     n = N // nb
+    _shape(S0, (B, H, d, d), "S0")
+    _shape(z0, (B, H, d), "z0")
+    _shape(g, (B, H, nb), "g")
+    _shape(out, Q.shape, "out")
+    _pair(S0, z0, "S0", "z0")
+    dt = _qkv(Q, K, V)
     S0, z0, g = _opt(S0, "S0"), _opt(z0, "z0"), _opt(g, "g")
     lib = library()
     O = torch.empty_like(Q) if out is None else _dev(out, "out", Q.dtype)
@@ -180,8 +210,15 @@ def block_step(Q, K, V, S_in=None, z_in=None, S_out=None, z_out=None, g=None, ro
 
     ``S_out``/``z_out`` default to new tensors; pass S_out=S_in, z_out=z_in to
     commit in place.  Returns (O, S_out, z_out)."""
+    B, H, n, d = _qkv_shape(Q, K, V)
+    _shape(S_in, (B, H, d, d), "S_in")
+    _shape(z_in, (B, H, d), "z_in")
+    _shape(S_out, (B, H, d, d), "S_out")
+    _shape(z_out, (B, H, d), "z_out")
+    _shape(g, (B, H), "g")
+    _shape(out, Q.shape, "out")
+    _pair(S_in, z_in, "S_in", "z_in")
     dt = _qkv(Q, K, V)
-    B, H, n, d = Q.shape
     S_in, z_in, g = _opt(S_in, "S_in"), _opt(z_in, "z_in"), _opt(g, "g")
     lib = library()
     O = torch.empty_like(Q) if out is None else _dev(out, "out", Q.dtype)
@@ -207,6 +244,7 @@ def block_step(Q, K, V, S_in=None, z_in=None, S_out=None, z_out=None, g=None, ro
 
 def state_build(K, V, nb: int, rope=None):
     """Each block's own contribution: S_local [B,H,nb,d,d], z_local [B,H,nb,d]."""
+    _qkv_shape(K, K, V)
     _dev(K, "K")
     dt = _dtype(K)
     _dev(V, "V", K.dtype)
@@ -224,9 +262,17 @@ def state_build(K, V, nb: int, rope=None):
 
 def state_scan(S_local, z_local, g=None, S0=None, z0=None):
     """Inclusive (decayed) prefix over blocks of the local states."""
+    if not isinstance(S_local, torch.Tensor) or S_local.dim() != 5 or \
+            S_local.shape[3] != S_local.shape[4]:
+        raise ValueError("S_local must be a [B,H,nb,d,d] tensor")
+    B, H, nb, d, _ = S_local.shape
+    _shape(z_local, (B, H, nb, d), "z_local")
+    _shape(g, (B, H, nb), "g")
+    _shape(S0, (B, H, d, d), "S0")
+    _shape(z0, (B, H, d), "z0")
+    _pair(S0, z0, "S0", "z0")
     _dev(S_local, "S_local", torch.float32)
     _dev(z_local, "z_local", torch.float32)
-    B, H, nb, d, _ = S_local.shape
     g, S0, z0 = _opt(g, "g"), _opt(S0, "S0"), _opt(z0, "z0")
     lib = library()
     Sp = torch.empty_like(S_local)
@@ -239,13 +285,15 @@ def state_scan(S_local, z_local, g=None, S0=None, z0=None):
 
 def apply(Q, S_prefix, z_prefix, nb: int, rope=None, eps: float = 1e-6):
     """O of every token against its block's (given) inclusive state."""
+    B, H, N, d = _qkv_shape(Q, Q, Q)
+    if nb <= 0 or N % nb:
+        raise ValueError("N=%d is not a multiple of nb=%d" % (N, nb))
+    _shape(S_prefix, (B, H, nb, d, d), "S_prefix")
+    _shape(z_prefix, (B, H, nb, d), "z_prefix")
     _dev(Q, "Q")
     dt = _dtype(Q)
     _dev(S_prefix, "S_prefix", torch.float32)
     _dev(z_prefix, "z_prefix", torch.float32)
-    B, H, N, d = Q.shape
-    if nb <= 0 or N % nb:
-        raise ValueError("N=%d is not a multiple of nb=%d" % (N, nb))
     n = N // nb
     lib = library()
     O = torch.empty_like(Q)

@@ -104,12 +104,14 @@ def scaled_config(cfg: Config, **overrides) -> Config:
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round-to-nearest-even, NaN kept quiet."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # in uint32: the sum stays below 2^32 for every non-NaN pattern (at most
+    # 0xFF7FFFFF + 0x8000); NaN patterns, which may wrap, are replaced below
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     out = rounded.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return out
 
 
