@@ -102,6 +102,21 @@
 #ifndef SVLA_APPLY_XCD
 #define SVLA_APPLY_XCD 1           // apply: the token tiles of one block on one XCD
 #endif
+#ifndef SVLA_FUSED_MAX_N
+#define SVLA_FUSED_MAX_N 2048      // one-launch block step (bf16, d = 32): longest block
+#endif
+#ifndef SVLA_FUSED_WGS
+#define SVLA_FUSED_WGS 256         // ... workgroups per launch at most (one per CU), unless B*H is larger
+#endif
+#ifndef SVLA_FUSED_W
+#define SVLA_FUSED_W 16            // ... waves per workgroup
+#endif
+#ifndef SVLA_FUSED_PF
+#define SVLA_FUSED_PF 3            // ... K/V stages in flight per wave
+#endif
+#ifndef SVLA_FUSED_QG
+#define SVLA_FUSED_QG 2            // ... Q groups of 16 tokens per wave (tile <= 16 * W * QG)
+#endif
 // Cache-policy bits of the streaming accesses (gfx950 buffer instructions:
 // bit 1 = nt, non-temporal).  Measured: nt pays for K/V (read once by the
 // state build), for Q (read once by the apply) and not for O.
@@ -270,9 +285,17 @@ __device__ __forceinline__ int rope_entries(const RopeK &r, int nf)
 // entry's angle is reduced to a fraction of a turn in fp64 (so large frame
 // indices keep their accuracy) and only then goes through an fp32 sin/cos
 // of pi times that small argument.
-__device__ __forceinline__ double rope_freq(const RopeK &r, int a, int m)
+// A kernel-argument double held in scalar registers (read once per wave).
+__device__ __forceinline__ double sreg_f64(double x)
 {
-    double f = r.freq0[a], q = r.ratio[a];
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double rope_freq(double f, double q, int m)
+{
 #pragma unroll
     for (int b = 0; b < 6; ++b) {
         if ((m >> b) & 1) f *= q;
@@ -285,6 +308,12 @@ __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
 {
     const int pt = r.dt / 2, ph = r.dh / 2;
     const int nT = nf * pt, nH = r.gh * ph, total = rope_entries(r, nf);
+    // per-axis values in scalar registers, chosen by value below: an index
+    // into the kernel argument that differs across lanes would become a
+    // vector memory load, whose wait (loads complete in order) would also wait
+    // for every K/V/Q load the kernel issued before the table
+    const double fT = sreg_f64(r.freq0[0]), fH = sreg_f64(r.freq0[1]), fW = sreg_f64(r.freq0[2]);
+    const double qT = sreg_f64(r.ratio[0]), qH = sreg_f64(r.ratio[1]), qW = sreg_f64(r.ratio[2]);
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
         int pos, m, a;
         if (e < nT) {
@@ -294,7 +323,8 @@ __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
         } else {
             const int x = e - nT - nH; m = x / r.gw; pos = x - m * r.gw; a = 2;
         }
-        double turns = (double)pos * rope_freq(r, a, m);
+        const double fa = a == 0 ? fT : a == 1 ? fH : fW, qa = a == 0 ? qT : a == 1 ? qH : qW;
+        double turns = (double)pos * rope_freq(fa, qa, m);
         turns -= floor(turns);
         float s, c;
         sincospif(2.0f * (float)turns, &s, &c);
@@ -1502,9 +1532,9 @@ svla_apply_bf16(const ApplyArgs a)
         }
     }
 
-    // 2. without RoPE, the first PF groups of Q (slot p holds this wave's
-    // group i, i % PF == p; the scheduling barriers keep the loads in slot
-    // order)
+    // 2. the first PF groups of Q, issued before the state is formed so they
+    // land meanwhile (slot p holds this wave's group i, i % PF == p; the
+    // scheduling barriers keep the loads in slot order)
     const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
     const int nw = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
     auto qoff = [&](int i, int ks) -> uint32_t {
@@ -1513,13 +1543,11 @@ svla_apply_bf16(const ApplyArgs a)
     };
     __builtin_amdgcn_sched_barrier(0);
     u32x4_t qreg[PF][KS];
-    if constexpr (!ROPE) {
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
+    for (int p = 0; p < PF; ++p) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(p, ks));
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(p, ks));
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // 3. the state in registers: A fragments sf (lane (rho + 16 kg), value i
@@ -1646,13 +1674,21 @@ svla_apply_bf16(const ApplyArgs a)
     };
     if constexpr (ROPE) {
         // the rotation makes this loop bound by the vector ALU: batches of PF
-        // groups, loaded together, keep the register count (and occupancy) up
+        // groups, loaded together, keep the register count (and occupancy) up;
+        // the first batch was issued before the state was formed
         for (int i0 = 0; i0 < nw; i0 += PF) {
             u32x4_t qb[PF][KS];
+            if (i0 == 0) {
 #pragma unroll
-            for (int p = 0; p < PF; ++p)
+                for (int p = 0; p < PF; ++p)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) qb[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(i0 + p, ks));
+                    for (int ks = 0; ks < KS; ++ks) qb[p][ks] = qreg[p][ks];
+            } else {
+#pragma unroll
+                for (int p = 0; p < PF; ++p)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) qb[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(i0 + p, ks));
+            }
 #pragma unroll
             for (int p = 0; p < PF; ++p) {
                 if (i0 + p >= nw) break;
@@ -2013,6 +2049,300 @@ svla_apply_f32(const ApplyArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// svla_step_fused: a one-block call (a block step, or a non-causal call over
+// a short sequence) of bf16 inputs at d = 32 in one launch, with no hand-off
+// between workgroups.
+//
+// Workgroup = (bh, tile t), `tiles` workgroups per (bh), all on one XCD (the
+// tiles of a bh are 8 workgroup ids apart and the dispatch is round-robin over
+// the eight XCDs).  Every workgroup builds the block's whole state itself:
+// the workgroups of one bh read the same K and V rows, which their shared L2
+// serves after the first miss, and sum them in the same fixed order, so they
+// all hold the same bits.  Each adds the decayed carried state and reads out
+// the Q rows of its own tile; tile 0 writes the new state.  The host takes
+// this path only when the new state does not overlap the carried one, so no
+// workgroup of a launch reads memory that another one writes, and nothing
+// waits on another workgroup.
+//
+// Build: W waves, wave w takes every W-th 16-token stage of the block (one
+// token row chunk of 16 bytes per lane and tensor, PF stages of K/V loads in
+// flight in registers); phi (and with RoPE the rotation, the key split into
+// bf16 hi + lo) is applied in registers, the stage goes through a
+// wave-private LDS slot, and the token contraction runs on
+// v_mfma_f32_32x32x16_bf16 from transposing reads; z sums the unrotated
+// phi(k) on the vector ALU.  The W tiles are summed in wave order.
+// Read-out: O^T = S^T phi~(Q)^T on v_mfma_f32_16x16x32_bf16 with the state
+// as the A operand in registers; the tile's Q groups (wave w: groups w,
+// w + W, ..., at most QG) are loaded into registers right after the first K/V
+// stages, so they arrive while the state is built.  The RoPE table covers the
+// whole block and serves both halves.
+// ---------------------------------------------------------------------------
+struct StepArgs {
+    const void *Q, *K, *V;
+    void *O;
+    const float *S_in, *z_in;      // carried state or null
+    const float *g;                // [BH] decay of the carried state, or null
+    float *S_out, *z_out;          // new state or null
+    int n;                         // tokens of the block
+    int tiles, tile;               // workgroups per bh, tokens per workgroup (multiple of 16)
+    int work_bytes;                // dynamic LDS: stage slots / epilogue, after the RoPE table
+    long BH;
+    float eps;
+    RopeK rope;
+};
+
+template <bool ROPE, int W, int PF, int QG>
+__global__ void __launch_bounds__(64 * W)
+svla_step_fused(const StepArgs a)
+{
+    constexpr int D = 32;
+    constexpr int NT = 64 * W;
+    constexpr int ROWB = D * 2;           // 64 bytes per token row
+    constexpr int TILEB = 16 * ROWB;      // one 16-token stage of one tensor
+    constexpr int NK = ROPE ? 2 : 1;      // K tiles per stage: (rotated) hi, lo
+    constexpr int SLOTB = (NK + 1) * TILEB;
+    static_assert(2 * PF + QG < 64, "the loads issued together must fit the vmcnt counter");
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int k8 = (int)(blockIdx.x >> 3);
+    const long bh = 8L * (k8 / a.tiles) + (blockIdx.x & 7);
+    const int tile = k8 % a.tiles;
+    if (bh >= a.BH) return;
+    const int n = a.n;
+    const int t_lo = tile * a.tile, t_hi = min(t_lo + a.tile, n);
+
+    const uint32_t slice = (uint32_t)n * D * 2;
+    const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
+    const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
+    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
+    const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
+
+    float2 *tab = (float2 *)lds;
+    unsigned char *work = lds + (ROPE ? a.rope.tab_bytes : 0);
+    float *st = (float *)(work + a.work_bytes);           // the new state, S[k][v] then z
+
+    // 1. the first PF stages of K and V: stage st = wave + W i; lane -> row
+    // lane / 4 of the stage, chunk lane % 4
+    const int row = lane >> 2, q = lane & 3;
+    const int nst = (n + 15) / 16;
+    const int nw = nst > wave ? (nst - wave + W - 1) / W : 0;
+    auto kv_off = [&](int i) -> uint32_t {
+        const int t = 16 * (wave + W * i) + row;
+        return t < n ? (uint32_t)(t * D + q * 8) * 2u : kOOB;
+    };
+    u32x4_t kreg[PF], vreg[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        kreg[p] = load16p<0>(rK, kv_off(p));
+        vreg[p] = load16p<0>(rV, kv_off(p));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // 2. this wave's Q groups of the tile, in the read-out's operand layout
+    // (token lane % 16 of the group, features 8 (lane / 16) ..): issued now,
+    // after the first K/V stages, so they land while the state is built
+    const int kg = lane >> 4, tl = lane & 15;
+    u32x4_t qreg[QG];
+#pragma unroll
+    for (int j = 0; j < QG; ++j) {
+        const int tok = t_lo + 16 * (wave + W * j) + tl;
+        qreg[j] = load16p<SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * kg) * 2u : kOOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. the carried state: thread -> S elements 4 tid .. (and z for tid < d / 4)
+    const float gb = a.g ? a.g[bh] : 1.f;
+    f32x4_t s_in = {0.f, 0.f, 0.f, 0.f}, z_in = {0.f, 0.f, 0.f, 0.f};
+    const int e0 = 4 * tid;
+    if (a.S_in) {
+        if (e0 < D * D) s_in = *(const f32x4_t *)(a.S_in + bh * D * D + e0);
+        if (e0 < D) z_in = *(const f32x4_t *)(a.z_in + bh * D + e0);
+    }
+
+    // 4. the RoPE table of the whole block, while the loads are in flight
+    const int nf = ROPE ? (n - 1) / (a.rope.gh * a.rope.gw) + 1 : 1;
+    RopePairs<4> ppk;
+    if constexpr (ROPE) {
+        rope_fill(tab, a.rope, a.rope.t0, nf);
+        ppk = rope_pairs<4>(a.rope, q * 8, nf);
+        lds_barrier();
+    }
+    unsigned char *slot = work + wave * SLOTB;
+
+    // 5. the block's state
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    float zacc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
+    const int m = lane & 31, g = lane >> 5;
+    const int fl = trb_offset<D>(lane, 0);
+    const int nwr = (nw + PF - 1) / PF * PF;
+    for (int i0 = 0; i0 < nwr; i0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int i = i0 + p;
+            u32x4_t kr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kr[e] = relu_bf16x2(kreg[p][e]);
+            float kf[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kf[2 * e] = bf16lo(kr[e]);
+                kf[2 * e + 1] = bf16hi(kr[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
+            if constexpr (ROPE) {
+                const int tok = 16 * (wave + W * i) + row;
+                rope_rotate<4>(kf, rope_pos((uint32_t)tok, 0, a.rope), ppk, tab);
+                u32x4_t hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = pack_bf16(kf[2 * e], kf[2 * e + 1]);
+                    lo[e] = pack_bf16(kf[2 * e] - bf16lo(hi[e]), kf[2 * e + 1] - bf16hi(hi[e]));
+                }
+                *(u32x4_t *)(slot + row * ROWB + q * 16) = hi;
+                *(u32x4_t *)(slot + TILEB + row * ROWB + q * 16) = lo;
+            } else {
+                *(u32x4_t *)(slot + row * ROWB + q * 16) = kr;
+            }
+            *(u32x4_t *)(slot + NK * TILEB + row * ROWB + q * 16) = vreg[p];
+            // refill this register slot with the stage PF ahead
+            __builtin_amdgcn_sched_barrier(0);
+            kreg[p] = load16p<0>(rK, kv_off(i + PF));
+            vreg[p] = load16p<0>(rV, kv_off(i + PF));
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8_t av = trb_load<D>(slot, fl);
+            const bf16x8_t bv = trb_load<D>(slot + NK * TILEB, fl);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+            if constexpr (ROPE) {
+                const bf16x8_t al = trb_load<D>(slot + TILEB, fl);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc, 0, 0, 0);
+            }
+        }
+    }
+
+    // 6. the W tiles summed in a fixed order, plus the decayed carried state:
+    // with more than 8 waves, wave w + 8 first adds its tile into wave w's
+    // (through LDS), then the 8 tiles are summed in wave order
+    constexpr int WR = W > 8 ? 8 : W;           // tiles in the final sum
+    static_assert(W <= 16 && (W <= 8 || W == 16), "W = 1 .. 8 or 16");
+    float *red = (float *)work;                 // WR x D x D floats
+    float *zw = red + WR * D * D;               // W x D floats
+    auto tile_pos = [&](int r) { return (8 * (r >> 2) + 4 * g + (r & 3)) * D + m; };
+    __syncthreads();                            // every wave is done with its slot (and its loads)
+    if constexpr (W > 8) {
+        if (wave >= 8) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(wave - 8) * D * D + tile_pos(r)] = acc[r];
+        }
+        __syncthreads();
+        if (wave < 8) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] += red[wave * D * D + tile_pos(r)];
+        }
+        __syncthreads();
+    }
+    if (wave < WR) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[wave * D * D + tile_pos(r)] = acc[r];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float v = zacc[e];
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        zacc[e] = v;
+    }
+    if (lane < 4) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zw[wave * D + lane * 8 + e] = zacc[e];
+    }
+    __syncthreads();
+    if (e0 < D * D) {
+        f32x4_t t = *(const f32x4_t *)(red + e0);
+#pragma unroll
+        for (int w = 1; w < WR; ++w) t += *(const f32x4_t *)(red + w * D * D + e0);
+        const f32x4_t s = gb * s_in + t;
+        *(f32x4_t *)(st + e0) = s;
+        if (tile == 0 && a.S_out) *(f32x4_t *)(a.S_out + bh * D * D + e0) = s;
+    }
+    if (e0 < D) {
+        f32x4_t t = *(const f32x4_t *)(zw + e0);
+#pragma unroll
+        for (int w = 1; w < W; ++w) t += *(const f32x4_t *)(zw + w * D + e0);
+        const f32x4_t z = gb * z_in + t;
+        *(f32x4_t *)(st + D * D + e0) = z;
+        if (tile == 0 && a.z_out) *(f32x4_t *)(a.z_out + bh * D + e0) = z;
+    }
+    lds_barrier();
+
+    // 7. the state as A fragments: lane (rho + 16 kg), value i = S[8 kg + i][op_col(mi, rho)]
+    bf16x8_t sf[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int f = op_col(mi, tl);
+        u32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = pack_bf16(st[(8 * kg + 2 * e) * D + f], st[(8 * kg + 2 * e + 1) * D + f]);
+        sf[mi] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    float zf[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zf[e] = st[D * D + 8 * kg + e];
+    RopePairs<4> ppq;
+    if constexpr (ROPE) ppq = rope_pairs<4>(a.rope, 8 * kg, nf);
+
+    // 8. read-out of this wave's groups of the tile
+    const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
+    const int nq = ngroups > wave ? (ngroups - wave + W - 1) / W : 0;
+#pragma unroll
+    for (int j = 0; j < QG; ++j) {
+        if (j >= nq) break;                     // (uniform)
+        const int tok = t_lo + 16 * (wave + W * j) + tl;
+        const bool valid = tok < t_hi;
+        const u32x4_t qr = qreg[j];
+        u32x4_t pq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[e]);
+        float pf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pf[2 * e] = bf16lo(pq[e]);
+            pf[2 * e + 1] = bf16hi(pq[e]);
+        }
+        float den = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) den = fmaf(pf[e], zf[e], den);
+        if constexpr (ROPE) {
+            rope_rotate<4>(pf, rope_pos((uint32_t)tok, 0, a.rope), ppq, tab);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pq[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
+        }
+        const bf16x8_t qf = __builtin_bit_cast(bf16x8_t, pq);
+        den += __shfl_xor(den, 16);
+        den += __shfl_xor(den, 32);
+        den += a.eps;
+        const float inv = den != 0.f ? 1.0f / den : 0.f;
+        f32x4_t o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+        o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[0], qf, o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[1], qf, o1, 0, 0, 0);
+        // m-tiles 0 and 1 hold O[tok][8 kg .. 8 kg + 7]
+        u32x4_t o;
+        o[0] = pack_bf16(o0[0] * inv, o0[1] * inv);
+        o[1] = pack_bf16(o0[2] * inv, o0[3] * inv);
+        o[2] = pack_bf16(o1[0] * inv, o1[1] * inv);
+        o[3] = pack_bf16(o1[2] * inv, o1[3] * inv);
+        store16p<SVLA_O_AUX>(rO, valid ? (uint32_t)(tok * D + op_col(0, 4 * kg)) * 2u : kOOB, o);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // host side
@@ -2021,17 +2351,18 @@ thread_local char g_err[512] = "";
 thread_local void *const *t_events = nullptr;   // svla_set_timing_events
 thread_local int t_nev = 0;
 
-enum Slot { SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2 };
+enum Slot { SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2, SLOT_STEP = 3 };
+constexpr int kSlots = 4;
 
 // Every kernel goes through here.  With timing events set, the launch
 // carries a start/stop event pair that the runtime records around the
 // kernel's own execution.
 // svla_describe: while set, launch() records what it would launch instead.
 struct LaunchDesc {
-    char name[3][96];
-    unsigned grid[3], block[3];
-    size_t lds[3];
-    bool used[3];
+    char name[kSlots][96];
+    unsigned grid[kSlots], block[kSlots];
+    size_t lds[kSlots];
+    bool used[kSlots];
 };
 thread_local LaunchDesc *t_desc = nullptr;
 
@@ -2090,6 +2421,12 @@ struct Plan {
     size_t lds_build, lds_apply;
     size_t off_spart, off_zpart, off_sop, off_zpre, total;
     RopeK rope;
+    // one-launch block step (svla_step_fused), taken when the new state does
+    // not overlap the carried one
+    bool fused;
+    int ftiles, ftile;         // workgroups per bh, tokens per workgroup
+    int fwork, ftab;           // LDS bytes: stage slots / epilogue, RoPE table
+    size_t lds_fused;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -2207,6 +2544,35 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     p->fold = (op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP) &&
               p->esize == 2 && d == 32 && nb == 1 && n > 0 &&
               p->splits + 1 <= (p->rope.on ? kFoldMaxPartsRope : kFoldMaxParts);
+    // the one-launch step: one block of bf16 at d = 32, short enough for every
+    // workgroup of a (b,h) to build the whole block state itself
+    p->fused = (op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP) &&
+               p->esize == 2 && d == 32 && nb == 1 && n > 0 && n <= SVLA_FUSED_MAX_N && p->BH > 0;
+    if (p->fused) {
+        // at most one workgroup per CU: (a second round of workgroups would
+        // repeat the whole build); at least one per (b,h)
+        const int ngr = (n + 15) / 16;                       // 16-token groups
+        long T = SVLA_FUSED_WGS / p->BH;
+        if (T > ngr) T = ngr;
+        if (T < 1) T = 1;
+        const int maxg = SVLA_FUSED_W * SVLA_FUSED_QG;        // groups one workgroup reads out
+        if ((ngr + T - 1) / T > maxg) T = (ngr + maxg - 1) / maxg;
+        const int gpt = (int)((ngr + T - 1) / T);
+        p->ftile = 16 * gpt;
+        p->ftiles = (ngr + gpt - 1) / gpt;
+        const int slotb = (p->rope.on ? 3 : 2) * 1024;
+        const int epi = ((SVLA_FUSED_W > 8 ? 8 : SVLA_FUSED_W) * d * d + SVLA_FUSED_W * d) * 4;
+        p->fwork = SVLA_FUSED_W * slotb > epi ? SVLA_FUSED_W * slotb : epi;
+        p->ftab = 0;
+        if (p->rope.on) {
+            const long nf = (n - 1) / ((long)p->rope.gh * p->rope.gw) + 1;
+            const long e = nf * (p->rope.dt / 2) + (long)p->rope.gh * (p->rope.dh / 2) +
+                           (long)p->rope.gw * (p->rope.dw / 2) + 1;
+            if (e > kMaxRopeEntries) p->fused = false;          // (the split build takes it)
+            p->ftab = (int)((e * 8 + 255) & ~255L);
+        }
+        p->lds_fused = (size_t)p->ftab + p->fwork + (d * d + d) * 4;   // (+ the static Q rows)
+    }
     p->tile = (p->esize == 2 && d >= 64) ? SVLA_APPLY_TILE_LDS
               : d == 128 ? SVLA_APPLY_TILE128
               : p->rope.on ? (p->fold ? SVLA_APPLY_TILE_FOLD_ROPE : SVLA_APPLY_TILE_ROPE)
@@ -2375,6 +2741,31 @@ void apply_any(const Plan &p, const ApplyArgs &a, hipStream_t s)
     else launch_apply<128>(p, a, s);
 }
 
+void launch_fused(const Plan &p, const StepArgs &args, hipStream_t s)
+{
+    StepArgs a = args;
+    a.tiles = p.ftiles;
+    a.tile = p.ftile;
+    a.work_bytes = p.fwork;
+    a.BH = p.BH;
+    a.rope = p.rope;
+    a.rope.tab_bytes = p.ftab;
+    const unsigned grid = (unsigned)(8L * p.ftiles * ((p.BH + 7) / 8));
+    constexpr int W = SVLA_FUSED_W, PF = SVLA_FUSED_PF, QG = SVLA_FUSED_QG;
+    char nm[96];
+    snprintf(nm, sizeof nm, "void svla_step_fused<%s, %d, %d, %d>", p.rope.on ? "true" : "false", W, PF, QG);
+    if (p.rope.on) launch(svla_step_fused<true, W, PF, QG>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+    else launch(svla_step_fused<false, W, PF, QG>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+}
+
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte (null: no).
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
 svla_status check_launch(const char *fn)
 {
     hipError_t e = hipGetLastError();
@@ -2413,6 +2804,17 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
     (void)hipGetLastError();
+    const size_t sb = (size_t)p.BH * d * d * 4, zb = (size_t)p.BH * d * 4;
+    if (p.fused && !overlap(S0, sb, S_fin, sb) && !overlap(S0, sb, z_fin, zb) &&
+        !overlap(z0, zb, S_fin, sb) && !overlap(z0, zb, z_fin, zb)) {
+        StepArgs fa;
+        memset(&fa, 0, sizeof fa);
+        fa.Q = Q; fa.K = K; fa.V = V; fa.O = O;
+        fa.S_in = S0; fa.z_in = z0; fa.g = g; fa.S_out = S_fin; fa.z_out = z_fin;
+        fa.n = n; fa.eps = eps;
+        launch_fused(p, fa, s);
+        return check_launch(fn);
+    }
     ScanArgs sa;
     memset(&sa, 0, sizeof sa);
     sa.S_part = (const float *)(w + p.off_spart);
@@ -2500,32 +2902,46 @@ svla_status svla_describe(svla_op op, svla_dtype dt, int B, int H, int nb, int n
     Plan p;
     svla_status st = make_plan(fn, op, dt, B, H, nb, n, d, rope, &p);
     if (st) return st;
-    LaunchDesc desc;
-    memset(&desc, 0, sizeof desc);
-    t_desc = &desc;
+    // the plan the call takes, and (for a call that can take the one-launch
+    // step) the two-kernel plan it takes when the new state overlaps the old
+    LaunchDesc desc[2];
+    memset(desc, 0, sizeof desc);
     BuildArgs ba;
     memset(&ba, 0, sizeof ba);
     ScanArgs sa;
     memset(&sa, 0, sizeof sa);
     ApplyArgs aa;
     memset(&aa, 0, sizeof aa);
+    StepArgs fa;
+    memset(&fa, 0, sizeof fa);
     if (p.BH > 0) {
+        t_desc = &desc[0];
+        if (p.fused) launch_fused(p, fa, nullptr);
+        t_desc = &desc[p.fused ? 1 : 0];
         if ((long)nb * n > 0) build_any(p, ba, nullptr);
         if (!p.fold) scan_any<SCAN_FORWARD>(p, sa, nullptr);
         if ((long)nb * n > 0) apply_any(p, aa, nullptr);
+        t_desc = nullptr;
     }
-    t_desc = nullptr;
-    static const char *slot_name[3] = {"build", "scan", "apply"};
-    int w = snprintf(buf, len, "{\"splits\": %d, \"chunk\": %d, \"apply_tile\": %d, \"workspace\": %zu, \"kernels\": [",
+    static const char *slot_name[kSlots] = {"build", "scan", "apply", "step"};
+    int w = snprintf(buf, len, "{\"fused\": %s, \"step_tiles\": %d, \"step_tile\": %d, \"splits\": %d, "
+                     "\"chunk\": %d, \"apply_tile\": %d, \"workspace\": %zu",
+                     p.fused ? "true" : "false", p.fused ? p.ftiles : 0, p.fused ? p.ftile : 0,
                      p.splits, p.chunk, p.tile, p.total);
-    bool first = true;
-    for (int k = 0; k < 3; ++k) {
-        if (!desc.used[k] || w < 0 || (size_t)w >= len) continue;
-        w += snprintf(buf + w, len - w, "%s{\"slot\": \"%s\", \"name\": \"%s\", \"grid\": %u, \"block\": %u, \"lds\": %zu}",
-                      first ? "" : ", ", slot_name[k], desc.name[k], desc.grid[k], desc.block[k], desc.lds[k]);
-        first = false;
+    for (int pl = 0; pl < (p.fused ? 2 : 1); ++pl) {
+        if (w < 0 || (size_t)w >= len) break;
+        w += snprintf(buf + w, len - w, ", \"%s\": [", pl == 0 ? "kernels" : "in_place_kernels");
+        bool first = true;
+        for (int k = 0; k < kSlots; ++k) {
+            if (!desc[pl].used[k] || w < 0 || (size_t)w >= len) continue;
+            w += snprintf(buf + w, len - w, "%s{\"slot\": \"%s\", \"name\": \"%s\", \"grid\": %u, \"block\": %u, \"lds\": %zu}",
+                          first ? "" : ", ", slot_name[k], desc[pl].name[k], desc[pl].grid[k],
+                          desc[pl].block[k], desc[pl].lds[k]);
+            first = false;
+        }
+        if (w >= 0 && (size_t)w < len) w += snprintf(buf + w, len - w, "]");
     }
-    if (w >= 0 && (size_t)w < len) w += snprintf(buf + w, len - w, "]}");
+    if (w >= 0 && (size_t)w < len) w += snprintf(buf + w, len - w, "}");
     if (w < 0 || (size_t)w >= len) return fail(SVLA_ERR_VALUE, fn, "buffer of %zu bytes too small", len);
     return SVLA_OK;
 }

@@ -167,6 +167,17 @@ def test_workspace_covers_every_plan():
         # as long as the block's splits fit the apply's partial count: the
         # minute-long block step does)
         if nb == 1 and d == 32:
-            assert [k["slot"] for k in plain["kernels"]] == ["build", "apply"]
+            # up to 2048 tokens: one launch, or (new state over the old one)
+            # build and apply
+            short = n <= 2048
+            key = "in_place_kernels" if short else "kernels"
+            assert plain["fused"] is short and rot["fused"] is short
+            assert [k["slot"] for k in plain[key]] == ["build", "apply"]
+            if short:
+                assert [k["slot"] for k in plain["kernels"]] == ["step"]
+                assert [k["slot"] for k in rot["kernels"]] == ["step"]
             if op == "block_step" and n == 1170:
-                assert [k["slot"] for k in rot["kernels"]] == ["build", "apply"]
+                assert [k["slot"] for k in rot["in_place_kernels"]] == ["build", "apply"]
+                assert rot["step_tiles"] * rot["step_tile"] >= n
+        else:
+            assert plain["fused"] is False and "in_place_kernels" not in plain
