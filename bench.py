@@ -1,24 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of block-causal ReLU linear attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5]
-                    [--c4-mode stream|oneshot] [--rotate R] [--settle S] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4|c2|c3|c5]
+                    [--c4-mode both|stream|oneshot] [--inplace] [--rotate R] [--settle S]
+                    [--no-cpu-baseline]
 
-A step is one pass of the whole path (state build -> scan -> apply) over one
-batch of the workload's synthetic input, with inputs resident in HBM.  R
-copies of the inputs and outputs rotate so that consecutive steps do not hit
-in the 256 MB Infinity Cache.  About S seconds of untimed steps let the
-clocks settle, then W untimed steps, then K timed steps between two device
-synchronisations; one JSON line on stdout.
+A step is one pass of the whole path over one batch of the workload's
+synthetic input, with the inputs resident in HBM.  R copies of the inputs and
+outputs rotate so that consecutive steps do not hit in the 256 MB Infinity
+Cache.  About S seconds of untimed steps let the clocks settle, then W untimed
+steps, then K timed steps between two device synchronisations; one JSON line
+on stdout.
+
+The default workload is the minute-long 480p stream (B1 H70 d32, 80 blocks of
+1170 tokens, 3D RoPE), the largest one: a step is the 80 sequential
+`svla_block_step` calls of one video (replayed from a HIP graph), with the
+state committed into the other of two state buffers (the one-launch step;
+--inplace commits in place, the two-kernel step).  `value` is that stream's
+tokens*heads/s.  With --c4-mode both (the default) the same 80 blocks are also
+timed as one `svla_block_causal` call and reported under "c4_oneshot".
 
 Also:
-  --copy-calibration           time a plain device copy of known size (run it
-                               under rocprofv3 --pmc to calibrate byte counters)
-  --summarize-counters F W CF CW
+  --ceiling                    time a plain device copy and a read-only
+                               reduction of 2 GiB (the achievable HBM rates)
+  --copy-calibration           a plain device copy of known size (run it under
+                               rocprofv3 --pmc to calibrate byte counters)
+  --summarize-counters F W CF CW --tag T
                                fold rocprofv3 --pmc CSVs (FETCH_SIZE run F,
                                WRITE_SIZE run W, and the same two counters
                                over --copy-calibration runs CF, CW) into
-                               profiles/counters_<config>.json
+                               profiles/counters_<T>.json
+  --summarize-mfma M --tag T   fold a rocprofv3 --pmc run of the matrix-core
+                               counters into profiles/mfma_<T>.json
 """
 from __future__ import annotations
 
@@ -37,9 +50,16 @@ sys.path.insert(0, ROOT)
 METRIC = "block linear-attn tokens·heads/s + achieved HBM GB/s vs MI355X peak"
 UNIT = "tokens·heads/s"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+GATE_FRAC = 0.60                # the minute-long and 720p shapes' target fraction of peak HBM
 SOURCE = os.path.join(ROOT, "block_causal_linear_relu_amd", "csrc", "svla.hip")
-KERNEL_SLOTS = {"build": (0, 1), "scan": (2, 3), "apply": (4, 5)}
+KERNEL_SLOTS = {"build": (0, 1), "scan": (2, 3), "apply": (4, 5), "step": (6, 7)}
 COPY_BYTES = 1 << 29            # 512 MiB read + 512 MiB written
+# one rocprofv3 --pmc pass (3 SQ counters underneath, 1 GRBM): MfmaUtil =
+# 100 * sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs); MfmaFlopsBF16 =
+# 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16; VALUBusy = 100 * sum SQ_ACTIVE_INST_VALU /
+# CUs / GRBM_GUI_ACTIVE (the box's own derived-counter definitions)
+MFMA_COUNTERS = ("MfmaUtil", "MfmaFlopsBF16", "VALUBusy", "GRBM_GUI_ACTIVE")
 
 
 def source_hash() -> str:
@@ -51,15 +71,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5"])
-    ap.add_argument("--c4-mode", default="stream", choices=["stream", "oneshot"])
+    ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--c4-mode", default="both", choices=["both", "stream", "oneshot"])
+    ap.add_argument("--inplace", action="store_true",
+                    help="streaming: commit the state in place (the two-kernel step)")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup (clock settling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceiling", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--summarize-mfma", metavar="DIR")
+    ap.add_argument("--tag", help="name of the summary written by --summarize-*")
     return ap.parse_args()
 
 
@@ -67,9 +92,13 @@ def parse():
 # workload
 # ---------------------------------------------------------------------------
 class Workload:
-    """Device buffers (R rotating sets) and the call for one step."""
+    """Device buffers (R rotating sets) and the call for one step.
 
-    def __init__(self, name: str, rotate: int, c4_mode: str):
+    mode: "oneshot" (one call over all blocks; the non-causal call for a
+    one-block workload), "stream" (one svla_block_step per block, the state
+    double-buffered) or "stream_inplace" (the state committed in place)."""
+
+    def __init__(self, name: str, rotate: int, mode: str, x=None):
         import torch
         import block_causal_linear_relu_amd as svla
         from workloads import CONFIGS, make_inputs
@@ -77,8 +106,9 @@ class Workload:
         self.torch, self.svla = torch, svla
         self.cfg = cfg = CONFIGS[name]
         self.name = name
-        self.stream_mode = name == "c4" and c4_mode == "stream"
-        x = make_inputs(cfg)
+        self.mode = mode
+        self.stream_mode = mode != "oneshot"
+        x = make_inputs(cfg) if x is None else x
         self.x = x
         dev = torch.device("cuda:0")
         bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
@@ -87,15 +117,16 @@ class Workload:
         B, H, N, d = Q.shape
         self.B, self.H, self.N, self.d, self.nb, self.n = B, H, N, d, cfg.nb, cfg.n
         self.sets = []
+        nbuf = 2 if mode == "stream" else 1
         for r in range(rotate):
             if self.stream_mode:
                 n = cfg.n
                 blocks = [tuple(t[:, :, s * n:(s + 1) * n].contiguous() for t in (Q, K, V))
                           for s in range(cfg.nb)]
                 outs = [torch.empty_like(blocks[0][0]) for _ in range(cfg.nb)]
-                S = torch.zeros((B, H, d, d), device=dev)
-                z = torch.zeros((B, H, d), device=dev)
-                self.sets.append((blocks, outs, S, z))
+                states = [(torch.zeros((B, H, d, d), device=dev), torch.zeros((B, H, d), device=dev))
+                          for _ in range(nbuf)]
+                self.sets.append((blocks, outs, states))
             else:
                 q, k, v = (Q, K, V) if r == 0 else (Q.clone(), K.clone(), V.clone())
                 self.sets.append((q, k, v, torch.empty_like(q)))
@@ -103,8 +134,11 @@ class Workload:
         if self.stream_mode:
             self.ws = torch.empty(svla.workspace_size("block_step", torch.bfloat16, B, H, 1,
                                                       cfg.n, d), dtype=torch.uint8, device=dev)
-            self.frames = cfg.n // (cfg.rope.grid_h * cfg.rope.grid_w)
-            self.ropes = [cfg.rope.with_t0(self.frames * s) for s in range(cfg.nb)]
+            self.frames = cfg.n // (cfg.rope.grid_h * cfg.rope.grid_w) if cfg.rope else 0
+            self.ropes = [cfg.rope.with_t0(self.frames * s) if cfg.rope else None
+                          for s in range(cfg.nb)]
+            self.gs = [None if self.g is None else self.g[:, :, s].contiguous()
+                       for s in range(cfg.nb)]
         else:
             op = "noncausal" if cfg.nb == 1 else "block_causal"
             self.ws = torch.empty(svla.workspace_size(op, torch.bfloat16, B, H, cfg.nb, cfg.n, d),
@@ -120,30 +154,38 @@ class Workload:
 
     def algorithmic_bytes(self) -> dict:
         """Bytes the method must move (Q, K, V read once, O written once; the
-        carried state read and written once per streaming step)."""
+        carried state read and written once per streaming step).  Per launch
+        of each kernel: the state build K and V, the read-out Q and O, the
+        one-launch step all four plus the state; the scan nothing."""
         e = 2
         t = self.B * self.H * self.N * self.d * e
-        per_launch = {"build": 2 * t, "apply": 2 * t, "scan": 0}
         state = self.B * self.H * (self.d * self.d + self.d) * 4
+        per_launch = {"build": 2 * t, "apply": 2 * t, "scan": 0, "step": 4 * t}
         if self.stream_mode:
             per_launch = {k: v // self.nb for k, v in per_launch.items()}
-            per_launch["scan"] = 2 * state
+            per_launch["step"] += 2 * state
             path = 4 * t + 2 * state * self.nb
         else:
             path = 4 * t
         return {"per_launch": per_launch, "path": path}
 
+    def block_step(self, r: int, s: int):
+        """Block s of rotating set r; the state starts from zero at block 0."""
+        blocks, outs, states = self.sets[r]
+        S, z = states[s % len(states)]
+        S_next, z_next = states[(s + 1) % len(states)]
+        q, k, v = blocks[s]
+        self.svla.block_step(q, k, v, S if s else None, z if s else None, S_out=S_next,
+                             z_out=z_next, g=self.gs[s], rope=self.ropes[s], out=outs[s],
+                             workspace=self.ws)
+
     def stream_pass(self, r: int):
-        """The 80 block steps of one video; the state starts from zero."""
-        blocks, outs, S, z = self.sets[r]
         for s in range(self.nb):
-            q, k, v = blocks[s]
-            self.svla.block_step(q, k, v, S if s else None, z if s else None, S_out=S, z_out=z,
-                                 rope=self.ropes[s], out=outs[s], workspace=self.ws)
+            self.block_step(r, s)
 
     def capture(self):
-        """Streaming mode: capture each set's pass in a HIP graph (the 240
-        launches of a pass would otherwise be bound by host launch cost)."""
+        """Streaming: capture each set's pass in a HIP graph (the launches of a
+        pass would otherwise be bound by host launch cost)."""
         torch = self.torch
         self.graphs = []
         side = torch.cuda.Stream()
@@ -162,26 +204,30 @@ class Workload:
 
     def step(self, i: int):
         svla = self.svla
+        r = i % len(self.sets)
         if self.stream_mode:
-            r = i % len(self.sets)
             if getattr(self, "graphs", None):
                 self.graphs[r].replay()
             else:
                 self.stream_pass(r)
         else:
-            q, k, v, o = self.sets[i % len(self.sets)]
+            q, k, v, o = self.sets[r]
             if self.nb == 1:
                 svla.noncausal(q, k, v, out=o, workspace=self.ws)
             else:
                 svla.block_causal(q, k, v, self.nb, g=self.g, rope=self.cfg.rope, out=o,
                                   workspace=self.ws)
 
-    def describe_plan(self) -> dict:
-        """The library's launch plan for one call of this workload."""
+    def plan(self) -> dict:
+        """The library's launch plan for one call of this workload, as taken."""
         torch = self.torch
         if self.stream_mode:
-            return self.svla.describe("block_step", torch.bfloat16, self.B, self.H, 1, self.n,
-                                      self.d, rope=self.ropes[0])
+            p = self.svla.describe("block_step", torch.bfloat16, self.B, self.H, 1, self.n,
+                                   self.d, rope=self.ropes[0])
+            if self.mode == "stream_inplace" and p.get("fused"):
+                p["kernels"] = p["in_place_kernels"]
+                p["fused"] = False
+            return p
         op = "noncausal" if self.nb == 1 else "block_causal"
         return self.svla.describe(op, torch.bfloat16, self.B, self.H, self.nb, self.n, self.d,
                                   rope=self.cfg.rope)
@@ -191,9 +237,14 @@ class Workload:
         d = {"workload": "%s: %s" % (c.name, c.description), "B": c.B, "H": c.H, "N": c.N,
              "d": c.d, "blocks": c.nb, "block_tokens": c.n, "input_dtype": c.dtype,
              "rope": c.rope is not None, "gated": c.gated, "rotating_input_sets": len(self.sets)}
-        if c.name == "c4":
-            d["c4_mode"] = ("80 sequential block steps (HIP graph per pass)" if self.stream_mode
-                            else "one-shot call over the 80 blocks")
+        if self.mode == "stream":
+            d["mode"] = ("%d sequential block steps per step (one HIP graph per pass), the state "
+                         "committed into the other of two buffers" % c.nb)
+        elif self.mode == "stream_inplace":
+            d["mode"] = ("%d sequential block steps per step (one HIP graph per pass), the state "
+                         "committed in place" % c.nb)
+        else:
+            d["mode"] = "one call over all %d blocks" % c.nb
         return d
 
 
@@ -215,28 +266,40 @@ def settle(w: Workload, seconds: float) -> int:
     return n
 
 
-def time_steps(w: Workload, steps: int, warmup: int) -> float:
+def _pct(xs, p):
+    xs = sorted(xs)
+    k = (len(xs) - 1) * p / 100.0
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def time_steps(w: Workload, steps: int, warmup: int) -> dict:
+    """K steps between two device synchronisations, an event before each step
+    and one after the last: the mean over the whole bracket, and the median,
+    p10 and p90 of the single steps (ms)."""
     torch = w.torch
     for i in range(warmup):
         w.step(i)
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        w.step(i)
-    t1.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps       # ms per step
+    for i in range(steps):
+        ev[i].record()
+        w.step(i)
+    ev[steps].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return {"mean_ms": ev[0].elapsed_time(ev[steps]) / steps, "median_ms": _pct(per, 50),
+            "p10_ms": _pct(per, 10), "p90_ms": _pct(per, 90)}
 
 
 def time_kernels(w: Workload, steps: int) -> dict:
     """Average duration (ms) per launch of each kernel, from HIP events the
-    library records between its own launches, on the launch stream."""
+    library records around its own launches, on the launch stream."""
     torch, svla = w.torch, w.svla
-    per_step = w.launches_per_step()
     total = {k: 0.0 for k in KERNEL_SLOTS}
     count = 0
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(KERNEL_SLOTS))]
     for e in ev:
         e.record()
     torch.cuda.synchronize()
@@ -244,12 +307,9 @@ def time_kernels(w: Workload, steps: int) -> dict:
     try:
         for i in range(steps):
             if w.stream_mode:
-                # eager, one block step at a time, so the 6 events describe one launch set
-                blocks, outs, S, z = w.sets[i % len(w.sets)]
+                # eager, one block step at a time, so the events describe one launch set
                 for s in range(w.nb):
-                    q, k, v = blocks[s]
-                    svla.block_step(q, k, v, S if s else None, z if s else None, S_out=S,
-                                    z_out=z, rope=w.ropes[s], out=outs[s], workspace=w.ws)
+                    w.block_step(i % len(w.sets), s)
                     torch.cuda.synchronize()
                     for name, (a, b) in KERNEL_SLOTS.items():
                         total[name] += ev[a].elapsed_time(ev[b])
@@ -262,13 +322,14 @@ def time_kernels(w: Workload, steps: int) -> dict:
                 count += 1
     finally:
         svla.set_timing_events(None)
-    assert count == steps * per_step
+    assert count == steps * w.launches_per_step()
     return {k: v / count for k, v in total.items()}
 
 
-def cpu_baseline(w: Workload, budget_s: float = 10.0) -> dict:
+def cpu_baseline(w: Workload, budget_s: float = 10.0, single_thread: bool = False) -> dict:
     """The fp64 oracle, as it stands, on the host cores: the full workload,
-    repeated until about `budget_s` seconds of wall time have passed."""
+    repeated until about `budget_s` seconds of wall time have passed.  With
+    single_thread, also one thread on a bounded sample of heads."""
     import numpy as np
     import oracle
 
@@ -282,24 +343,80 @@ def cpu_baseline(w: Workload, budget_s: float = 10.0) -> dict:
         secs += r["seconds"]
         used = r["threads"]
         reps += 1
-    return {"value": reps * w.tokens_heads / secs, "unit": UNIT, "cores": used,
-            "kind": "oracle",
-            "sample": "%d full run(s) of %s (%d tokens x %d heads x batch %d, fp64, one-shot "
-                      "over all %d blocks), %.1f s on %d host threads"
-                      % (reps, w.name, w.N, w.H, w.B, w.cfg.nb, secs, used)}
+    out = {"value": reps * w.tokens_heads / secs, "unit": UNIT, "cores": used,
+           "kind": "oracle", "affinity_cores": threads,
+           "sample": "%d full run(s) of %s (%d tokens x %d heads x batch %d, fp64, one call "
+                     "over all %d blocks), %.1f s on %d host threads"
+                     % (reps, w.name, w.N, w.H, w.B, w.cfg.nb, secs, used)}
+    if single_thread:
+        hs = slice(0, max(1, w.H // 7))
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[:, hs])
+        r = oracle.forward(sub(Q), sub(K), sub(V), w.cfg.nb, g=sub(x["g"]), rope=w.cfg.rope,
+                           eps=x["eps"], threads=1)
+        th = w.B * (hs.stop - hs.start) * w.N
+        out["single_thread"] = {"value": th / r["seconds"], "unit": UNIT, "cores": r["threads"],
+                                "sample": "%d of %d heads of %s on one thread, %.1f s"
+                                          % (hs.stop - hs.start, w.H, w.name, r["seconds"])}
+    return out
 
 
-def load_traffic(config: str, kernel: str, launches_per_step: int):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when the summary is missing or the kernels changed since."""
-    path = os.path.join(ROOT, "profiles", "counters_%s.json" % config)
+def _load_summary(prefix: str, tag: str):
+    path = os.path.join(ROOT, "profiles", "%s_%s.json" % (prefix, tag))
     if not os.path.exists(path):
         return None
     c = json.load(open(path))
     if c.get("source_sha256") != source_hash():
-        return None
-    k = c.get("kernels", {}).get(kernel)
+        return None          # the kernels changed since the counters were taken
+    return c
+
+
+def load_traffic(tag: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when the summary is missing or the kernels changed since."""
+    c = _load_summary("counters", tag)
+    k = None if c is None else c.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_dispatch")
+
+
+def load_mfma(tag: str, kernel: str):
+    c = _load_summary("mfma", tag)
+    return None if c is None else c.get("kernels", {}).get(kernel)
+
+
+def measure(w: Workload, args, settle_s: float) -> dict:
+    """Timing of K steps, per-kernel times, roofline of the dominant kernel."""
+    if w.stream_mode:
+        w.capture()
+    settled = settle(w, settle_s) if settle_s > 0 else 0
+    t = time_steps(w, args.steps, args.warmup)
+    plan = w.plan()
+    used = {k["slot"] for k in plan["kernels"]}
+    # a call that folds the scan into the apply launches no scan kernel
+    kern = {k: v for k, v in time_kernels(w, max(5, min(args.steps, 50))).items() if k in used}
+    ab = w.algorithmic_bytes()
+    dominant = max((k for k in ("build", "apply", "step") if k in kern), key=lambda k: kern[k])
+    dur_s = kern[dominant] * 1e-3
+    achieved = ab["per_launch"][dominant] / dur_s / 1e9
+    kernel_full = {k["slot"]: k["name"] for k in plan["kernels"]}[dominant]
+    tag = w.name + ("_" + w.mode if w.name == "c4" else "")
+    ms = t["mean_ms"]
+    path_gbps = ab["path"] / (ms * 1e-3) / 1e9
+    mf = load_mfma(tag, kernel_full)
+    return {
+        "settle_steps": settled, "ms_per_step": ms, "value": w.tokens_heads / (ms * 1e-3),
+        "timing": {k: t[k] for k in ("median_ms", "p10_ms", "p90_ms")},
+        "roofline": {"bound": "hbm", "kernel": kernel_full, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic(tag, kernel_full),
+                     "algorithmic_bytes_per_launch": ab["per_launch"][dominant],
+                     "avg_launch_ms": kern[dominant]},
+        "path": {"algorithmic_bytes_per_step": ab["path"], "achieved_GBps": path_gbps,
+                 "frac_of_peak": path_gbps / HBM_PEAK_GBPS,
+                 "kernel_ms_per_launch": kern, "launches_per_step": w.launches_per_step(),
+                 "plan": plan},
+        "mfma": mf,
+        "counter_tag": tag,
+    }
 
 
 # ---------------------------------------------------------------------------
@@ -330,7 +447,7 @@ def _per_kernel(rows, counter):
     return {k: sum(v.values()) / len(v) for k, v in acc.items()}
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, config):
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, tag):
     fetch = _per_kernel(_pmc_rows(fetch_dir), "FETCH_SIZE")
     write = _per_kernel(_pmc_rows(write_dir), "WRITE_SIZE")
     cf = _per_kernel(_pmc_rows(copy_fetch_dir), "FETCH_SIZE")
@@ -339,17 +456,38 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, con
     copy_name = max(cf, key=cf.get)
     f_factor = COPY_BYTES / (cf[copy_name] * 1024.0)
     w_factor = COPY_BYTES / (cw[copy_name] * 1024.0)
-    out = {"source_sha256": source_hash(), "config": config,
+    out = {"source_sha256": source_hash(), "tag": tag,
            "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
            "fetch_factor": f_factor, "write_factor": w_factor, "kernels": {}}
     for k in sorted(set(fetch) | set(write)):
-        if not k.startswith("void svla") and "svla" not in k:
+        if "svla" not in k:
             continue
         fb = fetch.get(k, 0.0) * 1024.0 * f_factor
         wb = write.get(k, 0.0) * 1024.0 * w_factor
         out["kernels"][k] = {"fetch_kib": fetch.get(k), "write_kib": write.get(k),
                              "hbm_bytes_per_dispatch": fb + wb}
-    path = os.path.join(ROOT, "profiles", "counters_%s.json" % config)
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % tag)
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def summarize_mfma(mdir, tag):
+    """Matrix-core and vector-ALU use per dispatch from one rocprofv3 --pmc
+    pass of MFMA_COUNTERS: MFMA busy percent of the SIMD cycles, bf16 MFMA
+    flops, VALU busy percent, and the dispatch's GPU-active cycles."""
+    rows = _pmc_rows(mdir)
+    vals = {c: _per_kernel(rows, c) for c in MFMA_COUNTERS}
+    out = {"source_sha256": source_hash(), "tag": tag, "counters": list(MFMA_COUNTERS),
+           "kernels": {}}
+    for k in sorted(vals["GRBM_GUI_ACTIVE"]):
+        if "svla" not in k:
+            continue
+        ent = {c: vals[c].get(k) for c in MFMA_COUNTERS}
+        ent["mfma_busy_frac"] = None if ent["MfmaUtil"] is None else ent["MfmaUtil"] / 100.0
+        ent["valu_busy_frac"] = None if ent["VALUBusy"] is None else ent["VALUBusy"] / 100.0
+        out["kernels"][k] = ent
+    path = os.path.join(ROOT, "profiles", "mfma_%s.json" % tag)
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
@@ -366,11 +504,48 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "dispatches": 3}))
 
 
+def ceiling(reps: int = 20):
+    """Achievable HBM rates on this GPU: a device-to-device copy of 2 GiB
+    (reads + writes) and a read-only reduction over 2 GiB, each the median of
+    `reps` event-timed runs over four rotating buffers (8 GiB, far past the
+    256 MB Infinity Cache)."""
+    import torch
+    nbytes = 2 << 30
+    src = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda:0") for _ in range(4)]
+    dst = [torch.empty_like(s) for s in src]
+    out = torch.empty((), dtype=torch.float32, device="cuda:0")
+
+    def med(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return _pct(ts, 50)
+
+    t_copy = med(lambda i: dst[i % 4].copy_(src[i % 4]))
+    t_read = med(lambda i: torch.sum(src[i % 4], dtype=torch.float32, out=out))
+    res = {"copy_GBps": 2 * nbytes / (t_copy * 1e-3) / 1e9, "read_GBps": nbytes / (t_read * 1e-3) / 1e9,
+           "copy_ms": t_copy, "read_ms": t_read, "bytes": nbytes, "peak_GBps": HBM_PEAK_GBPS}
+    res["copy_frac"] = res["copy_GBps"] / HBM_PEAK_GBPS
+    res["read_frac"] = res["read_GBps"] / HBM_PEAK_GBPS
+    print(json.dumps(res), flush=True)
+
+
 # ---------------------------------------------------------------------------
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, config=args.config)
+        summarize_counters(*args.summarize_counters, tag=args.tag or args.config)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, tag=args.tag or args.config)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: measures one GPU only (the path shards by (batch, head) with no "
@@ -384,51 +559,58 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.ceiling:
+        ceiling()
+        return
 
-    w = Workload(args.config, args.rotate, args.c4_mode)
-    if w.stream_mode:
-        w.capture()
-    settled = settle(w, args.settle) if args.settle > 0 else 0
-    ms = time_steps(w, args.steps, args.warmup)
-    plan = w.describe_plan()
-    used = {k["slot"] for k in plan["kernels"]}
-    # a call that folds the scan into the apply launches no scan kernel
-    kern = {k: v for k, v in time_kernels(w, max(5, min(args.steps, 50))).items() if k in used}
-    ab = w.algorithmic_bytes()
-    dominant = max(("build", "apply"), key=lambda k: kern[k])
-    dur_s = kern[dominant] * 1e-3
-    achieved = ab["per_launch"][dominant] / dur_s / 1e9
-    kernel_full = {k["slot"]: k["name"] for k in plan["kernels"]}[dominant]
-    traffic = load_traffic(args.config, kernel_full, w.launches_per_step())
-    path_gbps = ab["path"] / (ms * 1e-3) / 1e9
+    from workloads import CONFIGS, make_inputs
+    x = make_inputs(CONFIGS[args.config])
+    c4 = args.config == "c4"
+    stream_mode = "stream_inplace" if args.inplace else "stream"
+    primary = stream_mode if (c4 and args.c4_mode in ("both", "stream")) else "oneshot"
+    w = Workload(args.config, args.rotate, primary, x=x)
+    m = measure(w, args, args.settle)
     line = {
         "metric": METRIC,
-        "value": w.tokens_heads / (ms * 1e-3),
+        "value": m["value"],
         "unit": UNIT,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "settle_steps": settled,
-        "ms_per_step": ms,
+        "settle_steps": m["settle_steps"],
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), bf16-rounded; shapes of the pages' video workloads)",
         "config": w.describe(),
-        "roofline": {"bound": "hbm", "kernel": kernel_full, "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": ab["per_launch"][dominant],
-                     "avg_launch_ms": kern[dominant]},
-        "path": {"algorithmic_bytes_per_step": ab["path"], "achieved_GBps": path_gbps,
-                 "frac_of_peak": path_gbps / HBM_PEAK_GBPS,
-                 "kernel_ms_per_launch": kern, "launches_per_step": w.launches_per_step(),
-                 "plan": plan},
+        "timing": m["timing"],
+        "roofline": m["roofline"],
+        "path": m["path"],
+        "mfma": m["mfma"],
         "source_sha256": source_hash(),
     }
+    if c4 and args.c4_mode == "both":
+        del w
+        torch.cuda.empty_cache()
+        w1 = Workload(args.config, args.rotate, "oneshot", x=x)
+        m1 = measure(w1, args, 0.1)
+        line["c4_oneshot"] = {k: m1[k] for k in ("value", "ms_per_step", "timing", "roofline",
+                                                 "path", "mfma")}
+        line["c4_oneshot"]["config"] = w1.describe()
+        w = w1
+    if c4 or args.config == "c3":
+        fr = {"stream": line["path"]["frac_of_peak"]} if primary != "oneshot" else {}
+        if "c4_oneshot" in line:
+            fr["oneshot"] = line["c4_oneshot"]["path"]["frac_of_peak"]
+        elif primary == "oneshot":
+            fr["oneshot"] = line["path"]["frac_of_peak"]
+        carried = "stream" if fr.get("stream", 0.0) >= GATE_FRAC else "oneshot" if "oneshot" in fr else "stream"
+        line["gate"] = {"target_frac_of_peak": GATE_FRAC, "path_frac": fr, "carried_by": carried,
+                        "met": fr.get(carried, 0.0) >= GATE_FRAC}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = cpu_baseline(w, single_thread=args.config == "c3")
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
