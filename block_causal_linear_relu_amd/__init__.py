@@ -24,7 +24,8 @@ import torch
 from . import _lib
 from ._lib import SvlaError, rope_struct  # noqa: F401
 
-__all__ = ["noncausal", "block_causal", "block_step", "state_build", "state_scan", "apply",
+__all__ = ["noncausal", "block_causal", "block_step", "block_step_noalloc", "state_build",
+           "state_scan", "apply",
            "workspace_size", "describe", "set_timing_events", "SvlaError", "library"]
 
 _DT = {torch.bfloat16: _lib.SVLA_BF16, torch.float32: _lib.SVLA_F32}
@@ -240,6 +241,34 @@ def block_step(Q, K, V, S_in=None, z_in=None, S_out=None, z_out=None, g=None, ro
                                        rp, float(eps), _ptr(ws), nbytes, _stream(Q.device))
     _lib.check(lib, st)
     return O, S_out, z_out
+
+
+def block_step_noalloc(Q, K, V, S_in, z_in, S_out, z_out, out, g=None, rope=None,
+                       eps: float = 1e-6):
+    """svla_block_step with the library's own scratch: every output (``out``,
+    ``S_out``, ``z_out``) is passed in and nothing is allocated, here or in
+    the library.  Returns (out, S_out, z_out)."""
+    B, H, n, d = _qkv_shape(Q, K, V)
+    _shape(S_in, (B, H, d, d), "S_in")
+    _shape(z_in, (B, H, d), "z_in")
+    _shape(S_out, (B, H, d, d), "S_out")
+    _shape(z_out, (B, H, d), "z_out")
+    _shape(g, (B, H), "g")
+    _shape(out, Q.shape, "out")
+    _pair(S_in, z_in, "S_in", "z_in")
+    if out is None or S_out is None or z_out is None:
+        raise ValueError("out, S_out and z_out are required (nothing is allocated)")
+    dt = _qkv(Q, K, V)
+    S_in, z_in, g = _opt(S_in, "S_in"), _opt(z_in, "z_in"), _opt(g, "g")
+    _dev(out, "out", Q.dtype)
+    _dev(S_out, "S_out", torch.float32)
+    _dev(z_out, "z_out", torch.float32)
+    lib = library()
+    rp, _keep = _rope_arg(rope)
+    _lib.check(lib, lib.svla_block_step_noalloc(dt, B, H, n, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(out),
+                                                _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                                                _ptr(g), rp, float(eps), _stream(Q.device)))
+    return out, S_out, z_out
 
 
 def state_build(K, V, nb: int, rope=None):

@@ -51,6 +51,8 @@ PROTOTYPES = {
                              _vp, _sz, _vp]),
     "svla_block_step_gated": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _rp, _f, _vp, _sz, _vp]),
+    "svla_block_step_noalloc": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _rp, _f, _vp]),
     "svla_state_build": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _rp, _vp, _vp, _vp, _sz, _vp]),
     "svla_state_scan": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "svla_apply": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _rp, _f, _vp, _vp, _sz, _vp]),

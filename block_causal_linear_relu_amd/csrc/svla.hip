@@ -26,6 +26,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <type_traits>
 #include <math.h>
 #include <stdarg.h>
@@ -2779,7 +2780,7 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
                     int d, const void *Q, const void *K, const void *V, void *O,
                     const float *S0, const float *z0, float *S_fin, float *z_fin,
                     const float *g, const svla_rope *rope, float eps, void *ws,
-                    size_t ws_bytes, svla_stream stream)
+                    size_t ws_bytes, svla_stream stream, bool dry = false)
 {
     Plan p;
     svla_status st = make_plan(fn, op, dt, B, H, nb, n, d, rope, &p);
@@ -2800,6 +2801,7 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
     if (ws_bytes < p.total)
         return fail(SVLA_ERR_WORKSPACE, fn, "workspace of %zu bytes is smaller than the %zu needed",
                     ws_bytes, p.total);
+    if (dry) return SVLA_OK;           // validation only (no HIP call made)
 
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
@@ -2854,6 +2856,58 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
         apply_any(p, aa, s);
         if ((st = check_launch(fn))) return st;
     }
+    return SVLA_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The scratch of svla_block_step_noalloc: device memory that the library holds
+// for callers that cannot allocate (one copy per GPU, from module load until
+// the process ends).  In host code `scratch` names a host-side stand-in, not
+// the device address: the address comes from hipGetSymbolAddress, resolved
+// once per device with that device current and kept in g_scratch_ptr.
+// Every call on a GPU shares that GPU's copy and leaves its content behind;
+// the block step needs nothing in it to start at zero.  Calls that overlap on
+// one GPU race on it.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device of `stream` (which must be the current
+// device: its copy of `scratch` is resolved with that device current).
+svla_status scratch_for(const char *fn, svla_stream stream, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SVLA_ERR_HIP, fn, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (stream) {
+        hipDevice_t sd = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &sd);
+        if (e != hipSuccess)
+            return fail(SVLA_ERR_HIP, fn, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+        if ((int)sd != dev)
+            return fail(SVLA_ERR_VALUE, fn, "the stream belongs to device %d, the current device is %d",
+                        (int)sd, dev);
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SVLA_ERR_UNSUPPORTED, fn, "device %d is beyond the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(SVLA_ERR_HIP, fn, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return SVLA_OK;
 }
 
@@ -3010,6 +3064,31 @@ svla_status svla_block_step_gated(svla_dtype dt, int B, int H, int n, int d, con
     if (!g && (long)B * H > 0) return fail(SVLA_ERR_NULL, fn, "g is required");
     return forward(fn, SVLA_OP_BLOCK_STEP, dt, B, H, 1, n, d, Q, K, V, O, S_in, z_in, S_out,
                    z_out, g, rope, eps, ws, ws_bytes, stream);
+}
+
+svla_status svla_block_step_noalloc(svla_dtype dt, int B, int H, int n, int d, const void *Q,
+                                    const void *K, const void *V, void *O, const float *S_in,
+                                    const float *z_in, float *S_out, float *z_out,
+                                    const float *g, const svla_rope *rope, float eps,
+                                    svla_stream stream)
+{
+    const char *fn = "svla_block_step_noalloc";
+    Plan p;
+    svla_status st = make_plan(fn, SVLA_OP_BLOCK_STEP, dt, B, H, 1, n, d, rope, &p);
+    if (st) return st;
+    if (p.total > kScratchBytes)
+        return fail(SVLA_ERR_WORKSPACE, fn, "this step needs %zu bytes of scratch; the library holds %zu "
+                    "per device", p.total, kScratchBytes);
+    // every check of the call first (an aligned stand-in for the scratch
+    // address, which is only checked, never used), then the first HIP call
+    void *const stand_in = (void *)(uintptr_t)256;
+    st = forward(fn, SVLA_OP_BLOCK_STEP, dt, B, H, 1, n, d, Q, K, V, O, S_in, z_in, S_out, z_out, g,
+                 rope, eps, stand_in, kScratchBytes, stream, true);
+    if (st || p.BH == 0) return st;
+    void *ws = nullptr;
+    if ((st = scratch_for(fn, stream, &ws))) return st;
+    return forward(fn, SVLA_OP_BLOCK_STEP, dt, B, H, 1, n, d, Q, K, V, O, S_in, z_in, S_out, z_out, g,
+                   rope, eps, ws, kScratchBytes, stream);
 }
 
 svla_status svla_state_build(svla_dtype dt, int B, int H, int nb, int n, int d, const void *K,

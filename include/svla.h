@@ -199,6 +199,24 @@ svla_status svla_block_step_gated(svla_dtype dt, int B, int H, int n, int d,
                                   const float *g, const svla_rope *rope, float eps,
                                   void *ws, size_t ws_bytes, svla_stream stream);
 
+/* For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): svla_block_step (g NULL) or svla_block_step_gated (g [B,H]
+ * non-NULL) with the library's own scratch instead of a caller workspace.
+ * The scratch is 32 MiB per GPU, held from the library's load until the
+ * process ends; a step whose svla_workspace_size(SVLA_OP_BLOCK_STEP, ...) is
+ * larger returns SVLA_ERR_WORKSPACE.  The call allocates nothing.  `stream`
+ * must belong to the current device (NULL = its default stream), otherwise
+ * SVLA_ERR_VALUE.  Every call on a GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  Validation runs before any HIP call, as elsewhere. */
+svla_status svla_block_step_noalloc(svla_dtype dt, int B, int H, int n, int d,
+                                    const void *Q, const void *K, const void *V, void *O,
+                                    const float *S_in, const float *z_in,
+                                    float *S_out, float *z_out,
+                                    const float *g, const svla_rope *rope, float eps,
+                                    svla_stream stream);
+
 /* ---- the three kernels, one by one ------------------------------------------ */
 
 /* Each block's own contribution: S_local [B,H,nb,d,d] = sum_j R_j phi(k_j) (x) v_j,

@@ -181,3 +181,25 @@ def test_workspace_covers_every_plan():
                 assert rot["step_tiles"] * rot["step_tile"] >= n
         else:
             assert plain["fused"] is False and "in_place_kernels" not in plain
+
+
+def test_noalloc_step_validates_before_any_hip_call(lib):
+    """The no-alloc block step rejects a step whose workspace exceeds the
+    library's scratch, and bad arguments, on the host (no GPU here)."""
+    A = ctypes.c_void_p(4096)        # aligned stand-ins; never dereferenced on a rejection
+    MIS = ctypes.c_void_p(4100)
+    f = lib.svla_block_step_noalloc
+    # 40 heads of 8192 tokens at d = 128 need about 34 MiB of scratch (> 32 MiB)
+    assert f(_lib.SVLA_BF16, 1, 40, 8192, 128, A, A, A, A, None, None, A, A, None, None,
+             1e-6, None) == 6
+    assert b"scratch" in lib.svla_last_error()
+    assert f(_lib.SVLA_BF16, 1, 2, 64, 32, A, A, A, A, None, None, None, None, None, None,
+             1e-6, None) == 1                                  # S_out, z_out required
+    assert f(_lib.SVLA_BF16, 1, 2, 64, 32, A, A, A, MIS, None, None, A, A, None, None,
+             1e-6, None) == 4                                  # misaligned O
+    assert f(_lib.SVLA_BF16, 1, 2, 64, 48, A, A, A, A, None, None, A, A, None, None,
+             1e-6, None) == 5                                  # d = 48
+    assert f(_lib.SVLA_BF16, 1, 2, 64, 32, A, A, A, A, None, None, A, A, None, None,
+             -1.0, None) == 7                                  # eps < 0
+    assert f(_lib.SVLA_BF16, 0, 2, 64, 32, None, None, None, None, None, None, None, None,
+             None, None, 1e-6, None) == 0                      # empty: nothing to do
