@@ -27,6 +27,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
+    "ConvConfig", "CONV_CONFIGS", "make_conv_inputs",
     "Rope", "Config", "CONFIGS", "get_config", "bf16_round", "bf16_bits",
     "bf16_from_bits", "make_inputs", "scaled_config",
 ]
@@ -165,3 +166,72 @@ def make_inputs(cfg: Config, seed: Optional[int] = None, *, B=None, H=None,
 def step_slice(x: np.ndarray, step: int, n: int) -> np.ndarray:
     """Tokens of block ``step`` of a [B,H,N,d] array, as a contiguous copy."""
     return np.ascontiguousarray(x[:, :, step * n:(step + 1) * n, :])
+
+
+# ---------------------------------------------------------------------------
+# the causal temporal convolution of the Mix-FFN (block-boundary cache)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class ConvConfig:
+    """X [B, T, P, C]: T = nb * F latent frames in blocks of F, P = grid_h *
+    grid_w positions, C channels (C fastest)."""
+    name: str
+    B: int
+    nb: int
+    F: int
+    grid_h: int
+    grid_w: int
+    C: int
+    dtype: str
+    seed: int
+    streaming: bool = False
+    description: str = ""
+
+    @property
+    def T(self) -> int:
+        return self.nb * self.F
+
+    @property
+    def P(self) -> int:
+        return self.grid_h * self.grid_w
+
+
+# C = 2240 is the model width of the attention workloads above (70 heads x 32)
+CONV_CONFIGS = {
+    "t1": ConvConfig("t1", B=1, nb=2, F=2, grid_h=3, grid_w=4, C=24, dtype="f32", seed=11,
+                     description="tiny fp32 parity case, 2 blocks of 2 frames x 3x4, 24 channels"),
+    "t3": ConvConfig("t3", B=1, nb=7, F=3, grid_h=22, grid_w=40, C=2240, dtype="bf16", seed=13,
+                     description="720p 5 s one call, 7 blocks of 3 frames x 22x40, 2240 channels"),
+    "t4": ConvConfig("t4", B=1, nb=80, F=3, grid_h=15, grid_w=26, C=2240, dtype="bf16", seed=14,
+                     streaming=True,
+                     description="minute-long 480p stream, 80 steps of 3 frames x 15x26, 2240 channels"),
+}
+
+
+def make_conv_inputs(cfg: ConvConfig, seed: Optional[int] = None, *, B=None, nb=None, F=None,
+                     P=None, C=None) -> dict:
+    """Draw X ~ N(0,1) [B, T, P, C] (bf16-exact for bf16 configs; raw bits in
+    X_bits), depthwise taps w [C, 3] ~ N(0, 1/3) and bias [C] ~ N(0, 0.01) as
+    fp32, and a cache frame [B, P, C] ~ N(0,1) (storage-type exact), in that
+    order, from default_rng(seed)."""
+    B = cfg.B if B is None else B
+    nb = cfg.nb if nb is None else nb
+    F = cfg.F if F is None else F
+    P = cfg.P if P is None else P
+    C = cfg.C if C is None else C
+    T = nb * F
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    out = {"cfg": cfg, "B": B, "nb": nb, "F": F, "T": T, "P": P, "C": C, "dtype": cfg.dtype}
+    x = rng.standard_normal((B, T, P, C), dtype=np.float32)
+    w = (rng.standard_normal((C, 3)) / np.sqrt(3.0)).astype(np.float32)
+    bias = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    cache = rng.standard_normal((B, P, C), dtype=np.float32)
+    if cfg.dtype == "bf16":
+        out["X_bits"] = bf16_bits(x)
+        out["X"] = bf16_from_bits(out["X_bits"])
+        out["cache_bits"] = bf16_bits(cache)
+        out["cache"] = bf16_from_bits(out["cache_bits"])
+    else:
+        out["X"], out["cache"] = x, cache
+    out["w"], out["bias"] = w, bias
+    return out
