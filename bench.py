@@ -53,7 +53,9 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 GATE_FRAC = 0.60                # the minute-long and 720p shapes' target fraction of peak HBM
 SOURCE = os.path.join(ROOT, "block_causal_linear_relu_amd", "csrc", "svla.hip")
-KERNEL_SLOTS = {"build": (0, 1), "scan": (2, 3), "apply": (4, 5), "step": (6, 7)}
+KERNEL_SLOTS = {"build": (0, 1), "scan": (2, 3), "apply": (4, 5), "step": (6, 7), "conv": (8, 9)}
+CONV_METRIC = "causal temporal conv frames·positions·channels/s + achieved HBM GB/s vs MI355X peak"
+CONV_UNIT = "frames·positions·channels/s"
 COPY_BYTES = 1 << 29            # 512 MiB read + 512 MiB written
 # one rocprofv3 --pmc pass (3 SQ counters underneath, 1 GRBM): MfmaUtil =
 # 100 * sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs); MfmaFlopsBF16 =
@@ -71,7 +73,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5", "t3", "t4"])
     ap.add_argument("--c4-mode", default="both", choices=["both", "stream", "oneshot"])
     ap.add_argument("--inplace", action="store_true",
                     help="streaming: commit the state in place (the two-kernel step)")
@@ -248,6 +250,110 @@ class Workload:
         return d
 
 
+class ConvWorkload:
+    """The FFN's temporal convolution, causal across blocks: one call over the
+    whole clip, or (streaming) one call per block of F frames with the cache
+    carried in two buffers."""
+
+    def __init__(self, name: str, rotate: int):
+        import torch
+        import block_causal_linear_relu_amd as svla
+        from workloads import CONV_CONFIGS, make_conv_inputs
+
+        self.torch, self.svla = torch, svla
+        self.cfg = cfg = CONV_CONFIGS[name]
+        self.name = name
+        self.mode = "stream" if cfg.streaming else "oneshot"
+        self.stream_mode = cfg.streaming
+        self.x = x = make_conv_inputs(cfg)
+        dev = torch.device("cuda:0")
+        X = torch.from_numpy(x["X"]).to(dev).to(torch.bfloat16)
+        self.w = torch.from_numpy(x["w"]).to(dev)
+        self.b = torch.from_numpy(x["bias"]).to(dev)
+        self.cache0 = torch.from_numpy(x["cache"]).to(dev).to(torch.bfloat16)
+        self.nb, self.F = cfg.nb, cfg.F
+        self.sets = []
+        for r in range(rotate):
+            Xr = X if r == 0 else X.clone()
+            if self.stream_mode:
+                blocks = [Xr[:, s * cfg.F:(s + 1) * cfg.F].contiguous() for s in range(cfg.nb)]
+                outs = [torch.empty_like(blocks[0]) for _ in range(cfg.nb)]
+                caches = [self.cache0.clone(), torch.empty_like(self.cache0)]
+                self.sets.append((blocks, outs, caches))
+            else:
+                self.sets.append((Xr, torch.empty_like(Xr)))
+        torch.cuda.synchronize()
+
+    @property
+    def tokens_heads(self) -> int:              # elements: frames x positions x channels
+        c = self.cfg
+        return c.B * c.T * c.P * c.C
+
+    def launches_per_step(self) -> int:
+        return self.nb if self.stream_mode else 1
+
+    def algorithmic_bytes(self) -> dict:
+        """X read once, Y written once (bf16); the cache frame read (and, when
+        streaming, written) once per call."""
+        c = self.cfg
+        t = c.B * c.T * c.P * c.C * 2
+        frame = c.B * c.P * c.C * 2
+        if self.stream_mode:
+            per = 2 * t // c.nb + 2 * frame
+            return {"per_launch": {"conv": per}, "path": per * c.nb}
+        return {"per_launch": {"conv": 2 * t + frame}, "path": 2 * t + frame}
+
+    def block_step(self, r: int, s: int):
+        blocks, outs, caches = self.sets[r]
+        self.svla.temporal_conv(blocks[s], self.w, self.F, bias=self.b, cache_in=caches[s % 2],
+                                cache_out=caches[(s + 1) % 2], out=outs[s])
+
+    def stream_pass(self, r: int):
+        for s in range(self.nb):
+            self.block_step(r, s)
+
+    capture = Workload.capture
+
+    def step(self, i: int):
+        r = i % len(self.sets)
+        if self.stream_mode:
+            if getattr(self, "graphs", None):
+                self.graphs[r].replay()
+            else:
+                self.stream_pass(r)
+        else:
+            X, Y = self.sets[r]
+            self.svla.temporal_conv(X, self.w, self.F, bias=self.b, cache_in=self.cache0, out=Y)
+
+    def plan(self) -> dict:
+        # the kernel's name as profilers report it (bf16, the library's default chunk length)
+        return {"kernels": [{"slot": "conv", "name": "void svla_temporal_conv_k<2, 4>"}]}
+
+    def describe(self) -> dict:
+        c = self.cfg
+        return {"workload": "%s: %s" % (c.name, c.description), "B": c.B, "frames": c.T,
+                "frames_per_block": c.F, "positions": c.P, "channels": c.C, "input_dtype": c.dtype,
+                "mode": ("%d block steps per step (one HIP graph per pass), the cache in two "
+                         "buffers" % c.nb) if c.streaming else "one call over all %d blocks" % c.nb,
+                "rotating_input_sets": len(self.sets)}
+
+
+def conv_cpu_baseline(w: ConvWorkload, budget_s: float = 10.0) -> dict:
+    """The numpy fp64 oracle of the temporal convolution on the host, repeated
+    over the full workload until about `budget_s` seconds have passed."""
+    from oracle.tconv import temporal_conv
+    x = w.x
+    reps, secs = 0, 0.0
+    while secs < budget_s and reps < 1000:
+        t = time.perf_counter()
+        temporal_conv(x["X"], x["w"], x["F"], bias=x["bias"], cache_in=x["cache"])
+        secs += time.perf_counter() - t
+        reps += 1
+    return {"value": reps * w.tokens_heads / secs, "unit": CONV_UNIT, "cores": 1, "kind": "oracle",
+            "sample": "%d full run(s) of %s (numpy fp64, one call over all %d blocks), %.1f s"
+                      % (reps, w.name, w.nb, secs)}
+
+
 # ---------------------------------------------------------------------------
 # measurements
 # ---------------------------------------------------------------------------
@@ -394,7 +500,7 @@ def measure(w: Workload, args, settle_s: float) -> dict:
     # a call that folds the scan into the apply launches no scan kernel
     kern = {k: v for k, v in time_kernels(w, max(5, min(args.steps, 50))).items() if k in used}
     ab = w.algorithmic_bytes()
-    dominant = max((k for k in ("build", "apply", "step") if k in kern), key=lambda k: kern[k])
+    dominant = max((k for k in ("build", "apply", "step", "conv") if k in kern), key=lambda k: kern[k])
     dur_s = kern[dominant] * 1e-3
     achieved = ab["per_launch"][dominant] / dur_s / 1e9
     kernel_full = {k["slot"]: k["name"] for k in plan["kernels"]}[dominant]
@@ -563,6 +669,19 @@ def main():
         ceiling()
         return
 
+    if args.config.startswith("t"):
+        cw = ConvWorkload(args.config, args.rotate)
+        m = measure(cw, args, args.settle)
+        line = {"metric": CONV_METRIC, "value": m["value"], "unit": CONV_UNIT, "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "settle_steps": m["settle_steps"],
+                "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic (seeded N(0,1), bf16-rounded; random fp32 taps and bias)",
+                "config": cw.describe(), "timing": m["timing"], "roofline": m["roofline"],
+                "path": m["path"], "source_sha256": source_hash(),
+                "cpu_baseline": None if args.no_cpu_baseline else conv_cpu_baseline(cw)}
+        print(json.dumps(line), flush=True)
+        return
     from workloads import CONFIGS, make_inputs
     x = make_inputs(CONFIGS[args.config])
     c4 = args.config == "c4"

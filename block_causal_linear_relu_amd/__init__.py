@@ -25,7 +25,7 @@ from . import _lib
 from ._lib import SvlaError, rope_struct  # noqa: F401
 
 __all__ = ["noncausal", "block_causal", "block_step", "block_step_noalloc", "state_build",
-           "state_scan", "apply",
+           "state_scan", "apply", "temporal_conv",
            "workspace_size", "describe", "set_timing_events", "SvlaError", "library"]
 
 _DT = {torch.bfloat16: _lib.SVLA_BF16, torch.float32: _lib.SVLA_F32}
@@ -269,6 +269,36 @@ def block_step_noalloc(Q, K, V, S_in, z_in, S_out, z_out, out, g=None, rope=None
                                                 _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
                                                 _ptr(g), rp, float(eps), _stream(Q.device)))
     return out, S_out, z_out
+
+
+def temporal_conv(X, w, F: int, bias=None, cache_in=None, cache_out=None, out=None):
+    """The FFN's temporal convolution, causal across blocks of F frames.
+
+    X [B,T,P,C] (bf16 or fp32, C % 8 == 0), w [C,3] and bias [C] float32,
+    cache_in / cache_out [B,P,C] in X's dtype (cache_out receives X's last
+    frame; it may be cache_in itself).  Returns Y (and cache_out if given)."""
+    if not isinstance(X, torch.Tensor) or X.dim() != 4:
+        raise ValueError("X must be a [B,T,P,C] tensor")
+    B, T, P, C = X.shape
+    if F <= 0 or T % F:
+        raise ValueError("T=%d is not a multiple of F=%d" % (T, F))
+    _shape(w, (C, 3), "w")
+    _shape(bias, (C,), "bias")
+    _shape(cache_in, (B, P, C), "cache_in")
+    _shape(cache_out, (B, P, C), "cache_out")
+    _shape(out, X.shape, "out")
+    _dev(X, "X")
+    dt = _dtype(X)
+    _dev(w, "w", torch.float32)
+    bias = _opt(bias, "bias")
+    cache_in = None if cache_in is None else _dev(cache_in, "cache_in", X.dtype)
+    cache_out = None if cache_out is None else _dev(cache_out, "cache_out", X.dtype)
+    Y = torch.empty_like(X) if out is None else _dev(out, "out", X.dtype)
+    lib = library()
+    _lib.check(lib, lib.svla_temporal_conv(dt, B, T // F, F, P, C, _ptr(X), _ptr(Y), _ptr(w),
+                                           _ptr(bias), _ptr(cache_in), _ptr(cache_out),
+                                           _stream(X.device)))
+    return Y if cache_out is None else (Y, cache_out)
 
 
 def state_build(K, V, nb: int, rope=None):

@@ -103,6 +103,15 @@
 #ifndef SVLA_APPLY_XCD
 #define SVLA_APPLY_XCD 1           // apply: the token tiles of one block on one XCD
 #endif
+#ifndef SVLA_TCONV_MAXF
+#define SVLA_TCONV_MAXF 4          // temporal convolution: frames per chunk (loads in flight per thread)
+#endif
+#ifndef SVLA_TCONV_XAUX
+#define SVLA_TCONV_XAUX 2          // ... cache policy of the X loads (non-temporal: read once)
+#endif
+#ifndef SVLA_TCONV_YAUX
+#define SVLA_TCONV_YAUX 2          // ... and of the Y stores (non-temporal)
+#endif
 #ifndef SVLA_FUSED_MAX_N
 #define SVLA_FUSED_MAX_N 2048      // one-launch block step (bf16, d = 32): longest block
 #endif
@@ -2344,6 +2353,184 @@ svla_step_fused(const StepArgs a)
         store16p<SVLA_O_AUX>(rO, valid ? (uint32_t)(tok * D + op_col(0, 4 * kg)) * 2u : kOOB, o);
     }
 }
+// ---------------------------------------------------------------------------
+// svla_temporal_conv: the Mix-FFN's temporal convolution made causal across
+// blocks.  y[t,p,c] = bias[c] + w[c][0] x[t-1,p,c] + w[c][1] x[t,p,c] +
+// w[c][2] x[t+1,p,c], where a block's first frame reads the previous block's
+// last frame (the cache before the call's first frame) and a block's last
+// frame reads zero in place of the next frame.
+//
+// Thread = (b, grid position p, chunk of 8 channels), the chunk fastest, so
+// every load or store instruction of a wave covers 64 consecutive 16-byte
+// (bf16) or 32-byte (fp32) pieces of a row of channels.  Each thread walks
+// all T frames in chunks of MAXF frames, all loads of a chunk issued before
+// any is used, carrying the previous frame in registers: every element of X
+// is read once (plus one look-ahead frame per chunk boundary, which the L2
+// serves) and every element of Y written once.  The thread that reads its
+// cache element is the one that writes the new cache element, after it, so
+// the cache may be committed in place.
+// ---------------------------------------------------------------------------
+struct ConvArgs {
+    const void *X;
+    void *Y;
+    const float *w, *bias;          // [C][3], [C] or null
+    const void *cache_in;           // [B][P][C] or null (zero)
+    void *cache_out;                // [B][P][C] or null
+    int T, F, P, C8;                // frames, frames per block, positions, 8-channel chunks
+    long units;                     // B * P * C8
+};
+
+template <int ES>                   // bytes per element: 2 (bf16) or 4 (fp32)
+struct Chunk8 {
+    static constexpr int NL = ES / 2;            // 16-byte loads per 8 channels
+    u32x4_t q[NL];
+};
+
+template <int ES, int AUX = 0>
+__device__ __forceinline__ Chunk8<ES> chunk_load(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    Chunk8<ES> c;
+#pragma unroll
+    for (int i = 0; i < Chunk8<ES>::NL; ++i) c.q[i] = load16p<AUX>(r, off == kOOB ? kOOB : off + 16u * i);
+    return c;
+}
+
+template <int ES>
+__device__ __forceinline__ void chunk_floats(const Chunk8<ES> &c, float *f)
+{
+    if constexpr (ES == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = bf16lo(c.q[0][e]);
+            f[2 * e + 1] = bf16hi(c.q[0][e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = as_f32(c.q[e >> 2][e & 3]);
+    }
+}
+
+template <int ES, int MAXF>
+__global__ void __launch_bounds__(kThreads)
+svla_temporal_conv_k(const ConvArgs a)
+{
+    const long u = (long)blockIdx.x * kThreads + threadIdx.x;
+    if (u >= a.units) return;
+    const int c8 = (int)(u % a.C8);
+    const long r = u / a.C8;
+    const int p = (int)(r % a.P);
+    const long b = r / a.P;
+    const uint32_t rowb = (uint32_t)a.C8 * 8u * ES;             // bytes per (t, p) row of channels
+    const uint32_t slice = (uint32_t)a.T * (uint32_t)a.P * rowb;
+    const auto rX = make_rsrc((const char *)a.X + b * slice, slice);
+    const auto rY = make_rsrc((char *)a.Y + b * slice, slice);
+    const uint32_t col = (uint32_t)p * rowb + (uint32_t)c8 * 8u * ES;   // (p, chunk) within a frame
+    auto off = [&](int t) -> uint32_t { return t < a.T ? (uint32_t)t * (uint32_t)a.P * rowb + col : kOOB; };
+
+    // the taps and bias of this thread's 8 channels
+    float w0[8], w1[8], w2[8], bs[8];
+    {
+        const f32x4_t *wp = (const f32x4_t *)(a.w + (long)c8 * 24);
+        float wv[24];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const f32x4_t v = wp[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[4 * i + e] = v[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            w0[e] = wv[3 * e];
+            w1[e] = wv[3 * e + 1];
+            w2[e] = wv[3 * e + 2];
+        }
+        f32x4_t b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+        if (a.bias) {
+            b0 = *(const f32x4_t *)(a.bias + (long)c8 * 8);
+            b1 = *(const f32x4_t *)(a.bias + (long)c8 * 8 + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bs[e] = b0[e];
+            bs[4 + e] = b1[e];
+        }
+    }
+    const uint32_t coff = (uint32_t)(b * a.P + p) * rowb + (uint32_t)c8 * 8u * ES;   // cache offset
+    const uint32_t cbytes = (uint32_t)a.units * 8u * ES;
+    float prev[8];
+    {
+        Chunk8<ES> pc;
+#pragma unroll
+        for (int i = 0; i < Chunk8<ES>::NL; ++i) pc.q[i] = (u32x4_t){0u, 0u, 0u, 0u};
+        if (a.cache_in) pc = chunk_load<ES>(make_rsrc(a.cache_in, cbytes), coff);
+        chunk_floats<ES>(pc, prev);
+    }
+    float last[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) last[e] = prev[e];
+    int phase = 0;                                              // t % F
+    for (int t0 = 0; t0 < a.T; t0 += MAXF) {
+        // this chunk's frames and, when the chunk ends inside a block, the next frame
+        Chunk8<ES> v[MAXF + 1];
+#pragma unroll
+        for (int j = 0; j < MAXF; ++j) v[j] = chunk_load<ES, SVLA_TCONV_XAUX>(rX, off(t0 + j));
+        const int end = t0 + MAXF < a.T ? t0 + MAXF : a.T;
+        const bool look = end < a.T && (end % a.F) != 0;       // frame end - 1 is not a block end
+        v[MAXF] = chunk_load<ES>(rX, look ? off(end) : kOOB);
+#pragma unroll
+        for (int j = 0; j < MAXF; ++j) {
+            const int t = t0 + j;
+            if (t >= a.T) break;
+            float cur[8], nxt[8];
+            chunk_floats<ES>(v[j], cur);
+            chunk_floats<ES>(v[j + 1], nxt);
+            const bool block_end = phase == a.F - 1;            // then the next frame reads as zero
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                y[e] = fmaf(w2[e], block_end ? 0.f : nxt[e], fmaf(w1[e], cur[e], fmaf(w0[e], prev[e], bs[e])));
+            if constexpr (ES == 2) {
+                u32x4_t o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
+                store16p<SVLA_TCONV_YAUX>(rY, off(t), o);
+            } else {
+                u32x4_t o0, o1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o0[e] = as_u32(y[e]);
+                    o1[e] = as_u32(y[4 + e]);
+                }
+                store16p<SVLA_TCONV_YAUX>(rY, off(t), o0);
+                store16p<SVLA_TCONV_YAUX>(rY, off(t) + 16u, o1);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                prev[e] = cur[e];
+                last[e] = cur[e];
+            }
+            phase = phase == a.F - 1 ? 0 : phase + 1;
+        }
+    }
+    if (a.cache_out) {
+        const auto rC = make_rsrc(a.cache_out, cbytes);
+        if constexpr (ES == 2) {
+            u32x4_t o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack_bf16(last[2 * e], last[2 * e + 1]);   // exact: bf16 values
+            store16(rC, coff, o);
+        } else {
+            u32x4_t o0, o1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o0[e] = as_u32(last[e]);
+                o1[e] = as_u32(last[4 + e]);
+            }
+            store16(rC, coff, o0);
+            store16(rC, coff + 16u, o1);
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // host side
@@ -2352,8 +2539,8 @@ thread_local char g_err[512] = "";
 thread_local void *const *t_events = nullptr;   // svla_set_timing_events
 thread_local int t_nev = 0;
 
-enum Slot { SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2, SLOT_STEP = 3 };
-constexpr int kSlots = 4;
+enum Slot { SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2, SLOT_STEP = 3, SLOT_CONV = 4 };
+constexpr int kSlots = 5;
 
 // Every kernel goes through here.  With timing events set, the launch
 // carries a start/stop event pair that the runtime records around the
@@ -2977,7 +3164,7 @@ svla_status svla_describe(svla_op op, svla_dtype dt, int B, int H, int nb, int n
         if ((long)nb * n > 0) apply_any(p, aa, nullptr);
         t_desc = nullptr;
     }
-    static const char *slot_name[kSlots] = {"build", "scan", "apply", "step"};
+    static const char *slot_name[kSlots] = {"build", "scan", "apply", "step", "conv"};
     int w = snprintf(buf, len, "{\"fused\": %s, \"step_tiles\": %d, \"step_tile\": %d, \"splits\": %d, "
                      "\"chunk\": %d, \"apply_tile\": %d, \"workspace\": %zu",
                      p.fused ? "true" : "false", p.fused ? p.ftiles : 0, p.fused ? p.ftile : 0,
@@ -3089,6 +3276,48 @@ svla_status svla_block_step_noalloc(svla_dtype dt, int B, int H, int n, int d, c
     if ((st = scratch_for(fn, stream, &ws))) return st;
     return forward(fn, SVLA_OP_BLOCK_STEP, dt, B, H, 1, n, d, Q, K, V, O, S_in, z_in, S_out, z_out, g,
                    rope, eps, ws, kScratchBytes, stream);
+}
+
+svla_status svla_temporal_conv(svla_dtype dt, int B, int nb, int F, int P, int C, const void *X,
+                               void *Y, const float *w, const float *bias, const void *cache_in,
+                               void *cache_out, svla_stream stream)
+{
+    const char *fn = "svla_temporal_conv";
+    if (dt != SVLA_F32 && dt != SVLA_BF16)
+        return fail(SVLA_ERR_DTYPE, fn, "dtype %d is not SVLA_F32 or SVLA_BF16", (int)dt);
+    if (B < 0 || nb < 0 || F < 1 || P < 0 || C < 0)
+        return fail(SVLA_ERR_SHAPE, fn, "bad size (B=%d nb=%d F=%d P=%d C=%d; F >= 1)", B, nb, F, P, C);
+    if (C % 8) return fail(SVLA_ERR_UNSUPPORTED, fn, "C=%d is not a multiple of 8", C);
+    const long long es = dt == SVLA_BF16 ? 2 : 4;
+    const long long T = (long long)nb * F;
+    if (T * P * C * es >= (1LL << 31) || (long long)B * P * C * es >= (1LL << 31) || T >= (1LL << 31))
+        return fail(SVLA_ERR_SHAPE, fn, "one batch's frames or the cache exceed 2 GiB");
+    const long long units = (long long)B * P * (C / 8);
+    if (units == 0) return SVLA_OK;
+    if (T > 0 && (!X || !Y || !w)) return fail(SVLA_ERR_NULL, fn, "X, Y and w are required");
+    if (T == 0 && !cache_out) return SVLA_OK;                       // no frame and no cache: nothing to do
+    if (T == 0 && !w) return fail(SVLA_ERR_NULL, fn, "w is required");
+    if (misaligned(X) || misaligned(Y) || misaligned(w) || misaligned(bias) || misaligned(cache_in) ||
+        misaligned(cache_out))
+        return fail(SVLA_ERR_ALIGN, fn, "device pointers must be 16-byte aligned");
+    const size_t xb = (size_t)(B * T * P * C * es), cb = (size_t)(B * P * C * es);
+    if (overlap(X, xb, Y, xb) || overlap(cache_out, cb, X, xb) || overlap(cache_out, cb, Y, xb) ||
+        (cache_in && cache_out && cache_in != cache_out && overlap(cache_in, cb, cache_out, cb)))
+        return fail(SVLA_ERR_VALUE, fn, "Y overlaps X, or the cache out overlaps X, Y or (other than "
+                    "in place) the cache in");
+    ConvArgs a;
+    memset(&a, 0, sizeof a);
+    a.X = X; a.Y = Y; a.w = w; a.bias = bias; a.cache_in = cache_in; a.cache_out = cache_out;
+    a.T = (int)T; a.F = F; a.P = P; a.C8 = C / 8; a.units = units;
+    const unsigned grid = (unsigned)((units + kThreads - 1) / kThreads);
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    constexpr int MF = SVLA_TCONV_MAXF;
+    char nm[96];
+    snprintf(nm, sizeof nm, "void svla_temporal_conv_k<%d, %d>", dt == SVLA_BF16 ? 2 : 4, MF);
+    if (dt == SVLA_BF16) launch(svla_temporal_conv_k<2, MF>, grid, 0, s, SLOT_CONV, a, nm);
+    else launch(svla_temporal_conv_k<4, MF>, grid, 0, s, SLOT_CONV, a, nm);
+    return check_launch(fn);
 }
 
 svla_status svla_state_build(svla_dtype dt, int B, int H, int nb, int n, int d, const void *K,

@@ -246,11 +246,39 @@ svla_status svla_apply(svla_dtype dt, int B, int H, int nb, int n, int d,
                        const svla_rope *rope, float eps, void *O,
                        void *ws, size_t ws_bytes, svla_stream stream);
 
+/* ---- the FFN's temporal convolution, causal across blocks -------------------- */
+
+/* The Mix-FFN's temporal 1-D convolution made causal across blocks (talk, the
+ * passage on a causal FFN with temporal convolution: a zero token separates
+ * two blocks in training so a block cannot see the next one, and the previous
+ * block's last token is cached as the first token of the next block so it can
+ * see the previous one; comfyui-wiki model page, the temporal 1-D convolution
+ * added to Mix-FFN).  Depthwise, 3 taps over latent frames:
+ *   y[t,p,c] = bias[c] + w[c][0] x[t-1,p,c] + w[c][1] x[t,p,c] + w[c][2] x[t+1,p,c]
+ * where x[t-1] of the call's first frame is cache_in (zero when NULL), later
+ * blocks' first frames read the previous frame (the previous block's last
+ * frame), and x[t+1] reads zero for the last frame of every block.
+ *   X, Y       [B, T, P, C] contiguous, C fastest, one dtype; T = nb * F frames
+ *              in nb blocks of F; P = grid_h * grid_w positions; C % 8 == 0.
+ *   w          [C][3] fp32 (taps for t-1, t, t+1); bias [C] fp32 or NULL.
+ *   cache_in   [B, P, C] in X's dtype, or NULL: the frame before X's first.
+ *   cache_out  [B, P, C] in X's dtype, or NULL: receives X's last frame (the
+ *              next call's cache_in; with nb = 0, cache_in or zeros).  It may
+ *              equal cache_in (commit in place) but not overlap it otherwise,
+ *              and must not overlap X or Y.  Y must not overlap X.
+ * A stream of block steps (nb = 1, the cache carried) gives the same Y as
+ * one call over all blocks.  One batch's frames and the cache must each stay
+ * below 2 GiB.  Errors as elsewhere; overlaps are SVLA_ERR_VALUE. */
+svla_status svla_temporal_conv(svla_dtype dt, int B, int nb, int F, int P, int C,
+                               const void *X, void *Y, const float *w, const float *bias,
+                               const void *cache_in, void *cache_out, svla_stream stream);
+
 /* ---- instrumentation ----------------------------------------------------------- */
 
 /* For benchmarks that time each kernel with HIP events.  While set, every
  * kernel that a call made by this thread launches for slot k (0 = state
- * build, 1 = scan, 2 = apply, 3 = one-launch block step) is launched with the start/stop pair
+ * build, 1 = scan, 2 = apply, 3 = one-launch block step, 4 = temporal
+ * convolution) is launched with the start/stop pair
  * events[2k], events[2k+1], which the runtime records around that kernel's
  * execution (a kernel a call does not need is not launched and leaves its
  * pair alone; pairs past n are not used).  `events` are hipEvent_t handles

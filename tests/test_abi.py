@@ -203,3 +203,20 @@ def test_noalloc_step_validates_before_any_hip_call(lib):
              -1.0, None) == 7                                  # eps < 0
     assert f(_lib.SVLA_BF16, 0, 2, 64, 32, None, None, None, None, None, None, None, None,
              None, None, 1e-6, None) == 0                      # empty: nothing to do
+
+
+def test_temporal_conv_rejects(lib):
+    A, MIS = ctypes.c_void_p(4096), ctypes.c_void_p(4100)
+    f = lib.svla_temporal_conv
+    bf = _lib.SVLA_BF16
+    assert f(bf, 1, 2, 3, 4, 12, A, ctypes.c_void_p(1 << 20), A, None, None, None, None) == 5   # C % 8
+    assert f(bf, 1, 2, 0, 4, 16, A, ctypes.c_void_p(1 << 20), A, None, None, None, None) == 2   # F = 0
+    assert f(7, 1, 2, 3, 4, 16, A, ctypes.c_void_p(1 << 20), A, None, None, None, None) == 3
+    assert f(bf, 1, 2, 3, 4, 16, None, A, A, None, None, None, None) == 1
+    assert f(bf, 1, 2, 3, 4, 16, A, MIS, A, None, None, None, None) == 4
+    # Y overlapping X
+    assert f(bf, 1, 2, 3, 4, 16, A, ctypes.c_void_p(4096 + 64), A, None, None, None, None) == 7
+    # one batch's frames past 2 GiB
+    assert f(bf, 1, 1000, 3, 1000, 1024, A, ctypes.c_void_p(1 << 40), A, None, None, None, None) == 2
+    # nothing to do
+    assert f(bf, 0, 2, 3, 4, 16, None, None, None, None, None, None, None) == 0
