@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5", "t3", "t4"])
     ap.add_argument("--c4-mode", default="both", choices=["both", "stream", "oneshot"])
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="input type of Q, K, V (fp8: OCP E4M3, d = 32 workloads; O stays bf16)")
     ap.add_argument("--inplace", action="store_true",
                     help="streaming: commit the state in place (the two-kernel step)")
     ap.add_argument("--rotate", type=int, default=4)
@@ -100,21 +102,25 @@ class Workload:
     one-block workload), "stream" (one svla_block_step per block, the state
     double-buffered) or "stream_inplace" (the state committed in place)."""
 
-    def __init__(self, name: str, rotate: int, mode: str, x=None):
+    def __init__(self, name: str, rotate: int, mode: str, x=None, dtype: str = "bf16"):
         import torch
         import block_causal_linear_relu_amd as svla
-        from workloads import CONFIGS, make_inputs
+        from workloads import CONFIGS, make_inputs, scaled_config
 
         self.torch, self.svla = torch, svla
-        self.cfg = cfg = CONFIGS[name]
+        self.cfg = cfg = scaled_config(CONFIGS[name], dtype=dtype) if dtype != "bf16" else CONFIGS[name]
+        self.tdt = torch.float8_e4m3fn if cfg.dtype == "fp8" else torch.bfloat16
         self.name = name
         self.mode = mode
         self.stream_mode = mode != "oneshot"
         x = make_inputs(cfg) if x is None else x
         self.x = x
         dev = torch.device("cuda:0")
-        bf = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
-        Q, K, V = bf(x["Q"]), bf(x["K"]), bf(x["V"])
+        if cfg.dtype == "fp8":
+            bf = lambda k: torch.from_numpy(x[k + "_bits"]).to(dev).view(torch.float8_e4m3fn)
+        else:
+            bf = lambda k: torch.from_numpy(x[k]).to(dev).to(torch.bfloat16)
+        Q, K, V = bf("Q"), bf("K"), bf("V")
         self.g = None if x["g"] is None else torch.from_numpy(x["g"]).to(dev)
         B, H, N, d = Q.shape
         self.B, self.H, self.N, self.d, self.nb, self.n = B, H, N, d, cfg.nb, cfg.n
@@ -125,16 +131,17 @@ class Workload:
                 n = cfg.n
                 blocks = [tuple(t[:, :, s * n:(s + 1) * n].contiguous() for t in (Q, K, V))
                           for s in range(cfg.nb)]
-                outs = [torch.empty_like(blocks[0][0]) for _ in range(cfg.nb)]
+                outs = [torch.empty(blocks[0][0].shape, dtype=torch.bfloat16, device=dev)
+                        for _ in range(cfg.nb)]
                 states = [(torch.zeros((B, H, d, d), device=dev), torch.zeros((B, H, d), device=dev))
                           for _ in range(nbuf)]
                 self.sets.append((blocks, outs, states))
             else:
                 q, k, v = (Q, K, V) if r == 0 else (Q.clone(), K.clone(), V.clone())
-                self.sets.append((q, k, v, torch.empty_like(q)))
+                self.sets.append((q, k, v, torch.empty(q.shape, dtype=torch.bfloat16, device=dev)))
         del Q, K, V
         if self.stream_mode:
-            self.ws = torch.empty(svla.workspace_size("block_step", torch.bfloat16, B, H, 1,
+            self.ws = torch.empty(svla.workspace_size("block_step", self.tdt, B, H, 1,
                                                       cfg.n, d), dtype=torch.uint8, device=dev)
             self.frames = cfg.n // (cfg.rope.grid_h * cfg.rope.grid_w) if cfg.rope else 0
             self.ropes = [cfg.rope.with_t0(self.frames * s) if cfg.rope else None
@@ -143,7 +150,7 @@ class Workload:
                        for s in range(cfg.nb)]
         else:
             op = "noncausal" if cfg.nb == 1 else "block_causal"
-            self.ws = torch.empty(svla.workspace_size(op, torch.bfloat16, B, H, cfg.nb, cfg.n, d),
+            self.ws = torch.empty(svla.workspace_size(op, self.tdt, B, H, cfg.nb, cfg.n, d),
                                   dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -159,16 +166,17 @@ class Workload:
         carried state read and written once per streaming step).  Per launch
         of each kernel: the state build K and V, the read-out Q and O, the
         one-launch step all four plus the state; the scan nothing."""
-        e = 2
-        t = self.B * self.H * self.N * self.d * e
+        e = 1 if self.cfg.dtype == "fp8" else 2
+        t = self.B * self.H * self.N * self.d * e          # one input tensor
+        o = self.B * self.H * self.N * self.d * 2          # O (bf16)
         state = self.B * self.H * (self.d * self.d + self.d) * 4
-        per_launch = {"build": 2 * t, "apply": 2 * t, "scan": 0, "step": 4 * t}
+        per_launch = {"build": 2 * t, "apply": t + o, "scan": 0, "step": 3 * t + o}
         if self.stream_mode:
             per_launch = {k: v // self.nb for k, v in per_launch.items()}
             per_launch["step"] += 2 * state
-            path = 4 * t + 2 * state * self.nb
+            path = 3 * t + o + 2 * state * self.nb
         else:
-            path = 4 * t
+            path = 3 * t + o
         return {"per_launch": per_launch, "path": path}
 
     def block_step(self, r: int, s: int):
@@ -224,14 +232,14 @@ class Workload:
         """The library's launch plan for one call of this workload, as taken."""
         torch = self.torch
         if self.stream_mode:
-            p = self.svla.describe("block_step", torch.bfloat16, self.B, self.H, 1, self.n,
+            p = self.svla.describe("block_step", self.tdt, self.B, self.H, 1, self.n,
                                    self.d, rope=self.ropes[0])
             if self.mode == "stream_inplace" and p.get("fused"):
                 p["kernels"] = p["in_place_kernels"]
                 p["fused"] = False
             return p
         op = "noncausal" if self.nb == 1 else "block_causal"
-        return self.svla.describe(op, torch.bfloat16, self.B, self.H, self.nb, self.n, self.d,
+        return self.svla.describe(op, self.tdt, self.B, self.H, self.nb, self.n, self.d,
                                   rope=self.cfg.rope)
 
     def describe(self) -> dict:
@@ -504,7 +512,7 @@ def measure(w: Workload, args, settle_s: float) -> dict:
     dur_s = kern[dominant] * 1e-3
     achieved = ab["per_launch"][dominant] / dur_s / 1e9
     kernel_full = {k["slot"]: k["name"] for k in plan["kernels"]}[dominant]
-    tag = w.name + ("_" + w.mode if w.name == "c4" else "")
+    tag = w.name + ("_" + w.mode if w.name == "c4" else "") + ("_fp8" if w.cfg.dtype == "fp8" else "")
     ms = t["mean_ms"]
     path_gbps = ab["path"] / (ms * 1e-3) / 1e9
     mf = load_mfma(tag, kernel_full)
@@ -682,12 +690,15 @@ def main():
                 "cpu_baseline": None if args.no_cpu_baseline else conv_cpu_baseline(cw)}
         print(json.dumps(line), flush=True)
         return
-    from workloads import CONFIGS, make_inputs
-    x = make_inputs(CONFIGS[args.config])
+    from workloads import CONFIGS, make_inputs, scaled_config
+    if args.dtype == "fp8" and CONFIGS[args.config].d != 32:
+        print("bench.py: fp8 inputs are for the d = 32 workloads", file=sys.stderr)
+        sys.exit(2)
+    x = make_inputs(scaled_config(CONFIGS[args.config], dtype=args.dtype))
     c4 = args.config == "c4"
     stream_mode = "stream_inplace" if args.inplace else "stream"
     primary = stream_mode if (c4 and args.c4_mode in ("both", "stream")) else "oneshot"
-    w = Workload(args.config, args.rotate, primary, x=x)
+    w = Workload(args.config, args.rotate, primary, x=x, dtype=args.dtype)
     m = measure(w, args, args.settle)
     line = {
         "metric": METRIC,
@@ -701,8 +712,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1), bf16-rounded; shapes of the pages' video workloads)",
+        "dtype": args.dtype,
+        "data": "synthetic (seeded N(0,1), %s-rounded; shapes of the pages' video workloads)"
+                % ("OCP-E4M3" if args.dtype == "fp8" else "bf16"),
         "config": w.describe(),
         "timing": m["timing"],
         "roofline": m["roofline"],
@@ -713,7 +725,7 @@ def main():
     if c4 and args.c4_mode == "both":
         del w
         torch.cuda.empty_cache()
-        w1 = Workload(args.config, args.rotate, "oneshot", x=x)
+        w1 = Workload(args.config, args.rotate, "oneshot", x=x, dtype=args.dtype)
         m1 = measure(w1, args, 0.1)
         line["c4_oneshot"] = {k: m1[k] for k in ("value", "ms_per_step", "timing", "roofline",
                                                  "path", "mfma")}

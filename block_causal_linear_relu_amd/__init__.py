@@ -9,8 +9,9 @@ provides device memory (outputs, workspace) and the current stream.
     O, S, z = block_causal(Q, K, V, nb, g=g)           # gated (SANA-Video 2.0)
     O, S, z = block_step(Q, K, V, S, z, rope=rope)     # streaming, state carried
 
-Tensors are [B,H,N,d] contiguous CUDA (HIP) tensors of torch.bfloat16 or
-torch.float32; states S [B,H,d,d] (S[k][v]) and z [B,H,d] are float32.
+Tensors are [B,H,N,d] contiguous CUDA (HIP) tensors of torch.bfloat16,
+torch.float32 or torch.float8_e4m3fn (d = 32; O is then bfloat16); states
+S [B,H,d,d] (S[k][v]) and z [B,H,d] are float32.
 A ``rope`` is any object (or dict) with dt_dims, dh_dims, dw_dims, grid_h,
 grid_w, t0, base.  Errors of the library raise ``SvlaError``.
 """
@@ -28,7 +29,8 @@ __all__ = ["noncausal", "block_causal", "block_step", "block_step_noalloc", "sta
            "state_scan", "apply", "temporal_conv",
            "workspace_size", "describe", "set_timing_events", "SvlaError", "library"]
 
-_DT = {torch.bfloat16: _lib.SVLA_BF16, torch.float32: _lib.SVLA_F32}
+_DT = {torch.bfloat16: _lib.SVLA_BF16, torch.float32: _lib.SVLA_F32,
+       torch.float8_e4m3fn: _lib.SVLA_FP8}
 _OPS = {"noncausal": _lib.OP_NONCAUSAL, "block_causal": _lib.OP_BLOCK_CAUSAL,
         "block_step": _lib.OP_BLOCK_STEP, "state_build": _lib.OP_STATE_BUILD,
         "state_scan": _lib.OP_STATE_SCAN, "apply": _lib.OP_APPLY}
@@ -61,8 +63,19 @@ def _opt(t, name, dtype=torch.float32):
 
 def _dtype(t: torch.Tensor) -> int:
     if t.dtype not in _DT:
-        raise ValueError("dtype %s not supported (bfloat16 or float32)" % t.dtype)
+        raise ValueError("dtype %s not supported (bfloat16, float32 or float8_e4m3fn)" % t.dtype)
     return _DT[t.dtype]
+
+
+def _odtype(dtype):
+    """The dtype of O for inputs of `dtype` (fp8 inputs give a bf16 output)."""
+    return torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype
+
+
+def _out(out, Q):
+    if out is None:
+        return torch.empty(Q.shape, dtype=_odtype(Q.dtype), device=Q.device)
+    return _dev(out, "out", _odtype(Q.dtype))
 
 
 def _stream(device) -> ctypes.c_void_p:
@@ -160,7 +173,7 @@ def noncausal(Q, K, V, eps: float = 1e-6, return_state: bool = False,
     _shape(out, Q.shape, "out")
     dt = _qkv(Q, K, V)
     lib = library()
-    O = torch.empty_like(Q) if out is None else _dev(out, "out", Q.dtype)
+    O = _out(out, Q)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=Q.device) if return_state else None
     z = torch.empty((B, H, d), dtype=torch.float32, device=Q.device) if return_state else None
     ws, nbytes = _ws_arg(workspace, "noncausal", Q, B, H, 1, N, d)
@@ -188,7 +201,7 @@ def block_causal(Q, K, V, nb: int, S0=None, z0=None, g=None, rope=None, eps: flo
     dt = _qkv(Q, K, V)
     S0, z0, g = _opt(S0, "S0"), _opt(z0, "z0"), _opt(g, "g")
     lib = library()
-    O = torch.empty_like(Q) if out is None else _dev(out, "out", Q.dtype)
+    O = _out(out, Q)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=Q.device) if return_state else None
     z = torch.empty((B, H, d), dtype=torch.float32, device=Q.device) if return_state else None
     ws, nbytes = _ws_arg(workspace, "block_causal", Q, B, H, nb, n, d)
@@ -222,7 +235,7 @@ def block_step(Q, K, V, S_in=None, z_in=None, S_out=None, z_out=None, g=None, ro
     dt = _qkv(Q, K, V)
     S_in, z_in, g = _opt(S_in, "S_in"), _opt(z_in, "z_in"), _opt(g, "g")
     lib = library()
-    O = torch.empty_like(Q) if out is None else _dev(out, "out", Q.dtype)
+    O = _out(out, Q)
     if S_out is None:
         S_out = torch.empty((B, H, d, d), dtype=torch.float32, device=Q.device)
     if z_out is None:
@@ -260,7 +273,7 @@ def block_step_noalloc(Q, K, V, S_in, z_in, S_out, z_out, out, g=None, rope=None
         raise ValueError("out, S_out and z_out are required (nothing is allocated)")
     dt = _qkv(Q, K, V)
     S_in, z_in, g = _opt(S_in, "S_in"), _opt(z_in, "z_in"), _opt(g, "g")
-    _dev(out, "out", Q.dtype)
+    _dev(out, "out", _odtype(Q.dtype))
     _dev(S_out, "S_out", torch.float32)
     _dev(z_out, "z_out", torch.float32)
     lib = library()
@@ -355,7 +368,7 @@ def apply(Q, S_prefix, z_prefix, nb: int, rope=None, eps: float = 1e-6):
     _dev(z_prefix, "z_prefix", torch.float32)
     n = N // nb
     lib = library()
-    O = torch.empty_like(Q)
+    O = _out(None, Q)
     ws = _workspace(workspace_size("apply", Q.dtype, B, H, nb, n, d), Q.device)
     nbytes = 0 if ws is None else ws.numel()
     rp, _keep = _rope_arg(rope)

@@ -18,7 +18,7 @@ SVLA_OK = 0
 STATUS_NAMES = {0: "SVLA_OK", 1: "SVLA_ERR_NULL", 2: "SVLA_ERR_SHAPE", 3: "SVLA_ERR_DTYPE",
                 4: "SVLA_ERR_ALIGN", 5: "SVLA_ERR_UNSUPPORTED", 6: "SVLA_ERR_WORKSPACE",
                 7: "SVLA_ERR_VALUE", 8: "SVLA_ERR_HIP"}
-SVLA_F32, SVLA_BF16 = 0, 1
+SVLA_F32, SVLA_BF16, SVLA_FP8 = 0, 1, 2
 OP_NONCAUSAL, OP_BLOCK_CAUSAL, OP_BLOCK_STEP, OP_STATE_BUILD, OP_STATE_SCAN, OP_APPLY = range(6)
 
 

@@ -55,6 +55,9 @@
 #ifndef SVLA_DMA_R128
 #define SVLA_DMA_R128 3            // ... and for d = 128
 #endif
+#ifndef SVLA_DMA_U128
+#define SVLA_DMA_U128 SVLA_DMA_U   // ... 16-byte loads per thread per tensor per stage at d = 128
+#endif
 #ifndef SVLA_MIN_SPLIT_ROPE
 #define SVLA_MIN_SPLIT_ROPE 5      // builds with RoPE: tokens per split >= this * d
 #endif
@@ -69,6 +72,9 @@
 #endif
 #ifndef SVLA_ROPE_WGS
 #define SVLA_ROPE_WGS 2048         // ... (and fp32 builds): workgroups wanted per launch
+#endif
+#ifndef SVLA_F8_WGS
+#define SVLA_F8_WGS 420            // fp8 state build without RoPE: workgroups wanted per launch
 #endif
 #ifndef SVLA_MIN_SPLIT_PER_D
 #define SVLA_MIN_SPLIT_PER_D 8     // tokens per build workgroup and block >= this * d
@@ -224,6 +230,69 @@ __device__ __forceinline__ unsigned int pack_bf16(float lo, float hi)
     typedef __attribute__((ext_vector_type(2))) float f32x2_t;
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
     return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// Input element types of the bf16 kernels: bf16 (IN = 2 bytes) or OCP FP8
+// E4M3 (IN = 1).  A lane handles 8 consecutive features: 16 bytes of bf16 or
+// 8 bytes of fp8, kept in the low half of a u32x4_t.
+template <int IN, int AUX>
+__device__ __forceinline__ u32x4_t load8f(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    if constexpr (IN == 2) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+    } else {
+        typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, AUX);
+        return (u32x4_t){v[0], v[1], 0u, 0u};
+    }
+}
+
+// The 8 features as fp32 values, phi applied when RELU.  fp8 decodes on the
+// hardware converter (two values per instruction), exactly.
+template <int IN, bool RELU>
+__device__ __forceinline__ void feat8(const u32x4_t &v, float *f)
+{
+    if constexpr (IN == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const unsigned int w = RELU ? relu_bf16x2(v[e]) : v[e];
+            f[2 * e] = bf16lo(w);
+            f[2 * e + 1] = bf16hi(w);
+        }
+    } else {
+        typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], false);
+            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[e], true);
+            f[4 * e] = lo[0];
+            f[4 * e + 1] = lo[1];
+            f[4 * e + 2] = hi[0];
+            f[4 * e + 3] = hi[1];
+        }
+        if constexpr (RELU) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = fmaxf(f[e], 0.f);
+        }
+    }
+}
+
+// The 8 features as packed bf16 (phi applied when RELU); exact, since every
+// fp8 E4M3 value is a bf16 value.
+template <int IN, bool RELU>
+__device__ __forceinline__ u32x4_t bf16x8_of(const u32x4_t &v)
+{
+    u32x4_t o;
+    if constexpr (IN == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = RELU ? relu_bf16x2(v[e]) : v[e];
+    } else {
+        float f[8];
+        feat8<IN, RELU>(v, f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16(f[2 * e], f[2 * e + 1]);
+    }
+    return o;
 }
 
 // Barrier for LDS hand-offs inside a workgroup.  __syncthreads() also
@@ -1062,17 +1131,18 @@ svla_state_build_dma(const BuildArgs a)
 //   DG = 128   : D = 64 quadrant split; four workgroups per unit, each
 //                one 64 x 64 quadrant of S from K and V half-rows.
 // ---------------------------------------------------------------------------
-template <int D, int DG, int PF, int U>
+template <int D, int DG, int PF, int U, bool ROPE = true, int IN = 2>
 __global__ void __launch_bounds__(kThreads)
 svla_state_build_rope(const BuildArgs a)
 {
-    constexpr int CPR = D / 8;            // 16-byte chunks per (half-)row
+    constexpr int CPR = D / 8;            // 8-feature chunks per (half-)row
     constexpr int RPW = 64 / CPR;         // rows one wave load instruction covers
     constexpr int TW = U * RPW;           // tokens per wave stage
     constexpr int GPW = TW / 16;          // 16-token groups per wave stage
-    constexpr int ROWB = D * 2;
+    constexpr int ROWB = D * 2;           // bytes of a staged (bf16) row
     constexpr int TILEB = TW * ROWB;
-    constexpr int NK = 2;                 // K tiles: rotated hi and lo
+    constexpr int NK = ROPE ? 2 : 1;      // K tiles: (rotated) hi, and lo with RoPE
+    static_assert(IN == 2 || (D == 32 && DG == 32), "fp8 inputs at d = 32 only");
     constexpr int SLOTB = (NK + 1) * TILEB;
     constexpr int TPW = D / 32;           // 32 x 32 tiles per side
     constexpr bool QUAD = DG != D;
@@ -1103,7 +1173,7 @@ svla_state_build_rope(const BuildArgs a)
     const int tok_lo = c * a.n + s * a.chunk;
     const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
 
-    const uint32_t slice = (uint32_t)a.N * DG * 2;
+    const uint32_t slice = (uint32_t)a.N * DG * IN;
     const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
     const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
     const int kcol = 64 * qm, vcol = 64 * qn;   // first feature of this tile in K / V
@@ -1116,7 +1186,7 @@ svla_state_build_rope(const BuildArgs a)
     const int nw = nst > wave ? (nst - wave + 3) / 4 : 0;
     auto offset = [&](int i, int u, int col) -> uint32_t {
         const int t = tok_lo + (wave + 4 * i) * TW + u * RPW + row;
-        return t < tok_hi ? (uint32_t)(t * DG + col + q * 8) * 2u : kOOB;
+        return t < tok_hi ? (uint32_t)(t * DG + col + q * 8) * (uint32_t)IN : kOOB;
     };
     // Register slot p holds stage i with i % PF == p.  The scheduling
     // barriers keep the slots' loads in slot order, the order the loop
@@ -1127,21 +1197,26 @@ svla_state_build_rope(const BuildArgs a)
     for (int p = 0; p < PF; ++p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            kreg[p][u] = load16p<SVLA_KV_AUX>(rK, offset(p, u, kcol));
-            vreg[p][u] = load16p<SVLA_KV_AUX>(rV, offset(p, u, vcol));
+            kreg[p][u] = load8f<IN, SVLA_KV_AUX>(rK, offset(p, u, kcol));
+            vreg[p][u] = load8f<IN, SVLA_KV_AUX>(rV, offset(p, u, vcol));
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 
     // the RoPE table is built while the first stages load
     float2 *tab = (float2 *)lds;
-    const uint32_t frame_lo = tok_lo < tok_hi ? fdiv((uint32_t)tok_lo, a.rope.div_hw) : 0;
-    const uint32_t frame_hi = tok_lo < tok_hi ? fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw) : 0;
-    const int nf = (int)(frame_hi - frame_lo) + 1;
-    rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
-    const RopePairs<4> pp = rope_pairs<4>(a.rope, kcol + q * 8, nf);
-    lds_barrier();
-    unsigned char *slot = lds + a.rope.tab_bytes + wave * SLOTB;
+    uint32_t frame_lo = 0;
+    RopePairs<4> pp;
+    unsigned char *const work = lds + (ROPE ? a.rope.tab_bytes : 0);   // slots, then the epilogue
+    if constexpr (ROPE) {
+        frame_lo = tok_lo < tok_hi ? fdiv((uint32_t)tok_lo, a.rope.div_hw) : 0;
+        const uint32_t frame_hi = tok_lo < tok_hi ? fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw) : 0;
+        const int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+        pp = rope_pairs<4>(a.rope, kcol + q * 8, nf);
+        lds_barrier();
+    }
+    unsigned char *slot = work + wave * SLOTB;
 
     f32x16_t acc[TPW][TPW];
 #pragma unroll
@@ -1172,35 +1247,32 @@ svla_state_build_rope(const BuildArgs a)
             for (int u = 0; u < U; ++u) {
                 const int r = u * RPW + row;              // row within the stage
                 const int cpos = swz16<D>(r, q);
-                u32x4_t kr;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) kr[e] = relu_bf16x2(kreg[p][u][e]);
                 float kf[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kf[2 * e] = bf16lo(kr[e]);
-                    kf[2 * e + 1] = bf16hi(kr[e]);
-                }
+                feat8<IN, true>(kreg[p][u], kf);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
-                const int tok = tok_lo + (wave + 4 * i) * TW + r;
-                rope_rotate<4>(kf, rope_pos((uint32_t)tok, frame_lo, a.rope), pp, tab);
-                u32x4_t hi, lo;
+                if constexpr (ROPE) {
+                    const int tok = tok_lo + (wave + 4 * i) * TW + r;
+                    rope_rotate<4>(kf, rope_pos((uint32_t)tok, frame_lo, a.rope), pp, tab);
+                    u32x4_t hi, lo;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    hi[e] = pack_bf16(kf[2 * e], kf[2 * e + 1]);
-                    lo[e] = pack_bf16(kf[2 * e] - bf16lo(hi[e]), kf[2 * e + 1] - bf16hi(hi[e]));
+                    for (int e = 0; e < 4; ++e) {
+                        hi[e] = pack_bf16(kf[2 * e], kf[2 * e + 1]);
+                        lo[e] = pack_bf16(kf[2 * e] - bf16lo(hi[e]), kf[2 * e + 1] - bf16hi(hi[e]));
+                    }
+                    *(u32x4_t *)(slot + r * ROWB + cpos * 16) = hi;
+                    *(u32x4_t *)(slot + TILEB + r * ROWB + cpos * 16) = lo;
+                } else {
+                    *(u32x4_t *)(slot + r * ROWB + cpos * 16) = bf16x8_of<IN, true>(kreg[p][u]);
                 }
-                *(u32x4_t *)(slot + r * ROWB + cpos * 16) = hi;
-                *(u32x4_t *)(slot + TILEB + r * ROWB + cpos * 16) = lo;
-                *(u32x4_t *)(slot + NK * TILEB + r * ROWB + cpos * 16) = vreg[p][u];
+                *(u32x4_t *)(slot + NK * TILEB + r * ROWB + cpos * 16) = bf16x8_of<IN, false>(vreg[p][u]);
             }
             // refill this register slot with the stage PF ahead
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                kreg[p][u] = load16p<SVLA_KV_AUX>(rK, offset(i + PF, u, kcol));
-                vreg[p][u] = load16p<SVLA_KV_AUX>(rV, offset(i + PF, u, vcol));
+                kreg[p][u] = load8f<IN, SVLA_KV_AUX>(rK, offset(i + PF, u, kcol));
+                vreg[p][u] = load8f<IN, SVLA_KV_AUX>(rV, offset(i + PF, u, vcol));
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1209,7 +1281,7 @@ svla_state_build_rope(const BuildArgs a)
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) {
                     av[t] = trb_load<D>(slot + 16 * gi * ROWB, fl[t]);
-                    al[t] = trb_load<D>(slot + TILEB + 16 * gi * ROWB, fl[t]);
+                    if constexpr (ROPE) al[t] = trb_load<D>(slot + TILEB + 16 * gi * ROWB, fl[t]);
                     bv[t] = trb_load<D>(slot + NK * TILEB + 16 * gi * ROWB, fl[t]);
                 }
 #pragma unroll
@@ -1217,7 +1289,8 @@ svla_state_build_rope(const BuildArgs a)
 #pragma unroll
                     for (int tn = 0; tn < TPW; ++tn) {
                         acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[tm], bv[tn], acc[tm][tn], 0, 0, 0);
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[tm], bv[tn], acc[tm][tn], 0, 0, 0);
+                        if constexpr (ROPE)
+                            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[tm], bv[tn], acc[tm][tn], 0, 0, 0);
                     }
             }
         }
@@ -1228,7 +1301,7 @@ svla_state_build_rope(const BuildArgs a)
         // own, then every thread sums four values in wave order (the same
         // order as the pass-by-pass sum below); z is summed within each wave
         // over the 16 lanes that share a chunk, then over the waves
-        float *red = (float *)(lds + a.rope.tab_bytes);            // 4 x D x D floats
+        float *red = (float *)work;                                // 4 x D x D floats
         float *zw = red + 4 * D * D;                               // 4 x D floats
         __syncthreads();          // every wave is done with its slot
 #pragma unroll
@@ -1271,7 +1344,7 @@ svla_state_build_rope(const BuildArgs a)
 
     // ---- epilogue: the four waves' tiles summed in wave order, then
     // S_part (row-major [k][v], row stride DG) and z_part
-    float *red = (float *)(lds + a.rope.tab_bytes);                // D x D floats
+    float *red = (float *)work;                                    // D x D floats
     float *zred = red + D * D;                                     // 256 x 8 floats
     __syncthreads();          // every wave is done with its slot
 #pragma unroll 1
@@ -1482,10 +1555,11 @@ svla_state_build_f32(const BuildArgs a)
 // Q loads are in flight; tile 0 also writes it out as the final state.
 // Otherwise the state comes from the scan's packed operand and prefix z.
 // ---------------------------------------------------------------------------
-template <int D, bool ROPE, bool FOLD>
+template <int D, bool ROPE, bool FOLD, int IN = 2>
 __global__ void __launch_bounds__(kThreads)
 svla_apply_bf16(const ApplyArgs a)
 {
+    static_assert(IN == 2 || D == 32, "fp8 inputs at d = 32 only");
     constexpr int MT = D / 16;
     constexpr int KS = D / 32;
     constexpr int PF = ROPE ? SVLA_APPLY32_PF_ROPE : SVLA_APPLY32_PF;
@@ -1505,8 +1579,9 @@ svla_apply_bf16(const ApplyArgs a)
     const int t_hi = min(t_lo + a.tile, (c + 1) * a.n);
     const long unit = bh * a.nb + c;
 
-    const uint32_t slice = (uint32_t)a.N * D * 2;
-    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
+    const uint32_t slice = (uint32_t)a.N * D * 2;              // O: bf16
+    const uint32_t qslice = (uint32_t)a.N * D * IN;
+    const auto rQ = make_rsrc((const char *)a.Q + bh * qslice, qslice);
     const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
     const int kg = lane >> 4, tl = lane & 15;
 
@@ -1549,14 +1624,14 @@ svla_apply_bf16(const ApplyArgs a)
     const int nw = ngroups > wave ? (ngroups - wave + 3) / 4 : 0;
     auto qoff = [&](int i, int ks) -> uint32_t {
         const int tok = t_lo + 16 * (wave + 4 * i) + tl;
-        return tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * 2u : kOOB;
+        return tok < t_hi ? (uint32_t)(tok * D + 8 * (4 * ks + kg)) * (uint32_t)IN : kOOB;
     };
     __builtin_amdgcn_sched_barrier(0);
     u32x4_t qreg[PF][KS];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(p, ks));
+        for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load8f<IN, SVLA_Q_AUX>(rQ, qoff(p, ks));
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -1638,19 +1713,17 @@ svla_apply_bf16(const ApplyArgs a)
         if constexpr (ROPE) rp = rope_pos((uint32_t)tok, frame_lo, a.rope);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4_t pq;
+            u32x4_t pq = {0u, 0u, 0u, 0u};
+            if constexpr (IN == 2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[ks][e]);
-            float pf[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pf[2 * e] = bf16lo(pq[e]);
-                pf[2 * e + 1] = bf16hi(pq[e]);
+                for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[ks][e]);
             }
+            float pf[8];
+            feat8<IN, true>(qr[ks], pf);
 #pragma unroll
             for (int e = 0; e < 8; ++e) den = fmaf(pf[e], zf[ks][e], den);
-            if constexpr (ROPE) {
-                rope_rotate<4>(pf, rp, pp[ks], tab);
+            if constexpr (ROPE) rope_rotate<4>(pf, rp, pp[ks], tab);
+            if constexpr (ROPE || IN != 2) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) pq[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
             }
@@ -1697,7 +1770,7 @@ svla_apply_bf16(const ApplyArgs a)
 #pragma unroll
                 for (int p = 0; p < PF; ++p)
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) qb[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(i0 + p, ks));
+                    for (int ks = 0; ks < KS; ++ks) qb[p][ks] = load8f<IN, SVLA_Q_AUX>(rQ, qoff(i0 + p, ks));
             }
 #pragma unroll
             for (int p = 0; p < PF; ++p) {
@@ -1719,7 +1792,7 @@ svla_apply_bf16(const ApplyArgs a)
                 for (int ks = 0; ks < KS; ++ks) qr[ks] = qreg[p][ks];
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load16p<SVLA_Q_AUX>(rQ, qoff(i + PF, ks));
+                for (int ks = 0; ks < KS; ++ks) qreg[p][ks] = load8f<IN, SVLA_Q_AUX>(rQ, qoff(i + PF, ks));
                 __builtin_amdgcn_sched_barrier(0);
                 group(i, qr);
             }
@@ -2102,7 +2175,7 @@ struct StepArgs {
     RopeK rope;
 };
 
-template <bool ROPE, int W, int PF, int QG>
+template <bool ROPE, int W, int PF, int QG, int IN = 2>
 __global__ void __launch_bounds__(64 * W)
 svla_step_fused(const StepArgs a)
 {
@@ -2125,10 +2198,11 @@ svla_step_fused(const StepArgs a)
     const int n = a.n;
     const int t_lo = tile * a.tile, t_hi = min(t_lo + a.tile, n);
 
-    const uint32_t slice = (uint32_t)n * D * 2;
-    const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
-    const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
-    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
+    const uint32_t slice = (uint32_t)n * D * 2;                 // O: bf16
+    const uint32_t islice = (uint32_t)n * D * IN;               // Q, K, V: bf16 or fp8
+    const auto rK = make_rsrc((const char *)a.K + bh * islice, islice);
+    const auto rV = make_rsrc((const char *)a.V + bh * islice, islice);
+    const auto rQ = make_rsrc((const char *)a.Q + bh * islice, islice);
     const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
 
     float2 *tab = (float2 *)lds;
@@ -2142,13 +2216,13 @@ svla_step_fused(const StepArgs a)
     const int nw = nst > wave ? (nst - wave + W - 1) / W : 0;
     auto kv_off = [&](int i) -> uint32_t {
         const int t = 16 * (wave + W * i) + row;
-        return t < n ? (uint32_t)(t * D + q * 8) * 2u : kOOB;
+        return t < n ? (uint32_t)(t * D + q * 8) * (uint32_t)IN : kOOB;
     };
     u32x4_t kreg[PF], vreg[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-        kreg[p] = load16p<0>(rK, kv_off(p));
-        vreg[p] = load16p<0>(rV, kv_off(p));
+        kreg[p] = load8f<IN, 0>(rK, kv_off(p));
+        vreg[p] = load8f<IN, 0>(rV, kv_off(p));
         __builtin_amdgcn_sched_barrier(0);
     }
     // 2. this wave's Q groups of the tile, in the read-out's operand layout
@@ -2159,7 +2233,7 @@ svla_step_fused(const StepArgs a)
 #pragma unroll
     for (int j = 0; j < QG; ++j) {
         const int tok = t_lo + 16 * (wave + W * j) + tl;
-        qreg[j] = load16p<SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * kg) * 2u : kOOB);
+        qreg[j] = load8f<IN, SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * kg) * (uint32_t)IN : kOOB);
     }
     __builtin_amdgcn_sched_barrier(0);
     // 3. the carried state: thread -> S elements 4 tid .. (and z for tid < d / 4)
@@ -2195,15 +2269,8 @@ svla_step_fused(const StepArgs a)
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const int i = i0 + p;
-            u32x4_t kr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kr[e] = relu_bf16x2(kreg[p][e]);
             float kf[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kf[2 * e] = bf16lo(kr[e]);
-                kf[2 * e + 1] = bf16hi(kr[e]);
-            }
+            feat8<IN, true>(kreg[p], kf);
 #pragma unroll
             for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
             if constexpr (ROPE) {
@@ -2218,13 +2285,13 @@ svla_step_fused(const StepArgs a)
                 *(u32x4_t *)(slot + row * ROWB + q * 16) = hi;
                 *(u32x4_t *)(slot + TILEB + row * ROWB + q * 16) = lo;
             } else {
-                *(u32x4_t *)(slot + row * ROWB + q * 16) = kr;
+                *(u32x4_t *)(slot + row * ROWB + q * 16) = bf16x8_of<IN, true>(kreg[p]);
             }
-            *(u32x4_t *)(slot + NK * TILEB + row * ROWB + q * 16) = vreg[p];
+            *(u32x4_t *)(slot + NK * TILEB + row * ROWB + q * 16) = bf16x8_of<IN, false>(vreg[p]);
             // refill this register slot with the stage PF ahead
             __builtin_amdgcn_sched_barrier(0);
-            kreg[p] = load16p<0>(rK, kv_off(i + PF));
-            vreg[p] = load16p<0>(rV, kv_off(i + PF));
+            kreg[p] = load8f<IN, 0>(rK, kv_off(i + PF));
+            vreg[p] = load8f<IN, 0>(rV, kv_off(i + PF));
             __builtin_amdgcn_sched_barrier(0);
             const bf16x8_t av = trb_load<D>(slot, fl);
             const bf16x8_t bv = trb_load<D>(slot + NK * TILEB, fl);
@@ -2319,20 +2386,18 @@ svla_step_fused(const StepArgs a)
         const int tok = t_lo + 16 * (wave + W * j) + tl;
         const bool valid = tok < t_hi;
         const u32x4_t qr = qreg[j];
-        u32x4_t pq;
+        u32x4_t pq = {0u, 0u, 0u, 0u};
+        if constexpr (IN == 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[e]);
-        float pf[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            pf[2 * e] = bf16lo(pq[e]);
-            pf[2 * e + 1] = bf16hi(pq[e]);
+            for (int e = 0; e < 4; ++e) pq[e] = relu_bf16x2(qr[e]);
         }
+        float pf[8];
+        feat8<IN, true>(qr, pf);
         float den = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) den = fmaf(pf[e], zf[e], den);
-        if constexpr (ROPE) {
-            rope_rotate<4>(pf, rope_pos((uint32_t)tok, 0, a.rope), ppq, tab);
+        if constexpr (ROPE) rope_rotate<4>(pf, rope_pos((uint32_t)tok, 0, a.rope), ppq, tab);
+        if constexpr (ROPE || IN != 2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) pq[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
         }
@@ -2606,6 +2671,7 @@ struct Plan {
     bool fold;                 // one block, bf16, d = 32: the apply sums the partials (no scan)
     int splits, chunk;         // build: workgroups per block, tokens per workgroup
     int tile, tiles;           // apply
+    int oesize;                // bytes per O element and per packed state operand element
     size_t lds_build, lds_apply;
     size_t off_spart, off_zpart, off_sop, off_zpre, total;
     RopeK rope;
@@ -2683,13 +2749,15 @@ svla_status check_rope(const char *fn, const svla_rope *r, int d, RopeK *out)
 
 svla_status check_sizes(const char *fn, svla_dtype dt, int B, int H, int nb, int n, int d)
 {
-    if (dt != SVLA_F32 && dt != SVLA_BF16)
-        return fail(SVLA_ERR_DTYPE, fn, "dtype %d is not SVLA_F32 or SVLA_BF16", (int)dt);
+    if (dt != SVLA_F32 && dt != SVLA_BF16 && dt != SVLA_FP8)
+        return fail(SVLA_ERR_DTYPE, fn, "dtype %d is not SVLA_F32, SVLA_BF16 or SVLA_FP8", (int)dt);
     if (B < 0 || H < 0 || nb < 0 || n < 0)
         return fail(SVLA_ERR_SHAPE, fn, "negative size (B=%d H=%d nb=%d n=%d)", B, H, nb, n);
     if (d != 32 && d != 64 && d != 128)
         return fail(SVLA_ERR_UNSUPPORTED, fn, "d=%d not in {32, 64, 128}", d);
-    const int es = dt == SVLA_BF16 ? 2 : 4;
+    if (dt == SVLA_FP8 && d != 32)
+        return fail(SVLA_ERR_UNSUPPORTED, fn, "fp8 inputs are supported at d = 32 only (got d=%d)", d);
+    const int es = dt == SVLA_F32 ? 4 : 2;          // the larger of the input and output element
     if ((long long)nb * n * d * es >= (1LL << 31))
         return fail(SVLA_ERR_SHAPE, fn, "one (b,h) slice of %lld tokens x d=%d exceeds 2 GiB",
                     (long long)nb * n, d);
@@ -2706,7 +2774,8 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     memset(p, 0, sizeof *p);
     p->B = B; p->H = H; p->nb = nb; p->n = n; p->d = d;
     p->BH = (long)B * H;
-    p->esize = dt == SVLA_BF16 ? 2 : 4;
+    p->esize = dt == SVLA_BF16 ? 2 : dt == SVLA_FP8 ? 1 : 4;
+    p->oesize = dt == SVLA_F32 ? 4 : 2;               // fp8 inputs give a bf16 output
     st = check_rope(fn, rope, d, &p->rope);
     if (st) return st;
     p->dma = p->esize == 2 && !p->rope.on;
@@ -2719,8 +2788,14 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
     int chunk_rope = 0;
     const int splits_plain = pick_splits(units, n, d, SVLA_ROPE_WGS, &chunk_other);
     const int splits_rope = pick_splits(units, n, d, SVLA_ROPE_WGS, &chunk_rope, SVLA_MIN_SPLIT_ROPE);
-    const int splits_other = p->rope.on ? splits_rope : splits_plain;
+    // fp8 without RoPE (the register build): fewer, longer splits, so a
+    // one-block call's partials fit the read-out that sums them
+    int chunk_f8 = 0;
+    const int splits_f8 = pick_splits(units, n, d, SVLA_F8_WGS, &chunk_f8);
+    const bool f8plain = p->esize == 1 && !p->rope.on;
+    const int splits_other = p->rope.on ? splits_rope : f8plain ? splits_f8 : splits_plain;
     if (p->rope.on) chunk_other = chunk_rope;
+    if (f8plain) chunk_other = chunk_f8;
     if (op == SVLA_OP_STATE_BUILD) {
         // one workgroup per block: its partial is the block's local state
         p->splits = n > 0 ? 1 : 0;
@@ -2730,12 +2805,12 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
         p->chunk = p->dma ? chunk_dma : chunk_other;
     }
     p->fold = (op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP) &&
-              p->esize == 2 && d == 32 && nb == 1 && n > 0 &&
+              p->esize <= 2 && d == 32 && nb == 1 && n > 0 &&
               p->splits + 1 <= (p->rope.on ? kFoldMaxPartsRope : kFoldMaxParts);
-    // the one-launch step: one block of bf16 at d = 32, short enough for every
+    // the one-launch step: one block of bf16 or fp8 at d = 32, short enough for every
     // workgroup of a (b,h) to build the whole block state itself
     p->fused = (op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP) &&
-               p->esize == 2 && d == 32 && nb == 1 && n > 0 && n <= SVLA_FUSED_MAX_N && p->BH > 0;
+               p->esize <= 2 && d == 32 && nb == 1 && n > 0 && n <= SVLA_FUSED_MAX_N && p->BH > 0;
     if (p->fused) {
         // at most one workgroup per CU: (a second round of workgroups would
         // repeat the whole build); at least one per (b,h)
@@ -2769,11 +2844,13 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
 
     // dynamic LDS: [RoPE table][stage buffers | epilogue] (the direct-to-LDS
     // build has static LDS only)
-    if (p->esize == 2) {
+    if (p->esize <= 2) {
         const int td = d == 128 ? 64 : d;                 // tile side (quadrants for d = 128)
         const size_t slots = (size_t)4 * 3 * rope_tokens(d) * td * 2;
-        const size_t epi = td == 32 && p->rope.on ? ((size_t)4 * td * td + 4 * td) * 4   // one-pass epilogue
-                                                  : ((size_t)td * td + td + 2048) * 4;
+        // (the register build's d = 32 epilogue sums the four wave tiles in one
+        // pass; at d >= 64 it sums them pass by pass)
+        const size_t epi = td == 32 ? ((size_t)4 * td * td + 4 * td) * 4
+                                    : ((size_t)td * td + td + 2048) * 4;
         p->lds_build = p->dma ? 0 : (slots > epi ? slots : epi);
     } else {
         const size_t stage = (size_t)2 * 2 * 4096;
@@ -2809,12 +2886,13 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
         // the carried state there)
         int most = splits_dma > splits_plain ? splits_dma : splits_plain;
         if (splits_rope > most) most = splits_rope;
+        if (splits_f8 > most) most = splits_f8;
         const size_t slots = (size_t)most + 1;
         p->off_spart = off; off = align256(off + (size_t)units * slots * d * d * 4);
         p->off_zpart = off; off = align256(off + (size_t)units * slots * d * 4);
     }
     if (fused || op == SVLA_OP_APPLY) {
-        p->off_sop = off; off = align256(off + (size_t)units * d * d * p->esize);
+        p->off_sop = off; off = align256(off + (size_t)units * d * d * p->oesize);
     }
     if (fused) {
         p->off_zpre = off; off = align256(off + (size_t)units * d * 4);
@@ -2838,18 +2916,26 @@ void launch_build(const Plan &p, const BuildArgs &args, hipStream_t s)
     const unsigned qgrid = (unsigned)((grid + 7) / 8 * 8 * 4);   // RoPE build at d = 128: four quadrants
     char nm[96];
     if (p.dma) {
-        constexpr int U = D == 32 ? SVLA_DMA_U32 : SVLA_DMA_U;
+        constexpr int U = D == 32 ? SVLA_DMA_U32 : D == 64 ? SVLA_DMA_U : SVLA_DMA_U128;
         constexpr int R = D == 32 ? SVLA_DMA_R32 : D == 64 ? SVLA_DMA_R : SVLA_DMA_R128;
         snprintf(nm, sizeof nm, "void svla_state_build_dma<%d, %d, %d>", D, U, R);
         launch(svla_state_build_dma<D, U, R>, grid, 0, s, SLOT_BUILD, a, nm);
-    } else if (p.esize == 2) {
+    } else if (p.esize <= 2) {
         constexpr int PF = rope_pf(), U = rope_u(D);
         if constexpr (D == 128) {
-            snprintf(nm, sizeof nm, "void svla_state_build_rope<64, 128, %d, %d>", PF, U);
+            snprintf(nm, sizeof nm, "void svla_state_build_rope<64, 128, %d, %d, true, 2>", PF, U);
             launch(svla_state_build_rope<64, 128, PF, U>, qgrid, p.lds_build, s, SLOT_BUILD, a, nm);
         } else {
-            snprintf(nm, sizeof nm, "void svla_state_build_rope<%d, %d, %d, %d>", D, D, PF, U);
-            launch(svla_state_build_rope<D, D, PF, U>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
+            const bool r = p.rope.on;
+            snprintf(nm, sizeof nm, "void svla_state_build_rope<%d, %d, %d, %d, %s, %d>", D, D, PF, U,
+                     r ? "true" : "false", p.esize);
+            if constexpr (D == 32) {
+                if (p.esize == 1 && r) launch(svla_state_build_rope<D, D, PF, U, true, 1>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
+                else if (p.esize == 1) launch(svla_state_build_rope<D, D, PF, U, false, 1>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
+                else launch(svla_state_build_rope<D, D, PF, U>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
+            } else {
+                launch(svla_state_build_rope<D, D, PF, U>, grid, p.lds_build, s, SLOT_BUILD, a, nm);
+            }
         }
     } else {
         snprintf(nm, sizeof nm, "void svla_state_build_f32<%d, %s>", D, p.rope.on ? "true" : "false");
@@ -2862,7 +2948,7 @@ template <int D, int MODE>
 void launch_scan_d(const Plan &p, const ScanArgs &a, hipStream_t s)
 {
     const unsigned grid = (unsigned)(p.BH * (ScanShape<D>::STILES + 1));
-    const bool bf = p.esize == 2;
+    const bool bf = p.oesize == 2;
     char nm[96];
     if (MODE != SCAN_PACK && p.nb >= kScanLongChain) {
         snprintf(nm, sizeof nm, "void svla_state_scan_k<%d, %d, %s, 4>", D, MODE, bf ? "true" : "false");
@@ -2882,23 +2968,28 @@ void launch_apply(const Plan &p, const ApplyArgs &args, hipStream_t s)
     a.groups = p.BH * p.nb * p.tiles;
     const unsigned grid = xcd_grid(a.groups);
     char nm[96];
-    snprintf(nm, sizeof nm, "void svla_apply_%s<%d, %s>", p.esize == 2 ? "bf16" : "f32", D,
+    snprintf(nm, sizeof nm, "void svla_apply_%s<%d, %s>", p.esize <= 2 ? "bf16" : "f32", D,
              p.rope.on ? "true" : "false");
-    if (p.esize == 2) {
+    if (p.esize <= 2) {
         if constexpr (D >= 64) {
             constexpr int PF = SVLA_APPLY_RING_PF;
             snprintf(nm, sizeof nm, "void svla_apply_ring<%d, %s, %d>", D, p.rope.on ? "true" : "false", PF);
             if (p.rope.on) launch(svla_apply_ring<D, true, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
             else launch(svla_apply_ring<D, false, PF>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
         } else {
-            if (p.fold) {
-                snprintf(nm, sizeof nm, "void svla_apply_bf16<%d, %s, true>", D, p.rope.on ? "true" : "false");
-                if (p.rope.on) launch(svla_apply_bf16<D, true, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-                else launch(svla_apply_bf16<D, false, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
-            } else {
-                snprintf(nm, sizeof nm, "void svla_apply_bf16<%d, %s, false>", D, p.rope.on ? "true" : "false");
-                if (p.rope.on) launch(svla_apply_bf16<D, true, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            const bool r = p.rope.on, f = p.fold;
+            snprintf(nm, sizeof nm, "void svla_apply_bf16<%d, %s, %s, %d>", D, r ? "true" : "false",
+                     f ? "true" : "false", p.esize);
+            if (p.esize == 2) {
+                if (r && f) launch(svla_apply_bf16<D, true, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else if (r) launch(svla_apply_bf16<D, true, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else if (f) launch(svla_apply_bf16<D, false, true>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
                 else launch(svla_apply_bf16<D, false, false>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+            } else {
+                if (r && f) launch(svla_apply_bf16<D, true, true, 1>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else if (r) launch(svla_apply_bf16<D, true, false, 1>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else if (f) launch(svla_apply_bf16<D, false, true, 1>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
+                else launch(svla_apply_bf16<D, false, false, 1>, grid, p.lds_apply, s, SLOT_APPLY, a, nm);
             }
         }
     } else {
@@ -2941,9 +3032,15 @@ void launch_fused(const Plan &p, const StepArgs &args, hipStream_t s)
     const unsigned grid = (unsigned)(8L * p.ftiles * ((p.BH + 7) / 8));
     constexpr int W = SVLA_FUSED_W, PF = SVLA_FUSED_PF, QG = SVLA_FUSED_QG;
     char nm[96];
-    snprintf(nm, sizeof nm, "void svla_step_fused<%s, %d, %d, %d>", p.rope.on ? "true" : "false", W, PF, QG);
-    if (p.rope.on) launch(svla_step_fused<true, W, PF, QG>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
-    else launch(svla_step_fused<false, W, PF, QG>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+    snprintf(nm, sizeof nm, "void svla_step_fused<%s, %d, %d, %d, %d>", p.rope.on ? "true" : "false", W, PF,
+             QG, p.esize);
+    if (p.esize == 2) {
+        if (p.rope.on) launch(svla_step_fused<true, W, PF, QG>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+        else launch(svla_step_fused<false, W, PF, QG>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+    } else {
+        if (p.rope.on) launch(svla_step_fused<true, W, PF, QG, 1>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+        else launch(svla_step_fused<false, W, PF, QG, 1>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+    }
 }
 
 // Whether the byte ranges [a, a + na) and [b, b + nb) share a byte (null: no).

@@ -37,7 +37,8 @@
  * unrotated.
  *
  * Conventions shared by every entry point:
- *   Layout   Q, K, V, O: contiguous [B,H,N,d] (d fastest), one dtype.
+ *   Layout   Q, K, V, O: contiguous [B,H,N,d] (d fastest), one dtype (with
+ *            SVLA_FP8, Q, K, V are fp8 and O is bf16).
  *            S: [B,H,d,d] fp32, S[k][v] (row = key feature, column = value
  *            feature).  z: [B,H,d] fp32.  g: fp32.
  *   Memory   All pointers except `rope` are device pointers (HIP), 16-byte
@@ -76,7 +77,7 @@ typedef enum svla_status {
     SVLA_OK = 0,
     SVLA_ERR_NULL = 1,        /* a required pointer is NULL                   */
     SVLA_ERR_SHAPE = 2,       /* negative size, slice too large, N % nb != 0  */
-    SVLA_ERR_DTYPE = 3,       /* dtype not SVLA_F32 / SVLA_BF16               */
+    SVLA_ERR_DTYPE = 3,       /* dtype not SVLA_F32 / SVLA_BF16 / SVLA_FP8    */
     SVLA_ERR_ALIGN = 4,       /* a device pointer not 16-byte aligned         */
     SVLA_ERR_UNSUPPORTED = 5, /* d not in {32,64,128}; RoPE split or grid too large */
     SVLA_ERR_WORKSPACE = 6,   /* workspace smaller than svla_workspace_size() */
@@ -86,7 +87,10 @@ typedef enum svla_status {
 
 typedef enum svla_dtype {
     SVLA_F32 = 0,   /* IEEE binary32 Q/K/V/O */
-    SVLA_BF16 = 1   /* bfloat16 Q/K/V/O; arithmetic accumulates in fp32 */
+    SVLA_BF16 = 1,  /* bfloat16 Q/K/V/O; arithmetic accumulates in fp32 */
+    SVLA_FP8 = 2    /* OCP FP8 E4M3 Q/K/V (1 byte per element; d = 32 only) with a
+                       bfloat16 O: the low-precision inputs that the abstract's
+                       NVFP4 deployment points to; arithmetic as for bf16 */
 } svla_dtype;
 
 /* Which call a workspace is sized for. */

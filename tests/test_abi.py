@@ -220,3 +220,10 @@ def test_temporal_conv_rejects(lib):
     assert f(bf, 1, 1000, 3, 1000, 1024, A, ctypes.c_void_p(1 << 40), A, None, None, None, None) == 2
     # nothing to do
     assert f(bf, 0, 2, 3, 4, 16, None, None, None, None, None, None, None) == 0
+
+
+def test_fp8_is_d32_only(lib):
+    st, _ = _ws(lib, _lib.OP_BLOCK_CAUSAL, _lib.SVLA_FP8, 1, 70, 7, 2640, 64)
+    assert st == 5 and b"fp8" in lib.svla_last_error()
+    st, n = _ws(lib, _lib.OP_BLOCK_CAUSAL, _lib.SVLA_FP8, 1, 70, 7, 2640, 32)
+    assert st == 0 and n > 0

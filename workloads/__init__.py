@@ -28,7 +28,8 @@ import numpy as np
 
 __all__ = [
     "ConvConfig", "CONV_CONFIGS", "make_conv_inputs",
-    "Rope", "Config", "CONFIGS", "get_config", "bf16_round", "bf16_bits",
+    "Rope", "Config", "CONFIGS", "get_config", "bf16_round", "bf16_bits", "fp8_bits",
+    "fp8_from_bits", "fp8_round",
     "bf16_from_bits", "make_inputs", "scaled_config",
 ]
 
@@ -60,7 +61,7 @@ class Config:
     d: int
     nb: int
     n: int
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16" or "fp8" (OCP E4M3 inputs)
     seed: int
     eps: float = 1e-6
     rope: Optional[Rope] = None
@@ -122,6 +123,44 @@ def bf16_from_bits(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def fp8_from_bits(b: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 ("fn": 1 sign, 4 exponent bits of bias 7, 3 mantissa bits,
+    no infinities, S.1111.111 is NaN) bit patterns (uint8) -> exact float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint8).astype(np.int32)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = (sign * mag).astype(np.float32)
+    out[(b & 0x7F) == 0x7F] = np.nan
+    return out
+
+
+def fp8_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3 bit patterns, round to nearest, ties to even
+    mantissa; magnitudes past the largest finite value (448) saturate to it;
+    NaN -> 0x7F with its sign."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    ax = np.abs(x).astype(np.float64)
+    out = np.zeros(x.shape, dtype=np.int32)
+    # the 127 non-negative finite codes, their values in increasing order
+    codes = np.arange(0x7F, dtype=np.int32)
+    vals = fp8_from_bits(codes.astype(np.uint8)).astype(np.float64)
+    idx = np.clip(np.searchsorted(vals, ax), 1, len(vals) - 1)   # vals[idx-1] <= ax <= vals[idx]
+    lo, hi = vals[idx - 1], vals[idx]
+    up = (ax - lo > hi - ax) | ((ax - lo == hi - ax) & ((idx - 1) % 2 == 1))
+    out = np.where(up, idx, idx - 1)
+    out = np.where(ax >= vals[-1], len(vals) - 1, out)           # saturate at 448
+    out = out | np.where(np.signbit(x), 0x80, 0)
+    out = np.where(np.isnan(x), 0x7F | np.where(np.signbit(x), 0x80, 0), out)
+    return out.astype(np.uint8)
+
+
+def fp8_round(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest OCP FP8 E4M3 value, as float32."""
+    return fp8_from_bits(fp8_bits(x))
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """float32 values rounded (RNE) to the nearest bf16, returned as float32."""
     return bf16_from_bits(bf16_bits(x))
@@ -157,6 +196,10 @@ def make_inputs(cfg: Config, seed: Optional[int] = None, *, B=None, H=None,
             bits = bf16_bits(x)
             out[name + "_bits"] = bits
             out[name] = bf16_from_bits(bits)
+        elif cfg.dtype == "fp8":
+            bits = fp8_bits(x)
+            out[name + "_bits"] = bits
+            out[name] = fp8_from_bits(bits)
         else:
             out[name] = x
     out["g"] = _gate(rng, (B, H, nb)) if cfg.gated else None
