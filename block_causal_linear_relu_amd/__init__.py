@@ -8,6 +8,7 @@ provides device memory (outputs, workspace) and the current stream.
     O, S, z = block_causal(Q, K, V, nb, return_state=True)
     O, S, z = block_causal(Q, K, V, nb, g=g)           # gated (SANA-Video 2.0)
     O, S, z = block_step(Q, K, V, S, z, rope=rope)     # streaming, state carried
+    grads = block_causal_backward(Q, K, V, dO, nb)     # dQ, dK, dV (+ dg, dS0, dz0)
 
 Tensors are [B,H,N,d] contiguous CUDA (HIP) tensors of torch.bfloat16,
 torch.float32 or torch.float8_e4m3fn (d = 32; O is then bfloat16); states
@@ -26,14 +27,15 @@ from . import _lib
 from ._lib import SvlaError, rope_struct  # noqa: F401
 
 __all__ = ["noncausal", "block_causal", "block_step", "block_step_noalloc", "state_build",
-           "state_scan", "apply", "temporal_conv",
+           "state_scan", "apply", "temporal_conv", "block_causal_backward",
            "workspace_size", "describe", "set_timing_events", "SvlaError", "library"]
 
 _DT = {torch.bfloat16: _lib.SVLA_BF16, torch.float32: _lib.SVLA_F32,
        torch.float8_e4m3fn: _lib.SVLA_FP8}
 _OPS = {"noncausal": _lib.OP_NONCAUSAL, "block_causal": _lib.OP_BLOCK_CAUSAL,
         "block_step": _lib.OP_BLOCK_STEP, "state_build": _lib.OP_STATE_BUILD,
-        "state_scan": _lib.OP_STATE_SCAN, "apply": _lib.OP_APPLY}
+        "state_scan": _lib.OP_STATE_SCAN, "apply": _lib.OP_APPLY,
+        "backward": _lib.OP_BACKWARD}
 
 
 def library() -> ctypes.CDLL:
@@ -376,3 +378,40 @@ def apply(Q, S_prefix, z_prefix, nb: int, rope=None, eps: float = 1e-6):
                                    rp, float(eps), _ptr(O), _ptr(ws), nbytes,
                                    _stream(Q.device)))
     return O
+
+
+def block_causal_backward(Q, K, V, dO, nb: int, S0=None, z0=None, g=None, rope=None,
+                          eps: float = 1e-6, need_dg: bool = False, need_dstate: bool = False,
+                          workspace=None) -> dict:
+    """Gradients of ``block_causal`` (same arguments) given dO = dLoss/dO.
+
+    Returns {"dQ", "dK", "dV"} in Q's dtype, plus "dg" [B,H,nb] when
+    ``need_dg`` and "dS0" [B,H,d,d], "dz0" [B,H,d] when ``need_dstate``
+    (float32)."""
+    B, H, N, d = _qkv_shape(Q, K, V)
+    if nb <= 0 or N % nb:
+        raise ValueError("N=%d is not a multiple of nb=%d" % (N, nb))
+    n = N // nb
+    _shape(dO, Q.shape, "dO")
+    _shape(S0, (B, H, d, d), "S0")
+    _shape(z0, (B, H, d), "z0")
+    _shape(g, (B, H, nb), "g")
+    _pair(S0, z0, "S0", "z0")
+    dt = _qkv(Q, K, V)
+    _dev(dO, "dO", Q.dtype)
+    S0, z0, g = _opt(S0, "S0"), _opt(z0, "z0"), _opt(g, "g")
+    lib = library()
+    out = {name: torch.empty(Q.shape, dtype=Q.dtype, device=Q.device) for name in ("dQ", "dK", "dV")}
+    if need_dg:
+        out["dg"] = torch.empty((B, H, nb), dtype=torch.float32, device=Q.device)
+    if need_dstate:
+        out["dS0"] = torch.empty((B, H, d, d), dtype=torch.float32, device=Q.device)
+        out["dz0"] = torch.empty((B, H, d), dtype=torch.float32, device=Q.device)
+    ws, nbytes = _ws_arg(workspace, "backward", Q, B, H, nb, n, d)
+    rp, _keep = _rope_arg(rope)
+    st = lib.svla_block_causal_backward(
+        dt, B, H, nb, n, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(S0), _ptr(z0), _ptr(g), rp,
+        float(eps), _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out.get("dg")),
+        _ptr(out.get("dS0")), _ptr(out.get("dz0")), _ptr(ws), nbytes, _stream(Q.device))
+    _lib.check(lib, st)
+    return out

@@ -19,7 +19,8 @@ STATUS_NAMES = {0: "SVLA_OK", 1: "SVLA_ERR_NULL", 2: "SVLA_ERR_SHAPE", 3: "SVLA_
                 4: "SVLA_ERR_ALIGN", 5: "SVLA_ERR_UNSUPPORTED", 6: "SVLA_ERR_WORKSPACE",
                 7: "SVLA_ERR_VALUE", 8: "SVLA_ERR_HIP"}
 SVLA_F32, SVLA_BF16, SVLA_FP8 = 0, 1, 2
-OP_NONCAUSAL, OP_BLOCK_CAUSAL, OP_BLOCK_STEP, OP_STATE_BUILD, OP_STATE_SCAN, OP_APPLY = range(6)
+(OP_NONCAUSAL, OP_BLOCK_CAUSAL, OP_BLOCK_STEP, OP_STATE_BUILD, OP_STATE_SCAN, OP_APPLY,
+ OP_BACKWARD) = range(7)
 
 
 class SvlaRope(ctypes.Structure):
@@ -57,6 +58,8 @@ PROTOTYPES = {
     "svla_state_scan": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "svla_apply": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _rp, _f, _vp, _vp, _sz, _vp]),
     "svla_temporal_conv": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "svla_block_causal_backward": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _rp, _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "svla_set_timing_events": (_i, [ctypes.POINTER(_vp), _i]),
     "svla_describe": (_i, [_i, _i, _i, _i, _i, _i, _i, _rp, ctypes.c_char_p, _sz]),
 }

@@ -2598,14 +2598,640 @@ svla_temporal_conv_k(const ConvArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Backward pass: the gradients of the block-causal forward, for block-causal
+// training (SANA-Video talk, the passage on causal training: a block cannot
+// see the next one).  Per (b,h), with p = phi(q), a = phi(k), p~ = R p,
+// a~ = R a, S_c / z_c the inclusive state of block c and, for token i of
+// block c, num_i = S_c^T p~_i, den_i = p_i . z_c + eps, O_i = num_i / den_i:
+//   dnum_i = dO_i / den_i, dden_i = -(dO_i . O_i) / den_i
+//   dq_i = [q_i > 0] (R_i^T S_c dnum_i + dden_i z_c)
+//   G_c = sum_{i in c} p~_i dnum_i^T + g_{c+1} G_{c+1},
+//   H_c = sum_{i in c} dden_i p_i + g_{c+1} H_{c+1}   (the gradient reaching S_c, z_c)
+//   dv_j = G_c^T a~_j, dk_j = [k_j > 0] (R_j^T G_c v_j + H_c)
+//   dg_c = <G_c, S_{c-1}> + <H_c, z_{c-1}>, dS0 = g_0 G_0, dz0 = g_0 H_0.
+// Three kernels after the forward state is rebuilt (state build + export
+// scan): the query side (dq and each split's share of the sums of G and H),
+// the reverse scan over blocks (G_c, H_c, dS0, dz0) and the key side (dk,
+// dv, dg).  All arithmetic is fp32: every product over features or tokens
+// runs on v_mfma_f32_32x32x2f32.
+//
+// Lane layout of the per-token work ("J layout"): in a 32-token group of a
+// wave, lane (n = lane % 32, h = lane / 32) owns token n and the features
+// 32 t + 8 u + 4 h + e (t < d/32, u < 4, e < 4), which are exactly the rows
+// that register 4 u + e of accumulator tile t holds for column n when the
+// MFMA's output rows are features and its columns tokens.  A contraction over
+// features can take its k-slots in any order, as long as both operands agree,
+// so the k-slot of lane half h at step (t, x) is feature 32 t + row(x, h): the
+// B operand is then a register the lane already holds (its own p~, dnum, a~
+// or v) and only the state operand is read, from LDS.  Every per-token
+// vector (q, dO, num, dnum, dp~, k, v, dv, da~) lives in this layout, so the
+// element-wise steps, RoPE's pairs (e = 0,1 and 2,3) and the loads and stores
+// (4 consecutive features per lane and chunk) need no data exchange; the two
+// halves of a token meet through one lane swap for each dot product over
+// features.  The sum over tokens of p~ dnum^T goes through a per-wave LDS
+// tile (rows swizzled in 4-float chunks against bank conflicts).
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+    const void *Q, *K, *V, *dO;
+    void *dQ, *dK, *dV;
+    const float *S_pre, *z_pre;    // inclusive forward states [BH*nb][d*d], [BH*nb][d]
+    float *dS_part, *dz_part;      // query side: [BH*nb][splits][d*d], [BH*nb][splits][d]
+    float *G, *Hz;                 // reverse scan: [BH*nb][d*d], [BH*nb][d]
+    const float *g, *S0, *z0;      // gate [BH][nb], state entering block 0 (each nullable)
+    float *dg, *dS0, *dz0;         // [BH][nb], [BH][d*d], [BH][d] (each nullable)
+    int N, n, nb, splits, chunk;   // splits of a block's tokens, tokens per split (a multiple of 32)
+    long BH;
+    float eps;
+    RopeK rope;
+};
+
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+
+// Row of register r of a 32x32 MFMA accumulator, for lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// 4 consecutive features at byte offset off (bf16 when ES == 2, fp32 when 4),
+// raw; bwd_floats4 turns them into fp32.
+template <int ES>
+struct Raw4 {
+    u32x2_t w2;
+    u32x4_t w4;
+};
+
+template <int ES>
+__device__ __forceinline__ Raw4<ES> bwd_load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    Raw4<ES> v;
+    if constexpr (ES == 2) v.w2 = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    else v.w4 = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return v;
+}
+
+template <int ES>
+__device__ __forceinline__ void bwd_floats4(const Raw4<ES> &v, float *f)
+{
+    if constexpr (ES == 2) {
+        f[0] = bf16lo(v.w2[0]); f[1] = bf16hi(v.w2[0]);
+        f[2] = bf16lo(v.w2[1]); f[3] = bf16hi(v.w2[1]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = as_f32(v.w4[e]);
+    }
+}
+
+template <int ES>
+__device__ __forceinline__ void bwd_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *f)
+{
+    if constexpr (ES == 2) {
+        const u32x2_t w = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, 0);
+    } else {
+        const u32x4_t w = {as_u32(f[0]), as_u32(f[1]), as_u32(f[2]), as_u32(f[3])};
+        store16(r, off, w);
+    }
+}
+
+// x <- R^T x for the pairs (x[2j], x[2j+1]) of a token at `pos` (the inverse
+// rotation: the angles of rope_rotate, negated).
+template <int PAIRS>
+__device__ __forceinline__ void rope_rotate_t(float *x, const RopePos &pos,
+                                              const RopePairs<PAIRS> &pp, const float2 *tab)
+{
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+        const int idx = pp.base[j] + (pos.fr & pp.mt[j]) + (pos.row & pp.mh[j]) + (pos.col & pp.mw[j]);
+        const float2 cs = tab[idx];
+        const float x0 = x[2 * j], x1 = x[2 * j + 1];
+        x[2 * j] = x0 * cs.x + x1 * cs.y;
+        x[2 * j + 1] = x1 * cs.x - x0 * cs.y;
+    }
+}
+
+// Column swizzle of the per-wave token tiles (rows of d floats): 4-float
+// chunks are permuted inside each 32-float (d = 32) or 64-float (d = 64) row
+// segment, so the 16-byte writes of one row chunk by 32 tokens and the reads
+// of one row by 32 lanes both spread over the 64 banks.
+template <int D>
+__device__ __forceinline__ int bwd_swz(int t)
+{
+    return D == 32 ? 4 * ((t >> 1) & 7) : 4 * (t & 15);
+}
+
+// The state (S_c or G_c) of one block into LDS twice: M[k][j] row-major and
+// its transpose Mt[j][k] (rows of d floats), and the vector (z_c or H_c).
+template <int D>
+__device__ __forceinline__ void bwd_state_to_lds(const float *S, const float *z, float *M, float *Mt,
+                                                 float *vec)
+{
+    for (int e = threadIdx.x * 4; e < D * D; e += kThreads * 4) {
+        const f32x4_t v = *(const f32x4_t *)(S + e);
+        *(f32x4_t *)(M + e) = v;
+        const int k = e / D, j = e % D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Mt[(j + i) * D + k] = v[i];
+    }
+    if (threadIdx.x < D) vec[threadIdx.x] = z[threadIdx.x];
+}
+
+// Query side.  Workgroup = (bh, block c, split s); wave w takes the 32-token
+// groups w, w + 4, ... of the split and keeps the next group's loads in
+// flight.  Per group: num^T = S_c^T p~^T (MFMA), den, O, dnum, dden,
+// dp~^T = S_c dnum^T (MFMA), dq = [q > 0] (R^T dp~ + dden z_c) stored, and
+// p~^T dnum accumulated over the wave's tokens (MFMA over the LDS tile);
+// dden p is summed per lane.  At the end the four waves' sums are added
+// through LDS and written as split s's partial of block c.
+template <int D, int ES, bool ROPE>
+__global__ void __launch_bounds__(kThreads)
+svla_bwd_query(const BwdArgs a)
+{
+    constexpr int T = D / 32;               // 32-row tiles per side
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 31, h = lane >> 5;
+    const unsigned per_bh = (unsigned)(a.splits * a.nb);
+    const long bh = blockIdx.x / per_bh;
+    const int rest = (int)(blockIdx.x - bh * per_bh);
+    const int c = rest / a.splits, s = rest % a.splits;
+    const long unit = bh * a.nb + c;
+    const int tok_lo = c * a.n + s * a.chunk;
+    const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
+
+    float2 *tab = (float2 *)lds;
+    float *Ss = (float *)(lds + (ROPE ? a.rope.tab_bytes : 0));
+    float *St = Ss + D * D;
+    float *zs = St + D * D;
+    float *work = zs + 64;
+    float *Pt = work + wave * 2 * 32 * D, *Dn = Pt + 32 * D;
+
+    const uint32_t slice = (uint32_t)a.N * D * ES;
+    const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
+    const auto rO = make_rsrc((const char *)a.dO + bh * slice, slice);
+    const auto rdQ = make_rsrc((char *)a.dQ + bh * slice, slice);
+
+    const int ngroups = (tok_hi - tok_lo + 31) / 32;
+    auto row_off = [&](int grp) -> uint32_t {
+        const int tok = tok_lo + grp * 32 + m;
+        return grp < ngroups && tok < tok_hi ? (uint32_t)tok * (D * ES) : kOOB;
+    };
+    // first group's loads go out before the state and table are set up
+    Raw4<ES> qr[T][4], orw[T][4];
+    int grp = wave;
+    {
+        const uint32_t ro = row_off(grp);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t off = ro == kOOB ? kOOB : ro + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
+                qr[t][u] = bwd_load4<ES>(rQ, off);
+                orw[t][u] = bwd_load4<ES>(rO, off);
+            }
+    }
+    bwd_state_to_lds<D>(a.S_pre + unit * D * D, a.z_pre + unit * D, Ss, St, zs);
+    uint32_t frame_lo = 0;
+    RopePairs<2> pp[T][4];
+    if constexpr (ROPE) {
+        frame_lo = fdiv((uint32_t)tok_lo, a.rope.div_hw);
+        const uint32_t frame_hi = fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw);
+        const int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pp[t][u] = rope_pairs<2>(a.rope, 32 * t + 8 * u + 4 * h, nf);
+    }
+    __syncthreads();
+
+    f32x16_t dS[T][T];
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dS[i][j][r] = 0.f;
+    float dz[T][16];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dz[t][r] = 0.f;
+    float zr[T][16];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zr[t][r] = zs[32 * t + acc_row(r, h)];
+
+    for (; grp < ngroups; grp += 4) {
+        const uint32_t ro = row_off(grp);
+        float q[T][16], p[T][16], pt[T][16], dO[T][16];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                bwd_floats4<ES>(qr[t][u], &q[t][4 * u]);
+                bwd_floats4<ES>(orw[t][u], &dO[t][4 * u]);
+            }
+        // the next group's loads
+        {
+            const uint32_t rn = row_off(grp + 4);
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t off = rn == kOOB ? kOOB : rn + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
+                    qr[t][u] = bwd_load4<ES>(rQ, off);
+                    orw[t][u] = bwd_load4<ES>(rO, off);
+                }
+        }
+        float denp = 0.f;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[t][r] = fmaxf(q[t][r], 0.f);
+                pt[t][r] = p[t][r];
+                denp += p[t][r] * zr[t][r];
+            }
+        RopePos pos{0, 0, 0};
+        if constexpr (ROPE) {
+            const int tok = min(tok_lo + grp * 32 + m, tok_hi - 1);
+            pos = rope_pos((uint32_t)tok, frame_lo, a.rope);
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) rope_rotate<2>(&pt[t][4 * u], pos, pp[t][u], tab);
+        }
+        // num^T = S^T p~^T
+        f32x16_t num[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) num[t][r] = 0.f;
+#pragma unroll
+        for (int tk = 0; tk < T; ++tk)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const float *row = Ss + (32 * tk + acc_row(x, h)) * D + m;
+#pragma unroll
+                for (int to = 0; to < T; ++to)
+                    num[to] = __builtin_amdgcn_mfma_f32_32x32x2f32(row[32 * to], pt[tk][x], num[to], 0, 0, 0);
+            }
+        const float den = denp + __shfl_xor(denp, 32) + a.eps;
+        const float inv = den != 0.f ? 1.f / den : 0.f;
+        float dotp = 0.f;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dotp += dO[t][r] * (num[t][r] * inv);
+        const float dden = -(dotp + __shfl_xor(dotp, 32)) * inv;
+        float dn[T][16];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dn[t][r] = dO[t][r] * inv;
+        // dp~^T = S dnum^T
+        f32x16_t dpt[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dpt[t][r] = 0.f;
+#pragma unroll
+        for (int tj = 0; tj < T; ++tj)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const float *row = St + (32 * tj + acc_row(x, h)) * D + m;
+#pragma unroll
+                for (int to = 0; to < T; ++to)
+                    dpt[to] = __builtin_amdgcn_mfma_f32_32x32x2f32(row[32 * to], dn[tj][x], dpt[to], 0, 0, 0);
+            }
+        // dq = [q > 0] (R^T dp~ + dden z)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = dpt[t][4 * u + e];
+                if constexpr (ROPE) rope_rotate_t<2>(v, pos, pp[t][u], tab);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * u + e;
+                    v[e] = q[t][r] > 0.f ? v[e] + dden * zr[t][r] : 0.f;
+                }
+                bwd_store4<ES>(rdQ, ro == kOOB ? kOOB : ro + (uint32_t)((32 * t + 8 * u + 4 * h) * ES), v);
+            }
+        // the sums over tokens: dz per lane, p~^T dnum through the wave's tile
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dz[t][r] += dden * p[t][r];
+        const int sw = bwd_swz<D>(m);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int col = (32 * t + 8 * u + 4 * h) ^ sw;
+                *(f32x4_t *)(Pt + m * D + col) =
+                    (f32x4_t){pt[t][4 * u], pt[t][4 * u + 1], pt[t][4 * u + 2], pt[t][4 * u + 3]};
+                *(f32x4_t *)(Dn + m * D + col) =
+                    (f32x4_t){dn[t][4 * u], dn[t][4 * u + 1], dn[t][4 * u + 2], dn[t][4 * u + 3]};
+            }
+#pragma unroll
+        for (int pi = 0; pi < 16; ++pi) {
+            const int tt = 2 * pi + h, swr = bwd_swz<D>(tt);
+            float av[T], bv[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                av[t] = Pt[tt * D + ((32 * t + m) ^ swr)];
+                bv[t] = Dn[tt * D + ((32 * t + m) ^ swr)];
+            }
+#pragma unroll
+            for (int i = 0; i < T; ++i)
+#pragma unroll
+                for (int j = 0; j < T; ++j)
+                    dS[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], dS[i][j], 0, 0, 0);
+        }
+    }
+    // this split's partials: the four waves' p~^T dnum tiles, then dden p
+    __syncthreads();
+    float *red = work;
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[((wave * T * T + i * T + j) * 16 + r) * 64 + lane] = dS[i][j][r];
+    __syncthreads();
+    const auto rS = make_rsrc(a.dS_part + (unit * a.splits + s) * D * D, D * D * 4);
+    for (int e = tid * 4; e < D * D; e += kThreads * 4) {
+        const int k = e / D, j0 = e % D;
+        const int tile = (k / 32) * T + j0 / 32;
+        const int r = 4 * ((k % 32) / 8) + k % 4, hh = (k % 8) / 4;
+        u32x4_t o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ln = (j0 + i) % 32 + 32 * hh;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) v += red[((w * T * T + tile) * 16 + r) * 64 + ln];
+            o[i] = as_u32(v);
+        }
+        store16(rS, (uint32_t)e * 4u, o);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(wave * 64 + lane) * (16 * T) + 16 * t + r] = dz[t][r];
+    __syncthreads();
+    // feature f sits in register (t, r) of the lanes of half hh; 256 / D
+    // threads per feature each add a share of the 4 x 32 lanes, then one adds those
+    float *red2 = red + 4 * 64 * 16 * T;
+    {
+        constexpr int PARTS = kThreads / D;
+        const int f = tid % D, part = tid / D;
+        const int t = f / 32, r = 4 * ((f % 32) / 8) + f % 4, hh = (f % 8) / 4;
+        float v = 0.f;
+        for (int i = part; i < 128; i += PARTS) {
+            const int w = i / 32, ln = i % 32 + 32 * hh;
+            v += red[(w * 64 + ln) * (16 * T) + 16 * t + r];
+        }
+        red2[part * D + f] = v;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float v = 0.f;
+        for (int part = 0; part < kThreads / D; ++part) v += red2[part * D + tid];
+        a.dz_part[(unit * a.splits + s) * D + tid] = v;
+    }
+}
+
+// Reverse scan over blocks: G_c = (sum of block c's split partials) +
+// g_{c+1} G_{c+1} (H likewise), from the last block back; dS0 = g_0 G_0,
+// dz0 = g_0 H_0.  Each thread owns 4 consecutive entries of [S | z] of one
+// (bh) and walks the blocks in chunks of 4, all loads of a chunk issued
+// before any is added.  With no tokens (splits = 0) every G, H is zero.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+svla_bwd_scan(const BwdArgs a)
+{
+    constexpr int E4 = (D * D + D) / 4;
+    constexpr int TILES = (E4 + kThreads - 1) / kThreads;
+    constexpr int MS = 4;                    // split partials per block at most
+    const long bh = blockIdx.x / TILES;
+    const int idx = (int)(blockIdx.x % TILES) * kThreads + threadIdx.x;
+    if (a.splits == 0 && a.dg && blockIdx.x % TILES == 0) {
+        // no tokens: no key-side kernel forms the gate gradient, which is zero
+        for (int c = threadIdx.x; c < a.nb; c += kThreads) a.dg[bh * a.nb + c] = 0.f;
+    }
+    if (idx >= E4) return;
+    const int e = idx * 4;
+    const bool isz = e >= D * D;
+    const int off = isz ? e - D * D : e;
+    const int stride = isz ? D : D * D;
+    const float *part = (isz ? a.dz_part : a.dS_part) + bh * (long)a.nb * a.splits * stride + off;
+    float *out = (isz ? a.Hz : a.G) + bh * (long)a.nb * stride + off;
+    const float *g = a.g ? a.g + bh * a.nb : nullptr;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int sp = a.splits;
+    for (int c0 = a.nb - 1; c0 >= 0; c0 -= 4) {
+        f32x4_t L[4][MS];
+        if (sp > 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = max(c0 - j, 0);
+#pragma unroll
+                for (int q = 0; q < MS; ++q)
+                    L[j][q] = *(const f32x4_t *)(part + ((long)c * sp + min(q, sp - 1)) * stride);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = c0 - j;
+            if (c < 0) break;
+            const float gn = c + 1 < a.nb ? (g ? g[c + 1] : 1.f) : 0.f;
+            acc *= gn;
+#pragma unroll
+            for (int q = 0; q < MS; ++q)
+                if (q < sp) acc += L[j][q];
+            *(f32x4_t *)(out + (long)c * stride) = acc;
+        }
+    }
+    const float g0 = g ? g[0] : 1.f;
+    float *d0 = isz ? a.dz0 : a.dS0;
+    if (d0 && a.nb > 0) *(f32x4_t *)(d0 + bh * (long)stride + off) = g0 * acc;
+}
+
+// Key side.  Workgroup = (bh, block c, split s): G_c, H_c in LDS; per
+// 32-token group dv^T = G^T a~^T and da~^T = G v^T (MFMA), dk = [k > 0]
+// (R^T da~ + H).  Split 0 also forms dg_c = <G_c, S_{c-1}> + <H_c, z_{c-1}>.
+template <int D, int ES, bool ROPE>
+__global__ void __launch_bounds__(kThreads)
+svla_bwd_key(const BwdArgs a)
+{
+    constexpr int T = D / 32;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 31, h = lane >> 5;
+    const unsigned per_bh = (unsigned)(a.splits * a.nb);
+    const long bh = blockIdx.x / per_bh;
+    const int rest = (int)(blockIdx.x - bh * per_bh);
+    const int c = rest / a.splits, s = rest % a.splits;
+    const long unit = bh * a.nb + c;
+    const int tok_lo = c * a.n + s * a.chunk;
+    const int tok_hi = min(tok_lo + a.chunk, (c + 1) * a.n);
+
+    float2 *tab = (float2 *)lds;
+    float *Gs = (float *)(lds + (ROPE ? a.rope.tab_bytes : 0));
+    float *Gt = Gs + D * D;
+    float *hs = Gt + D * D;
+    float *red = hs + 64;
+
+    const uint32_t slice = (uint32_t)a.N * D * ES;
+    const auto rK = make_rsrc((const char *)a.K + bh * slice, slice);
+    const auto rV = make_rsrc((const char *)a.V + bh * slice, slice);
+    const auto rdK = make_rsrc((char *)a.dK + bh * slice, slice);
+    const auto rdV = make_rsrc((char *)a.dV + bh * slice, slice);
+
+    const int ngroups = (tok_hi - tok_lo + 31) / 32;
+    auto row_off = [&](int grp) -> uint32_t {
+        const int tok = tok_lo + grp * 32 + m;
+        return grp < ngroups && tok < tok_hi ? (uint32_t)tok * (D * ES) : kOOB;
+    };
+    Raw4<ES> kr[T][4], vr[T][4];
+    int grp = wave;
+    {
+        const uint32_t ro = row_off(grp);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t off = ro == kOOB ? kOOB : ro + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
+                kr[t][u] = bwd_load4<ES>(rK, off);
+                vr[t][u] = bwd_load4<ES>(rV, off);
+            }
+    }
+    bwd_state_to_lds<D>(a.G + unit * D * D, a.Hz + unit * D, Gs, Gt, hs);
+    uint32_t frame_lo = 0;
+    RopePairs<2> pp[T][4];
+    if constexpr (ROPE) {
+        frame_lo = fdiv((uint32_t)tok_lo, a.rope.div_hw);
+        const uint32_t frame_hi = fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw);
+        const int nf = (int)(frame_hi - frame_lo) + 1;
+        rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pp[t][u] = rope_pairs<2>(a.rope, 32 * t + 8 * u + 4 * h, nf);
+    }
+    __syncthreads();
+    if (s == 0 && a.dg) {
+        // dg_c: the state before block c is S_{c-1}, S0 for block 0 (zero without it)
+        const float *Sp = c > 0 ? a.S_pre + (unit - 1) * D * D : a.S0 ? a.S0 + bh * D * D : nullptr;
+        const float *zp = c > 0 ? a.z_pre + (unit - 1) * D : a.z0 ? a.z0 + bh * D : nullptr;
+        float v = 0.f;
+        if (Sp) {
+            for (int e = tid; e < D * D; e += kThreads) v += Gs[e] * Sp[e];
+            if (tid < D) v += hs[tid] * zp[tid];
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        if (lane == 0) red[wave] = v;
+        __syncthreads();
+        if (tid == 0) a.dg[unit] = red[0] + red[1] + red[2] + red[3];
+    }
+    float hr[T][16];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hr[t][r] = hs[32 * t + acc_row(r, h)];
+
+    for (; grp < ngroups; grp += 4) {
+        const uint32_t ro = row_off(grp);
+        float k[T][16], at[T][16], v[T][16];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                bwd_floats4<ES>(kr[t][u], &k[t][4 * u]);
+                bwd_floats4<ES>(vr[t][u], &v[t][4 * u]);
+            }
+        {
+            const uint32_t rn = row_off(grp + 4);
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t off = rn == kOOB ? kOOB : rn + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
+                    kr[t][u] = bwd_load4<ES>(rK, off);
+                    vr[t][u] = bwd_load4<ES>(rV, off);
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) at[t][r] = fmaxf(k[t][r], 0.f);
+        RopePos pos{0, 0, 0};
+        if constexpr (ROPE) {
+            const int tok = min(tok_lo + grp * 32 + m, tok_hi - 1);
+            pos = rope_pos((uint32_t)tok, frame_lo, a.rope);
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) rope_rotate<2>(&at[t][4 * u], pos, pp[t][u], tab);
+        }
+        // dv^T = G^T a~^T and da~^T = G v^T
+        f32x16_t dv[T], da[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { dv[t][r] = 0.f; da[t][r] = 0.f; }
+#pragma unroll
+        for (int tk = 0; tk < T; ++tk)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const int kap = 32 * tk + acc_row(x, h);
+                const float *rowG = Gs + kap * D + m, *rowT = Gt + kap * D + m;
+#pragma unroll
+                for (int to = 0; to < T; ++to) {
+                    dv[to] = __builtin_amdgcn_mfma_f32_32x32x2f32(rowG[32 * to], at[tk][x], dv[to], 0, 0, 0);
+                    da[to] = __builtin_amdgcn_mfma_f32_32x32x2f32(rowT[32 * to], v[tk][x], da[to], 0, 0, 0);
+                }
+            }
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t off = ro == kOOB ? kOOB : ro + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
+                float x4[4], y4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x4[e] = dv[t][4 * u + e];
+                    y4[e] = da[t][4 * u + e];
+                }
+                if constexpr (ROPE) rope_rotate_t<2>(y4, pos, pp[t][u], tab);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * u + e;
+                    y4[e] = k[t][r] > 0.f ? y4[e] + hr[t][r] : 0.f;
+                }
+                bwd_store4<ES>(rdV, off, x4);
+                bwd_store4<ES>(rdK, off, y4);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 thread_local char g_err[512] = "";
 thread_local void *const *t_events = nullptr;   // svla_set_timing_events
 thread_local int t_nev = 0;
 
-enum Slot { SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2, SLOT_STEP = 3, SLOT_CONV = 4 };
-constexpr int kSlots = 5;
+enum Slot {
+    SLOT_BUILD = 0, SLOT_SCAN = 1, SLOT_APPLY = 2, SLOT_STEP = 3, SLOT_CONV = 4,
+    SLOT_BWD_QUERY = 5, SLOT_BWD_SCAN = 6, SLOT_BWD_KEY = 7
+};
+constexpr int kSlots = 8;
 
 // Every kernel goes through here.  With timing events set, the launch
 // carries a start/stop event pair that the runtime records around the
@@ -3143,6 +3769,97 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
     return SVLA_OK;
 }
 
+
+// ---- backward ---------------------------------------------------------------
+
+constexpr int kBwdMaxSplits = 4;     // query/key splits per block (the reverse scan reads this many)
+constexpr long kBwdWgs = 2048;       // query/key: workgroups wanted per launch
+constexpr int kBwdMinChunk = 128;    // ... but at least one 32-token group per wave
+
+struct BwdPlan {
+    Plan fwd;                        // the forward state rebuild: state build + export scan
+    int splits, chunk;               // query/key workgroups per block, tokens per workgroup
+    int tab_bytes;                   // LDS of the RoPE table (query and key kernels)
+    size_t lds_query, lds_key;
+    size_t off_spre, off_zpre, off_dsp, off_dzp, off_G, off_H, total;
+};
+
+svla_status make_bwd_plan(const char *fn, svla_dtype dt, int B, int H, int nb, int n, int d,
+                          const svla_rope *rope, BwdPlan *bp)
+{
+    memset(bp, 0, sizeof *bp);
+    if (dt == SVLA_FP8) return fail(SVLA_ERR_UNSUPPORTED, fn, "the backward pass takes SVLA_F32 or SVLA_BF16");
+    svla_status st = make_plan(fn, SVLA_OP_BLOCK_CAUSAL, dt, B, H, nb, n, d, rope, &bp->fwd);
+    if (st) return st;
+    if (d == 128) return fail(SVLA_ERR_UNSUPPORTED, fn, "the backward pass takes d = 32 or 64 (got 128)");
+    const Plan &p = bp->fwd;
+    const long units = p.BH * nb;
+    if (n > 0 && units > 0) {
+        long sp = (kBwdWgs + units - 1) / units;
+        if (sp > kBwdMaxSplits) sp = kBwdMaxSplits;
+        int chunk = (int)((n + sp - 1) / sp);
+        chunk = (chunk + 31) / 32 * 32;
+        if (chunk < kBwdMinChunk) chunk = kBwdMinChunk;
+        bp->chunk = chunk;
+        bp->splits = (n + chunk - 1) / chunk;
+    }
+    if (p.rope.on) {
+        const long e = (long)frames_spanned_max(bp->chunk, p.rope.gh * p.rope.gw) * (p.rope.dt / 2) +
+                       (long)p.rope.gh * (p.rope.dh / 2) + (long)p.rope.gw * (p.rope.dw / 2) + 1;
+        if (e > kMaxRopeEntries)
+            return fail(SVLA_ERR_UNSUPPORTED, fn, "RoPE table of %ld entries exceeds %d (grid %dx%d too large)",
+                        e, kMaxRopeEntries, p.rope.gh, p.rope.gw);
+        bp->tab_bytes = (int)((e * 8 + 255) & ~255L);
+    }
+    bp->lds_query = (size_t)bp->tab_bytes + ((size_t)2 * d * d + 64 + 256 * (size_t)d) * 4;
+    bp->lds_key = (size_t)bp->tab_bytes + ((size_t)2 * d * d + 64 + 64) * 4;
+    // workspace: the forward's split partials, then the rebuilt prefix states,
+    // the query side's partials and the reverse scan's G, H
+    size_t off = p.off_sop;
+    bp->off_spre = off; off = align256(off + (size_t)units * d * d * 4);
+    bp->off_zpre = off; off = align256(off + (size_t)units * d * 4);
+    bp->off_dsp = off; off = align256(off + (size_t)units * kBwdMaxSplits * d * d * 4);
+    bp->off_dzp = off; off = align256(off + (size_t)units * kBwdMaxSplits * d * 4);
+    bp->off_G = off; off = align256(off + (size_t)units * d * d * 4);
+    bp->off_H = off; off = align256(off + (size_t)units * d * 4);
+    bp->total = off;
+    return SVLA_OK;
+}
+
+template <int D, int ES>
+void launch_bwd_d(const BwdPlan &bp, const BwdArgs &a, bool tokens, hipStream_t s)
+{
+    const Plan &p = bp.fwd;
+    const bool r = p.rope.on;
+    const unsigned grid = (unsigned)(p.BH * p.nb * bp.splits);
+    char nm[96];
+    if (tokens) {
+        snprintf(nm, sizeof nm, "void svla_bwd_query<%d, %d, %s>", D, ES, r ? "true" : "false");
+        if (r) launch(svla_bwd_query<D, ES, true>, grid, bp.lds_query, s, SLOT_BWD_QUERY, a, nm);
+        else launch(svla_bwd_query<D, ES, false>, grid, bp.lds_query, s, SLOT_BWD_QUERY, a, nm);
+        if (hipPeekAtLastError() != hipSuccess) return;
+    }
+    constexpr int E4 = (D * D + D) / 4;
+    const unsigned sgrid = (unsigned)(p.BH * ((E4 + kThreads - 1) / kThreads));
+    snprintf(nm, sizeof nm, "void svla_bwd_scan<%d>", D);
+    launch(svla_bwd_scan<D>, sgrid, 0, s, SLOT_BWD_SCAN, a, nm);
+    if (hipPeekAtLastError() != hipSuccess) return;
+    if (tokens) {
+        snprintf(nm, sizeof nm, "void svla_bwd_key<%d, %d, %s>", D, ES, r ? "true" : "false");
+        if (r) launch(svla_bwd_key<D, ES, true>, grid, bp.lds_key, s, SLOT_BWD_KEY, a, nm);
+        else launch(svla_bwd_key<D, ES, false>, grid, bp.lds_key, s, SLOT_BWD_KEY, a, nm);
+    }
+}
+
+void bwd_any(const BwdPlan &bp, const BwdArgs &a, bool tokens, hipStream_t s)
+{
+    const int d = bp.fwd.d, es = bp.fwd.esize;
+    if (d == 32 && es == 2) launch_bwd_d<32, 2>(bp, a, tokens, s);
+    else if (d == 32) launch_bwd_d<32, 4>(bp, a, tokens, s);
+    else if (es == 2) launch_bwd_d<64, 2>(bp, a, tokens, s);
+    else launch_bwd_d<64, 4>(bp, a, tokens, s);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -3261,7 +3978,8 @@ svla_status svla_describe(svla_op op, svla_dtype dt, int B, int H, int nb, int n
         if ((long)nb * n > 0) apply_any(p, aa, nullptr);
         t_desc = nullptr;
     }
-    static const char *slot_name[kSlots] = {"build", "scan", "apply", "step", "conv"};
+    static const char *slot_name[kSlots] = {"build", "scan", "apply", "step", "conv",
+                                            "bwd_query", "bwd_scan", "bwd_key"};
     int w = snprintf(buf, len, "{\"fused\": %s, \"step_tiles\": %d, \"step_tile\": %d, \"splits\": %d, "
                      "\"chunk\": %d, \"apply_tile\": %d, \"workspace\": %zu",
                      p.fused ? "true" : "false", p.fused ? p.ftiles : 0, p.fused ? p.ftile : 0,
@@ -3289,8 +4007,15 @@ svla_status svla_workspace_size(svla_op op, svla_dtype dt, int B, int H, int nb,
 {
     const char *fn = "svla_workspace_size";
     if (!bytes) return fail(SVLA_ERR_NULL, fn, "bytes is NULL");
-    if ((int)op < SVLA_OP_NONCAUSAL || (int)op > SVLA_OP_APPLY)
+    if ((int)op < SVLA_OP_NONCAUSAL || (int)op > SVLA_OP_BACKWARD)
         return fail(SVLA_ERR_VALUE, fn, "unknown op %d", (int)op);
+    if (op == SVLA_OP_BACKWARD) {
+        BwdPlan bp;
+        svla_status st = make_bwd_plan(fn, dt, B, H, nb, n, d, nullptr, &bp);
+        if (st) return st;
+        *bytes = bp.total;
+        return SVLA_OK;
+    }
     Plan p;
     svla_status st = make_plan(fn, op, dt, B, H, nb, n, d, nullptr, &p);
     if (st) return st;
@@ -3414,6 +4139,85 @@ svla_status svla_temporal_conv(svla_dtype dt, int B, int nb, int F, int P, int C
     snprintf(nm, sizeof nm, "void svla_temporal_conv_k<%d, %d>", dt == SVLA_BF16 ? 2 : 4, MF);
     if (dt == SVLA_BF16) launch(svla_temporal_conv_k<2, MF>, grid, 0, s, SLOT_CONV, a, nm);
     else launch(svla_temporal_conv_k<4, MF>, grid, 0, s, SLOT_CONV, a, nm);
+    return check_launch(fn);
+}
+
+svla_status svla_block_causal_backward(svla_dtype dt, int B, int H, int nb, int n, int d,
+                                       const void *Q, const void *K, const void *V, const void *dO,
+                                       const float *S0, const float *z0, const float *g,
+                                       const svla_rope *rope, float eps, void *dQ, void *dK,
+                                       void *dV, float *dg, float *dS0, float *dz0, void *ws,
+                                       size_t ws_bytes, svla_stream stream)
+{
+    const char *fn = "svla_block_causal_backward";
+    BwdPlan bp;
+    svla_status st = make_bwd_plan(fn, dt, B, H, nb, n, d, rope, &bp);
+    if (st) return st;
+    const Plan &p = bp.fwd;
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(SVLA_ERR_VALUE, fn, "eps must be finite and >= 0");
+    if (p.BH * nb == 0) return SVLA_OK;
+    const bool tokens = n > 0;
+    if (tokens && (!Q || !K || !V || !dO || !dQ || !dK || !dV))
+        return fail(SVLA_ERR_NULL, fn, "Q, K, V, dO, dQ, dK and dV are required");
+    if ((S0 == nullptr) != (z0 == nullptr)) return fail(SVLA_ERR_NULL, fn, "pass both S0 and z0, or neither");
+    if ((dS0 == nullptr) != (dz0 == nullptr)) return fail(SVLA_ERR_NULL, fn, "pass both dS0 and dz0, or neither");
+    if (misaligned(Q) || misaligned(K) || misaligned(V) || misaligned(dO) || misaligned(dQ) ||
+        misaligned(dK) || misaligned(dV) || misaligned(S0) || misaligned(z0) || misaligned(g) ||
+        misaligned(dg) || misaligned(dS0) || misaligned(dz0) || misaligned(ws))
+        return fail(SVLA_ERR_ALIGN, fn, "device pointers must be 16-byte aligned");
+    if (tokens) {
+        // every gradient is written while some input is still to be read
+        const size_t tb = (size_t)p.BH * nb * n * d * p.esize;
+        const void *in[4] = {Q, K, V, dO};
+        void *out[3] = {dQ, dK, dV};
+        for (int i = 0; i < 3; ++i) {
+            for (int j = 0; j < 4; ++j)
+                if (overlap(out[i], tb, in[j], tb))
+                    return fail(SVLA_ERR_VALUE, fn, "dQ, dK and dV must not overlap Q, K, V or dO");
+            for (int j = i + 1; j < 3; ++j)
+                if (overlap(out[i], tb, out[j], tb))
+                    return fail(SVLA_ERR_VALUE, fn, "dQ, dK and dV must not overlap each other");
+        }
+    }
+    if (!ws) return fail(SVLA_ERR_NULL, fn, "workspace of %zu bytes required", bp.total);
+    if (ws_bytes < bp.total)
+        return fail(SVLA_ERR_WORKSPACE, fn, "workspace of %zu bytes is smaller than the %zu needed",
+                    ws_bytes, bp.total);
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    (void)hipGetLastError();
+    if (tokens) {
+        // the forward's inclusive states, block by block
+        BuildArgs ba;
+        memset(&ba, 0, sizeof ba);
+        ba.K = K; ba.V = V;
+        ba.S_part = (float *)(w + p.off_spart);
+        ba.z_part = (float *)(w + p.off_zpart);
+        ba.N = nb * n; ba.n = n; ba.nb = nb; ba.splits = p.splits; ba.chunk = p.chunk;
+        ba.BH = p.BH;
+        ba.rope = p.rope;
+        build_any(p, ba, s);
+        if ((st = check_launch(fn))) return st;
+        ScanArgs sa;
+        memset(&sa, 0, sizeof sa);
+        sa.S_part = ba.S_part; sa.z_part = ba.z_part; sa.g = g; sa.S_in = S0; sa.z_in = z0;
+        sa.S_pre = (float *)(w + bp.off_spre); sa.z_pre = (float *)(w + bp.off_zpre);
+        sa.nb = nb; sa.splits = p.splits;
+        scan_any<SCAN_EXPORT>(p, sa, s);
+        if ((st = check_launch(fn))) return st;
+    }
+    BwdArgs a;
+    memset(&a, 0, sizeof a);
+    a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.dQ = dQ; a.dK = dK; a.dV = dV;
+    a.S_pre = (const float *)(w + bp.off_spre); a.z_pre = (const float *)(w + bp.off_zpre);
+    a.dS_part = (float *)(w + bp.off_dsp); a.dz_part = (float *)(w + bp.off_dzp);
+    a.G = (float *)(w + bp.off_G); a.Hz = (float *)(w + bp.off_H);
+    a.g = g; a.S0 = S0; a.z0 = z0; a.dg = dg; a.dS0 = dS0; a.dz0 = dz0;
+    a.N = nb * n; a.n = n; a.nb = nb; a.splits = bp.splits; a.chunk = bp.chunk;
+    a.BH = p.BH; a.eps = eps;
+    a.rope = p.rope;
+    a.rope.tab_bytes = bp.tab_bytes;
+    bwd_any(bp, a, tokens, s);
     return check_launch(fn);
 }
 

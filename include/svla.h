@@ -100,7 +100,8 @@ typedef enum svla_op {
     SVLA_OP_BLOCK_STEP = 2,     /* also the gated variant */
     SVLA_OP_STATE_BUILD = 3,
     SVLA_OP_STATE_SCAN = 4,
-    SVLA_OP_APPLY = 5
+    SVLA_OP_APPLY = 5,
+    SVLA_OP_BACKWARD = 6        /* svla_block_causal_backward */
 } svla_op;
 
 /* 3D RoPE on the numerator (host struct; may live on the stack).
@@ -277,12 +278,44 @@ svla_status svla_temporal_conv(svla_dtype dt, int B, int nb, int F, int P, int C
                                const void *X, void *Y, const float *w, const float *bias,
                                const void *cache_in, void *cache_out, svla_stream stream);
 
+/* ---- training: the backward pass ----------------------------------------------- */
+
+/* Gradients of svla_block_causal / svla_block_causal_gated for block-causal
+ * training (talk, the causal-training passage: block c cannot see block c+1,
+ * so its tokens read only the states of blocks 0 .. c).  Given the forward's
+ * inputs and dO = dLoss/dO [B,H,nb*n,d], writes
+ *   dQ, dK, dV [B,H,nb*n,d] in the input dtype (required when n > 0);
+ *   dg  [B,H,nb] fp32: dLoss/dg[b,h,c] (nullable; with g NULL it is the
+ *       gradient with respect to a gate of 1 on every block);
+ *   dS0 [B,H,d,d], dz0 [B,H,d] fp32: dLoss/dS0, dLoss/dz0 (nullable, both or
+ *       neither; zero when nothing reaches them).
+ * The forward's block states are rebuilt from K, V (and S0, z0, g) inside the
+ * call; nothing from the forward call is kept.  With num = S_c^T R phi(q),
+ * den = phi(q) . z_c + eps: dq = [q > 0] (R^T S_c dnum + dden z_c) with
+ * dnum = dO / den, dden = -(dO . O) / den; G_c = sum over block c of
+ * (R phi(q)) dnum^T + g_{c+1} G_{c+1} (H_c likewise with dden phi(q)) is the
+ * gradient reaching S_c; dv = G_c^T R phi(k), dk = [k > 0] (R^T G_c v + H_c);
+ * dg_c = <G_c, S_{c-1}> + <H_c, z_{c-1}>.  The derivative of phi at 0 is 0, and
+ * a token whose denominator is 0 passes no gradient.  Arithmetic is fp32
+ * throughout (the gradients are rounded once, to the output dtype).
+ * dt: SVLA_F32 or SVLA_BF16 (SVLA_FP8: SVLA_ERR_UNSUPPORTED); d: 32 or 64
+ * (128: SVLA_ERR_UNSUPPORTED).  dQ, dK, dV must not overlap each other or the
+ * inputs (SVLA_ERR_VALUE).  Workspace: svla_workspace_size(SVLA_OP_BACKWARD).
+ * Launches: state build, export scan, query side, reverse scan, key side. */
+svla_status svla_block_causal_backward(svla_dtype dt, int B, int H, int nb, int n, int d,
+                                       const void *Q, const void *K, const void *V,
+                                       const void *dO, const float *S0, const float *z0,
+                                       const float *g, const svla_rope *rope, float eps,
+                                       void *dQ, void *dK, void *dV, float *dg,
+                                       float *dS0, float *dz0, void *ws, size_t ws_bytes,
+                                       svla_stream stream);
+
 /* ---- instrumentation ----------------------------------------------------------- */
 
 /* For benchmarks that time each kernel with HIP events.  While set, every
  * kernel that a call made by this thread launches for slot k (0 = state
  * build, 1 = scan, 2 = apply, 3 = one-launch block step, 4 = temporal
- * convolution) is launched with the start/stop pair
+ * convolution, 5 / 6 / 7 = the backward's query side / reverse scan / key side) is launched with the start/stop pair
  * events[2k], events[2k+1], which the runtime records around that kernel's
  * execution (a kernel a call does not need is not launched and leaves its
  * pair alone; pairs past n are not used).  `events` are hipEvent_t handles

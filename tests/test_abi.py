@@ -227,3 +227,48 @@ def test_fp8_is_d32_only(lib):
     assert st == 5 and b"fp8" in lib.svla_last_error()
     st, n = _ws(lib, _lib.OP_BLOCK_CAUSAL, _lib.SVLA_FP8, 1, 70, 7, 2640, 32)
     assert st == 0 and n > 0
+
+
+def _bwd(lib, **kw):
+    a = dict(dt=_lib.SVLA_BF16, B=1, H=2, nb=2, n=64, d=32, Q=A, K=A, V=A, dO=A,
+             S0=None, z0=None, g=None, rope=None, eps=1e-6,
+             dQ=ctypes.c_void_p(1 << 30), dK=ctypes.c_void_p(2 << 30), dV=ctypes.c_void_p(3 << 30),
+             dg=None, dS0=None, dz0=None, ws=ctypes.c_void_p(4 << 30), wsb=1 << 30)
+    a.update(kw)
+    return lib.svla_block_causal_backward(
+        a["dt"], a["B"], a["H"], a["nb"], a["n"], a["d"], a["Q"], a["K"], a["V"], a["dO"],
+        a["S0"], a["z0"], a["g"], a["rope"], a["eps"], a["dQ"], a["dK"], a["dV"], a["dg"],
+        a["dS0"], a["dz0"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), 1),
+    (dict(dV=None), 1),
+    (dict(ws=None), 1),
+    (dict(S0=A), 1),                      # S0 without z0
+    (dict(dS0=A), 1),                     # dS0 without dz0
+    (dict(n=-1), 2),
+    (dict(dt=_lib.SVLA_FP8), 5),          # no backward for fp8 inputs
+    (dict(d=128), 5),
+    (dict(d=48), 5),
+    (dict(dQ=MIS), 4),
+    (dict(dg=MIS), 4),
+    (dict(wsb=64), 6),
+    (dict(eps=-1.0), 7),
+    (dict(dQ=A), 7),                      # dQ overlapping the inputs
+    (dict(dK=ctypes.c_void_p((1 << 30) + 64)), 7),   # dK overlapping dQ
+])
+def test_backward_rejects(lib, kw, status):
+    assert _bwd(lib, **kw) == status, lib.svla_last_error()
+
+
+def test_backward_empty_and_workspace(lib):
+    assert _bwd(lib, B=0, Q=None, K=None, V=None, dO=None, dQ=None, dK=None, dV=None,
+                ws=None) == 0
+    st, n = _ws(lib, _lib.OP_BACKWARD, _lib.SVLA_BF16, 1, 70, 7, 2640, 32)
+    assert st == 0
+    # at least the rebuilt prefix states, the query partials and G, H
+    assert n >= 70 * 7 * (32 * 32 + 32) * 4 * 3
+    assert _bwd(lib, B=1, H=70, nb=7, n=2640, wsb=n - 1) == 6
+    st, _ = _ws(lib, _lib.OP_BACKWARD, _lib.SVLA_BF16, 1, 20, 8, 1760, 128)
+    assert st == 5

@@ -76,3 +76,20 @@ def test_right_shapes_reach_the_device_check():
     with pytest.raises(ValueError, match="GPU"):
         svla.block_step(Q, K, V, torch.zeros(B, H, d, d), torch.zeros(B, H, d),
                         g=torch.zeros(B, H))
+
+
+@pytest.mark.parametrize("kw,name", [
+    (dict(dO=torch.zeros(B, H, N + 1, d, dtype=torch.bfloat16)), "dO"),
+    (dict(g=torch.zeros(B, H)), "g"),
+    (dict(S0=torch.zeros(B, H, d, d), z0=torch.zeros(B, H)), "z0"),
+    (dict(z0=torch.zeros(B, H, d)), "S0 and z0"),
+])
+def test_backward_shapes(kw, name):
+    args = dict(dO=torch.zeros(B, H, N, d, dtype=torch.bfloat16))
+    args.update(kw)
+    dO = args.pop("dO")
+    _raises(name, svla.block_causal_backward, *qkv(), dO, nb, **args)
+
+
+def test_backward_block_count():
+    _raises("multiple", svla.block_causal_backward, *qkv(), qkv()[0], 3)

@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "ConvConfig", "CONV_CONFIGS", "make_conv_inputs",
     "Rope", "Config", "CONFIGS", "get_config", "bf16_round", "bf16_bits", "fp8_bits",
-    "fp8_from_bits", "fp8_round",
+    "fp8_from_bits", "fp8_round", "make_grad_output",
     "bf16_from_bits", "make_inputs", "scaled_config",
 ]
 
@@ -204,6 +204,15 @@ def make_inputs(cfg: Config, seed: Optional[int] = None, *, B=None, H=None,
             out[name] = x
     out["g"] = _gate(rng, (B, H, nb)) if cfg.gated else None
     return out
+
+
+def make_grad_output(x: dict, seed: int) -> np.ndarray:
+    """dO for a backward case of the inputs ``x`` (from ``make_inputs``):
+    standard normal [B,H,N,d] float32 from its own generator (seed ``seed``),
+    rounded to the inputs' storage type as Q, K and V are."""
+    rng = np.random.default_rng(seed)
+    dO = rng.standard_normal((x["B"], x["H"], x["N"], x["d"]), dtype=np.float32)
+    return bf16_round(dO) if x["dtype"] == "bf16" else dO
 
 
 def step_slice(x: np.ndarray, step: int, n: int) -> np.ndarray:
