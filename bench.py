@@ -53,7 +53,10 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 GATE_FRAC = 0.60                # the minute-long and 720p shapes' target fraction of peak HBM
 SOURCE = os.path.join(ROOT, "block_causal_linear_relu_amd", "csrc", "svla.hip")
-KERNEL_SLOTS = {"build": (0, 1), "scan": (2, 3), "apply": (4, 5), "step": (6, 7), "conv": (8, 9)}
+KERNEL_SLOTS = {"build": (0, 1), "scan": (2, 3), "apply": (4, 5), "step": (6, 7), "conv": (8, 9),
+                "bwd_query": (10, 11), "bwd_scan": (12, 13), "bwd_key": (14, 15)}
+BWD_METRIC = "block-causal linear-attn backward tokens·heads/s + achieved TFLOP/s vs MI355X fp32 MFMA peak"
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
 CONV_METRIC = "causal temporal conv frames·positions·channels/s + achieved HBM GB/s vs MI355X peak"
 CONV_UNIT = "frames·positions·channels/s"
 COPY_BYTES = 1 << 29            # 512 MiB read + 512 MiB written
@@ -77,6 +80,8 @@ def parse():
     ap.add_argument("--c4-mode", default="both", choices=["both", "stream", "oneshot"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp8"],
                     help="input type of Q, K, V (fp8: OCP E4M3, d = 32 workloads; O stays bf16)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (block-causal training) of the workload")
     ap.add_argument("--inplace", action="store_true",
                     help="streaming: commit the state in place (the two-kernel step)")
     ap.add_argument("--rotate", type=int, default=4)
@@ -344,6 +349,129 @@ class ConvWorkload:
                 "mode": ("%d block steps per step (one HIP graph per pass), the cache in two "
                          "buffers" % c.nb) if c.streaming else "one call over all %d blocks" % c.nb,
                 "rotating_input_sets": len(self.sets)}
+
+
+class BackwardWorkload:
+    """The backward pass of one block-causal call over the whole workload:
+    Q, K, V, dO in, dQ, dK, dV (and, gated, dg) out; R rotating sets."""
+
+    def __init__(self, name: str, rotate: int, x=None):
+        import torch
+        import block_causal_linear_relu_amd as svla
+        from workloads import CONFIGS, make_grad_output, make_inputs
+
+        self.torch, self.svla = torch, svla
+        self.cfg = cfg = CONFIGS[name]
+        self.name, self.mode, self.stream_mode = name, "backward", False
+        self.x = x = make_inputs(cfg) if x is None else x
+        self.dO = dO = make_grad_output(x, 1000 + cfg.seed)
+        dev = torch.device("cuda:0")
+        t = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+        base = [t(x["Q"]), t(x["K"]), t(x["V"]), t(dO)]
+        self.g = None if x["g"] is None else torch.from_numpy(x["g"]).to(dev)
+        B, H, N, d = base[0].shape
+        self.B, self.H, self.N, self.d, self.nb, self.n = B, H, N, d, cfg.nb, cfg.n
+        self.sets = []
+        for r in range(rotate):
+            ins = base if r == 0 else [a.clone() for a in base]
+            outs = {k: torch.empty_like(base[0]) for k in ("dQ", "dK", "dV")}
+            if self.g is not None:
+                outs["dg"] = torch.empty((B, H, cfg.nb), dtype=torch.float32, device=dev)
+            self.sets.append((ins, outs))
+        self.ws = torch.empty(svla.workspace_size("backward", torch.bfloat16, B, H, cfg.nb, cfg.n, d),
+                              dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    @property
+    def tokens_heads(self) -> int:
+        return self.B * self.H * self.N
+
+    def launches_per_step(self) -> int:
+        return 1
+
+    def algorithmic(self) -> dict:
+        """Per launch of each kernel: HBM bytes the method must move and
+        matrix flops (multiply-adds x 2) it must do.  Rebuild: K, V read,
+        d^2 products per token.  Query side: Q, dO read, dQ written; three d x d
+        products per token (S^T p~, S dnum, p~ dnum^T).  Key side: K, V read,
+        dK, dV written; two (G^T a~, G v).  The scans: the d x d states only."""
+        t = self.B * self.H * self.N * self.d * 2
+        fl = 2 * self.B * self.H * self.N * self.d * self.d
+        return {"bytes": {"build": 2 * t, "bwd_query": 3 * t, "bwd_key": 4 * t, "scan": 0, "bwd_scan": 0},
+                "flops": {"build": fl, "bwd_query": 3 * fl, "bwd_key": 2 * fl, "scan": 0, "bwd_scan": 0},
+                "path_bytes": 9 * t, "path_flops": 6 * fl}
+
+    def block_step(self, r: int, s: int):
+        self.step(r)
+
+    def step(self, i: int):
+        ins, outs = self.sets[i % len(self.sets)]
+        q, k, v, dO = ins
+        self.svla.block_causal_backward(q, k, v, dO, self.nb, g=self.g, rope=self.cfg.rope,
+                                        eps=self.cfg.eps, workspace=self.ws, out=outs)
+
+    def describe(self) -> dict:
+        c = self.cfg
+        return {"workload": "%s backward: %s" % (c.name, c.description), "B": c.B, "H": c.H,
+                "N": c.N, "d": c.d, "blocks": c.nb, "block_tokens": c.n, "input_dtype": c.dtype,
+                "rope": c.rope is not None, "gated": c.gated,
+                "mode": "one backward call over all %d blocks (state rebuild, query side, reverse "
+                        "scan, key side)" % c.nb, "rotating_input_sets": len(self.sets)}
+
+
+def backward_cpu_baseline(w: BackwardWorkload, budget_s: float = 10.0) -> dict:
+    """The numpy fp64 backward oracle on the host, head by head over the
+    workload's heads until about `budget_s` seconds have passed."""
+    from oracle.backward import backward
+    x = w.x
+    heads, secs = 0, 0.0
+    while secs < budget_s and heads < w.B * w.H:
+        b, h = divmod(heads, w.H)
+        sl = lambda a: None if a is None else a[b:b + 1, h:h + 1]
+        t = time.perf_counter()
+        backward(sl(x["Q"]), sl(x["K"]), sl(x["V"]), w.nb, sl(w.dO), g=sl(x["g"]), rope=w.cfg.rope,
+                 eps=x["eps"])
+        secs += time.perf_counter() - t
+        heads += 1
+    return {"value": heads * w.N / secs, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": "%d of %d (batch, head) slices of %s backward (numpy fp64), %.1f s"
+                      % (heads, w.B * w.H, w.name, secs)}
+
+
+def measure_backward(w: BackwardWorkload, args, settle_s: float) -> dict:
+    settled = settle(w, settle_s) if settle_s > 0 else 0
+    t = time_steps(w, args.steps, args.warmup)
+    kern = time_kernels(w, max(5, min(args.steps, 50)))
+    kern = {k: v for k, v in kern.items() if k in ("build", "scan", "bwd_query", "bwd_scan", "bwd_key")}
+    al = w.algorithmic()
+    per = {}
+    for k in ("bwd_query", "bwd_key", "build"):
+        dur = kern[k] * 1e-3
+        tf = al["flops"][k] / dur / 1e12
+        gb = al["bytes"][k] / dur / 1e9
+        per[k] = {"avg_launch_ms": kern[k], "TFLOPs": tf, "frac_fp32_mfma": tf / FP32_MFMA_PEAK_TFLOPS,
+                  "GBps": gb, "frac_hbm": gb / HBM_PEAK_GBPS,
+                  "flops_per_launch": al["flops"][k], "bytes_per_launch": al["bytes"][k]}
+    names = {"bwd_query": "svla_bwd_query<%d, 2, %s>", "bwd_key": "svla_bwd_key<%d, 2, %s>"}
+    r = "true" if w.cfg.rope else "false"
+    q = per["bwd_query"]
+    ms = t["mean_ms"]
+    return {
+        "settle_steps": settled, "ms_per_step": ms, "value": w.tokens_heads / (ms * 1e-3),
+        "timing": {k: t[k] for k in ("median_ms", "p10_ms", "p90_ms")},
+        "roofline": {"bound": "mfma", "kernel": "void " + names["bwd_query"] % (w.d, r),
+                     "achieved": q["TFLOPs"], "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": q["frac_fp32_mfma"], "traffic": load_traffic(w.name + "_bwd",
+                                                                          "void " + names["bwd_query"] % (w.d, r)),
+                     "algorithmic_flops_per_launch": q["flops_per_launch"],
+                     "avg_launch_ms": q["avg_launch_ms"]},
+        "kernels": per,
+        "path": {"algorithmic_bytes_per_step": al["path_bytes"], "algorithmic_flops_per_step": al["path_flops"],
+                 "achieved_GBps": al["path_bytes"] / (ms * 1e-3) / 1e9,
+                 "achieved_TFLOPs": al["path_flops"] / (ms * 1e-3) / 1e12,
+                 "kernel_ms_per_launch": kern},
+        "mfma": load_mfma(w.name + "_bwd", "void " + names["bwd_query"] % (w.d, r)),
+    }
 
 
 def conv_cpu_baseline(w: ConvWorkload, budget_s: float = 10.0) -> dict:
@@ -677,6 +805,23 @@ def main():
         ceiling()
         return
 
+    if args.backward:
+        if args.config not in ("c3", "c2") or args.dtype != "bf16":
+            print("bench.py: --backward times the bf16 d = 32 training shapes (c3, c2)", file=sys.stderr)
+            sys.exit(2)
+        bw = BackwardWorkload(args.config, args.rotate)
+        m = measure_backward(bw, args, args.settle)
+        line = {"metric": BWD_METRIC, "value": m["value"], "unit": UNIT, "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "settle_steps": m["settle_steps"],
+                "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "bf16 (fp32 arithmetic)",
+                "data": "synthetic (seeded N(0,1) Q, K, V, dO, bf16-rounded)",
+                "config": bw.describe(), "timing": m["timing"], "roofline": m["roofline"],
+                "kernels": m["kernels"], "path": m["path"], "mfma": m["mfma"],
+                "source_sha256": source_hash(),
+                "cpu_baseline": None if args.no_cpu_baseline else backward_cpu_baseline(bw)}
+        print(json.dumps(line), flush=True)
+        return
     if args.config.startswith("t"):
         cw = ConvWorkload(args.config, args.rotate)
         m = measure(cw, args, args.settle)

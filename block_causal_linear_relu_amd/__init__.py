@@ -382,12 +382,12 @@ def apply(Q, S_prefix, z_prefix, nb: int, rope=None, eps: float = 1e-6):
 
 def block_causal_backward(Q, K, V, dO, nb: int, S0=None, z0=None, g=None, rope=None,
                           eps: float = 1e-6, need_dg: bool = False, need_dstate: bool = False,
-                          workspace=None) -> dict:
+                          workspace=None, out: Optional[dict] = None) -> dict:
     """Gradients of ``block_causal`` (same arguments) given dO = dLoss/dO.
 
     Returns {"dQ", "dK", "dV"} in Q's dtype, plus "dg" [B,H,nb] when
     ``need_dg`` and "dS0" [B,H,d,d], "dz0" [B,H,d] when ``need_dstate``
-    (float32)."""
+    (float32).  ``out`` may bring any of these tensors preallocated."""
     B, H, N, d = _qkv_shape(Q, K, V)
     if nb <= 0 or N % nb:
         raise ValueError("N=%d is not a multiple of nb=%d" % (N, nb))
@@ -401,12 +401,20 @@ def block_causal_backward(Q, K, V, dO, nb: int, S0=None, z0=None, g=None, rope=N
     _dev(dO, "dO", Q.dtype)
     S0, z0, g = _opt(S0, "S0"), _opt(z0, "z0"), _opt(g, "g")
     lib = library()
-    out = {name: torch.empty(Q.shape, dtype=Q.dtype, device=Q.device) for name in ("dQ", "dK", "dV")}
-    if need_dg:
-        out["dg"] = torch.empty((B, H, nb), dtype=torch.float32, device=Q.device)
-    if need_dstate:
-        out["dS0"] = torch.empty((B, H, d, d), dtype=torch.float32, device=Q.device)
-        out["dz0"] = torch.empty((B, H, d), dtype=torch.float32, device=Q.device)
+    given = dict(out or {})
+    shapes = {"dQ": tuple(Q.shape), "dK": tuple(Q.shape), "dV": tuple(Q.shape), "dg": (B, H, nb),
+              "dS0": (B, H, d, d), "dz0": (B, H, d)}
+    for k, t in given.items():
+        if k not in shapes:
+            raise ValueError("unknown output %s" % k)
+        _shape(t, shapes[k], k)
+    wanted = ["dQ", "dK", "dV"] + (["dg"] if need_dg or "dg" in given else []) + \
+        (["dS0", "dz0"] if need_dstate or "dS0" in given or "dz0" in given else [])
+    out = {}
+    for k in wanted:
+        dtype = Q.dtype if k in ("dQ", "dK", "dV") else torch.float32
+        out[k] = _dev(given[k], k, dtype) if k in given else \
+            torch.empty(shapes[k], dtype=dtype, device=Q.device)
     ws, nbytes = _ws_arg(workspace, "backward", Q, B, H, nb, n, d)
     rp, _keep = _rope_arg(rope)
     st = lib.svla_block_causal_backward(

@@ -133,6 +133,12 @@
 #ifndef SVLA_FUSED_QG
 #define SVLA_FUSED_QG 2            // ... Q groups of 16 tokens per wave (tile <= 16 * W * QG)
 #endif
+#ifndef SVLA_BWD_HOLD_Q
+#define SVLA_BWD_HOLD_Q 1          // backward query side: state operands in registers (1) or LDS (0)
+#endif
+#ifndef SVLA_BWD_WGS
+#define SVLA_BWD_WGS 2048          // backward query/key kernels: workgroups wanted per launch
+#endif
 // Cache-policy bits of the streaming accesses (gfx950 buffer instructions:
 // bit 1 = nt, non-temporal).  Measured: nt pays for K/V (read once by the
 // state build), for Q (read once by the apply) and not for O.
@@ -2180,7 +2186,6 @@ __global__ void __launch_bounds__(64 * W)
 svla_step_fused(const StepArgs a)
 {
     constexpr int D = 32;
-    constexpr int NT = 64 * W;
     constexpr int ROWB = D * 2;           // 64 bytes per token row
     constexpr int TILEB = 16 * ROWB;      // one 16-token stage of one tensor
     constexpr int NK = ROPE ? 2 : 1;      // K tiles per stage: (rotated) hi, lo
@@ -2613,23 +2618,28 @@ svla_temporal_conv_k(const ConvArgs a)
 // scan): the query side (dq and each split's share of the sums of G and H),
 // the reverse scan over blocks (G_c, H_c, dS0, dz0) and the key side (dk,
 // dv, dg).  All arithmetic is fp32: every product over features or tokens
-// runs on v_mfma_f32_32x32x2f32.
+// runs on v_mfma_f32_16x16x4f32.
 //
-// Lane layout of the per-token work ("J layout"): in a 32-token group of a
-// wave, lane (n = lane % 32, h = lane / 32) owns token n and the features
-// 32 t + 8 u + 4 h + e (t < d/32, u < 4, e < 4), which are exactly the rows
-// that register 4 u + e of accumulator tile t holds for column n when the
-// MFMA's output rows are features and its columns tokens.  A contraction over
-// features can take its k-slots in any order, as long as both operands agree,
-// so the k-slot of lane half h at step (t, x) is feature 32 t + row(x, h): the
-// B operand is then a register the lane already holds (its own p~, dnum, a~
-// or v) and only the state operand is read, from LDS.  Every per-token
-// vector (q, dO, num, dnum, dp~, k, v, dv, da~) lives in this layout, so the
-// element-wise steps, RoPE's pairs (e = 0,1 and 2,3) and the loads and stores
-// (4 consecutive features per lane and chunk) need no data exchange; the two
-// halves of a token meet through one lane swap for each dot product over
-// features.  The sum over tokens of p~ dnum^T goes through a per-wave LDS
-// tile (rows swizzled in 4-float chunks against bank conflicts).
+// Lane layout of the per-token work: the kernels run on
+// v_mfma_f32_16x16x4f32 with the MFMA's output rows as features and its
+// columns as tokens.  In a 16-token group of a wave, lane (n = lane % 16,
+// q = lane / 16) owns token n and the d/4 consecutive features
+// F(q, L) = (d/4) q + L, L < d/4: register i of output tile t is local
+// feature L = 4 t + i.  The state operand picks the feature order: tile t's
+// row m holds feature pi(t, m) = (d/4) (m / 4) + 4 t + m % 4, which is the
+// feature that row lands on in lane group m / 4.  A contraction over features
+// takes its k-slots in any order as long as both operands agree, so at step s
+// the k-slot of lane group q is feature F(q, s): the B operand is then a
+// register the lane already holds (its own p~, dnum, a~ or v) and only the
+// state operand is read.  Every per-token vector (q, dO, num, dnum, dp~, k, v,
+// dv, da~) lives in this layout, so the element-wise steps and RoPE's pairs
+// need no data exchange, and a lane's features are contiguous in memory: one
+// wave instruction of 16-byte accesses covers whole 64-byte rows of 16
+// tokens (bf16, d = 32).  The four lanes of a token meet through two lane
+// swaps for each dot product over features.  The sum over tokens of
+// p~ dnum^T goes through a per-wave LDS tile (rows padded to d + 16 floats,
+// which spreads the four token rows a step reads over the banks, and 4-float
+// chunks swapped per row, which spreads the 16 rows a write touches).
 // ---------------------------------------------------------------------------
 struct BwdArgs {
     const void *Q, *K, *V, *dO;
@@ -2639,7 +2649,7 @@ struct BwdArgs {
     float *G, *Hz;                 // reverse scan: [BH*nb][d*d], [BH*nb][d]
     const float *g, *S0, *z0;      // gate [BH][nb], state entering block 0 (each nullable)
     float *dg, *dS0, *dz0;         // [BH][nb], [BH][d*d], [BH][d] (each nullable)
-    int N, n, nb, splits, chunk;   // splits of a block's tokens, tokens per split (a multiple of 32)
+    int N, n, nb, splits, chunk;   // splits of a block's tokens, tokens per split (a multiple of 16)
     long BH;
     float eps;
     RopeK rope;
@@ -2647,48 +2657,66 @@ struct BwdArgs {
 
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
-// Row of register r of a 32x32 MFMA accumulator, for lane half h.
-__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-
-// 4 consecutive features at byte offset off (bf16 when ES == 2, fp32 when 4),
-// raw; bwd_floats4 turns them into fp32.
-template <int ES>
-struct Raw4 {
-    u32x2_t w2;
-    u32x4_t w4;
+// A lane's d/4 features of one token, as stored (bf16 when ES == 2, fp32 when 4).
+template <int D, int ES>
+struct LaneRaw {
+    static constexpr int NC = D / 4 * ES / 16;     // 16-byte chunks
+    u32x4_t c[NC];
 };
 
-template <int ES>
-__device__ __forceinline__ Raw4<ES> bwd_load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+template <int D, int ES>
+__device__ __forceinline__ void bwd_load(LaneRaw<D, ES> &v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    Raw4<ES> v;
-    if constexpr (ES == 2) v.w2 = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-    else v.w4 = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return v;
-}
-
-template <int ES>
-__device__ __forceinline__ void bwd_floats4(const Raw4<ES> &v, float *f)
-{
-    if constexpr (ES == 2) {
-        f[0] = bf16lo(v.w2[0]); f[1] = bf16hi(v.w2[0]);
-        f[2] = bf16lo(v.w2[1]); f[3] = bf16hi(v.w2[1]);
-    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = as_f32(v.w4[e]);
-    }
+    for (int i = 0; i < LaneRaw<D, ES>::NC; ++i)
+        v.c[i] = load16(r, off == kOOB ? kOOB : off + 16u * i);
 }
 
-template <int ES>
-__device__ __forceinline__ void bwd_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *f)
+template <int D, int ES>
+__device__ __forceinline__ void bwd_floats(const LaneRaw<D, ES> &v, float *f)
 {
-    if constexpr (ES == 2) {
-        const u32x2_t w = {pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, 0);
-    } else {
-        const u32x4_t w = {as_u32(f[0]), as_u32(f[1]), as_u32(f[2]), as_u32(f[3])};
-        store16(r, off, w);
-    }
+#pragma unroll
+    for (int i = 0; i < LaneRaw<D, ES>::NC; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (ES == 2) {
+                f[8 * i + 2 * e] = bf16lo(v.c[i][e]);
+                f[8 * i + 2 * e + 1] = bf16hi(v.c[i][e]);
+            } else {
+                f[4 * i + e] = as_f32(v.c[i][e]);
+            }
+        }
+}
+
+template <int D, int ES>
+__device__ __forceinline__ void bwd_pack(LaneRaw<D, ES> &v, const float *f)
+{
+#pragma unroll
+    for (int i = 0; i < LaneRaw<D, ES>::NC; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (ES == 2) v.c[i][e] = pack_bf16(f[8 * i + 2 * e], f[8 * i + 2 * e + 1]);
+            else v.c[i][e] = as_u32(f[4 * i + e]);
+        }
+}
+
+// Stores are not ordered with loads in the wait counter, so a wait for a load
+// also waits for every store issued before it.  The kernels therefore hold a
+// group's results and store them one group later, just before the next loads
+// go out: by the time those loads are waited for, the stores have had a whole
+// group's work to complete.
+template <int D, int ES>
+struct Pending {
+    LaneRaw<D, ES> v;
+    uint32_t off = kOOB;        // byte offset of the lane's features; kOOB: nothing pending
+};
+
+template <int D, int ES>
+__device__ __forceinline__ void bwd_flush(__amdgpu_buffer_rsrc_t r, const Pending<D, ES> &p)
+{
+#pragma unroll
+    for (int i = 0; i < LaneRaw<D, ES>::NC; ++i)
+        store16(r, p.off == kOOB ? kOOB : p.off + 16u * i, p.v.c[i]);
 }
 
 // x <- R^T x for the pairs (x[2j], x[2j+1]) of a token at `pos` (the inverse
@@ -2707,16 +2735,6 @@ __device__ __forceinline__ void rope_rotate_t(float *x, const RopePos &pos,
     }
 }
 
-// Column swizzle of the per-wave token tiles (rows of d floats): 4-float
-// chunks are permuted inside each 32-float (d = 32) or 64-float (d = 64) row
-// segment, so the 16-byte writes of one row chunk by 32 tokens and the reads
-// of one row by 32 lanes both spread over the 64 banks.
-template <int D>
-__device__ __forceinline__ int bwd_swz(int t)
-{
-    return D == 32 ? 4 * ((t >> 1) & 7) : 4 * (t & 15);
-}
-
 // The state (S_c or G_c) of one block into LDS twice: M[k][j] row-major and
 // its transpose Mt[j][k] (rows of d floats), and the vector (z_c or H_c).
 template <int D>
@@ -2733,21 +2751,71 @@ __device__ __forceinline__ void bwd_state_to_lds(const float *S, const float *z,
     if (threadIdx.x < D) vec[threadIdx.x] = z[threadIdx.x];
 }
 
-// Query side.  Workgroup = (bh, block c, split s); wave w takes the 32-token
+// Feature held by row m of output tile t (see the lane layout above).
+template <int D>
+__device__ __forceinline__ int bwd_pi(int t, int m) { return D / 4 * (m >> 2) + 4 * t + (m & 3); }
+
+// The state operands of the two feature contractions, for lane (m, q):
+// fwd[t][s] = M[F(q, s)][pi(t, m)] (output rows pi, k-slots F) and
+// bwd[t][s] = M[pi(t, m)][F(q, s)] = Mt[F(q, s)][pi(t, m)].  With HOLD (d = 32
+// only) they are read once per workgroup into registers, otherwise from LDS
+// per instruction (fewer registers, more waves per SIMD).
+template <int D, bool HOLD>
+struct StateOps {
+    static constexpr bool REG = HOLD && D == 32;
+    float fwd[REG ? D / 16 : 1][REG ? D / 4 : 1], bwd[REG ? D / 16 : 1][REG ? D / 4 : 1];
+    const float *M, *Mt;
+    int q, m;
+    __device__ __forceinline__ void init(const float *M_, const float *Mt_, int q_, int m_)
+    {
+        M = M_; Mt = Mt_; q = q_; m = m_;
+        if constexpr (REG) {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+                for (int s = 0; s < D / 4; ++s) {
+                    fwd[t][s] = M[(D / 4 * q + s) * D + bwd_pi<D>(t, m)];
+                    bwd[t][s] = Mt[(D / 4 * q + s) * D + bwd_pi<D>(t, m)];
+                }
+        }
+    }
+    __device__ __forceinline__ float f(int t, int s) const
+    {
+        if constexpr (REG) return fwd[t][s];
+        else return M[(D / 4 * q + s) * D + bwd_pi<D>(t, m)];
+    }
+    __device__ __forceinline__ float b(int t, int s) const
+    {
+        if constexpr (REG) return bwd[t][s];
+        else return Mt[(D / 4 * q + s) * D + bwd_pi<D>(t, m)];
+    }
+};
+
+// Sum of x over the four lanes (q = 0..3) of a token.
+__device__ __forceinline__ float token_sum(float x)
+{
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+// Query side.  Workgroup = (bh, block c, split s); wave w takes the 16-token
 // groups w, w + 4, ... of the split and keeps the next group's loads in
-// flight.  Per group: num^T = S_c^T p~^T (MFMA), den, O, dnum, dden,
-// dp~^T = S_c dnum^T (MFMA), dq = [q > 0] (R^T dp~ + dden z_c) stored, and
-// p~^T dnum accumulated over the wave's tokens (MFMA over the LDS tile);
-// dden p is summed per lane.  At the end the four waves' sums are added
-// through LDS and written as split s's partial of block c.
+// flight while it works on one.  Per group: num^T = S_c^T p~^T (MFMA), den,
+// O, dnum, dden, dp~^T = S_c dnum^T (MFMA), dq = [q > 0] (R^T dp~ + dden z_c)
+// stored one group later, and p~^T dnum accumulated over the wave's tokens
+// (MFMA over the LDS tile); dden p is summed per lane.  At the end the four
+// waves' sums are added through LDS and written as split s's partial of
+// block c.
 template <int D, int ES, bool ROPE>
 __global__ void __launch_bounds__(kThreads)
 svla_bwd_query(const BwdArgs a)
 {
-    constexpr int T = D / 32;               // 32-row tiles per side
+    constexpr int T = D / 16;               // 16-row output tiles
+    constexpr int FPL = D / 4;              // features per lane
+    constexpr int LD = D + 16;              // LDS tile row (floats)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int m = lane & 31, h = lane >> 5;
+    const int m = lane & 15, q = lane >> 4;
     const unsigned per_bh = (unsigned)(a.splits * a.nb);
     const long bh = blockIdx.x / per_bh;
     const int rest = (int)(blockIdx.x - bh * per_bh);
@@ -2761,196 +2829,139 @@ svla_bwd_query(const BwdArgs a)
     float *St = Ss + D * D;
     float *zs = St + D * D;
     float *work = zs + 64;
-    float *Pt = work + wave * 2 * 32 * D, *Dn = Pt + 32 * D;
+    float *Pt = work + wave * 2 * 16 * LD, *Dn = Pt + 16 * LD;
 
     const uint32_t slice = (uint32_t)a.N * D * ES;
     const auto rQ = make_rsrc((const char *)a.Q + bh * slice, slice);
     const auto rO = make_rsrc((const char *)a.dO + bh * slice, slice);
     const auto rdQ = make_rsrc((char *)a.dQ + bh * slice, slice);
 
-    const int ngroups = (tok_hi - tok_lo + 31) / 32;
-    auto row_off = [&](int grp) -> uint32_t {
-        const int tok = tok_lo + grp * 32 + m;
-        return grp < ngroups && tok < tok_hi ? (uint32_t)tok * (D * ES) : kOOB;
+    const int ngroups = (tok_hi - tok_lo + 15) / 16;
+    // byte offset of the lane's features in group grp (kOOB past the split)
+    auto lane_off = [&](int grp) -> uint32_t {
+        const int tok = tok_lo + grp * 16 + m;
+        return grp < ngroups && tok < tok_hi ? (uint32_t)(tok * D + FPL * q) * ES : kOOB;
     };
-    // first group's loads go out before the state and table are set up
-    Raw4<ES> qr[T][4], orw[T][4];
+    // the first group's loads go out before the state and table are set up
+    LaneRaw<D, ES> qr, orw;
     int grp = wave;
-    {
-        const uint32_t ro = row_off(grp);
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t off = ro == kOOB ? kOOB : ro + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
-                qr[t][u] = bwd_load4<ES>(rQ, off);
-                orw[t][u] = bwd_load4<ES>(rO, off);
-            }
-    }
+    bwd_load<D, ES>(qr, rQ, lane_off(grp));
+    bwd_load<D, ES>(orw, rO, lane_off(grp));
     bwd_state_to_lds<D>(a.S_pre + unit * D * D, a.z_pre + unit * D, Ss, St, zs);
     uint32_t frame_lo = 0;
-    RopePairs<2> pp[T][4];
+    RopePairs<FPL / 2> pp;
     if constexpr (ROPE) {
         frame_lo = fdiv((uint32_t)tok_lo, a.rope.div_hw);
         const uint32_t frame_hi = fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw);
         const int nf = (int)(frame_hi - frame_lo) + 1;
         rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) pp[t][u] = rope_pairs<2>(a.rope, 32 * t + 8 * u + 4 * h, nf);
+        pp = rope_pairs<FPL / 2>(a.rope, FPL * q, nf);
     }
     __syncthreads();
+    StateOps<D, SVLA_BWD_HOLD_Q> so;
+    so.init(Ss, St, q, m);
+    float zr[FPL];
+#pragma unroll
+    for (int L = 0; L < FPL; ++L) zr[L] = zs[FPL * q + L];
 
-    f32x16_t dS[T][T];
+    f32x4_t dS[T][T];
 #pragma unroll
     for (int i = 0; i < T; ++i)
 #pragma unroll
-        for (int j = 0; j < T; ++j)
+        for (int j = 0; j < T; ++j) dS[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float dz[FPL];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dS[i][j][r] = 0.f;
-    float dz[T][16];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dz[t][r] = 0.f;
-    float zr[T][16];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) zr[t][r] = zs[32 * t + acc_row(r, h)];
+    for (int L = 0; L < FPL; ++L) dz[L] = 0.f;
 
+    Pending<D, ES> pq;
     for (; grp < ngroups; grp += 4) {
-        const uint32_t ro = row_off(grp);
-        float q[T][16], p[T][16], pt[T][16], dO[T][16];
+        const uint32_t off = lane_off(grp);
+        float p[FPL], dO[FPL];
+        bwd_floats<D, ES>(qr, p);
+        bwd_floats<D, ES>(orw, dO);
+        bwd_flush<D, ES>(rdQ, pq);              // the previous group's dq
+        bwd_load<D, ES>(qr, rQ, lane_off(grp + 4));
+        bwd_load<D, ES>(orw, rO, lane_off(grp + 4));
+        // keep those loads here, ahead of this group's work (the scheduler
+        // would otherwise sink them to the end of the loop body)
+        __builtin_amdgcn_sched_barrier(0);
+        float denp = 0.f, pt[FPL];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                bwd_floats4<ES>(qr[t][u], &q[t][4 * u]);
-                bwd_floats4<ES>(orw[t][u], &dO[t][4 * u]);
-            }
-        // the next group's loads
-        {
-            const uint32_t rn = row_off(grp + 4);
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t off = rn == kOOB ? kOOB : rn + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
-                    qr[t][u] = bwd_load4<ES>(rQ, off);
-                    orw[t][u] = bwd_load4<ES>(rO, off);
-                }
+        for (int L = 0; L < FPL; ++L) {
+            p[L] = fmaxf(p[L], 0.f);               // p > 0 exactly where q > 0
+            denp += p[L] * zr[L];
+            pt[L] = p[L];
         }
-        float denp = 0.f;
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[t][r] = fmaxf(q[t][r], 0.f);
-                pt[t][r] = p[t][r];
-                denp += p[t][r] * zr[t][r];
-            }
         RopePos pos{0, 0, 0};
         if constexpr (ROPE) {
-            const int tok = min(tok_lo + grp * 32 + m, tok_hi - 1);
-            pos = rope_pos((uint32_t)tok, frame_lo, a.rope);
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) rope_rotate<2>(&pt[t][4 * u], pos, pp[t][u], tab);
+            pos = rope_pos((uint32_t)min(tok_lo + grp * 16 + m, tok_hi - 1), frame_lo, a.rope);
+            rope_rotate<FPL / 2>(pt, pos, pp, tab);
         }
         // num^T = S^T p~^T
-        f32x16_t num[T];
+        f32x4_t num[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int t = 0; t < T; ++t) num[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) num[t][r] = 0.f;
+        for (int st = 0; st < FPL; ++st)
 #pragma unroll
-        for (int tk = 0; tk < T; ++tk)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const float *row = Ss + (32 * tk + acc_row(x, h)) * D + m;
-#pragma unroll
-                for (int to = 0; to < T; ++to)
-                    num[to] = __builtin_amdgcn_mfma_f32_32x32x2f32(row[32 * to], pt[tk][x], num[to], 0, 0, 0);
-            }
-        const float den = denp + __shfl_xor(denp, 32) + a.eps;
+            for (int t = 0; t < T; ++t)
+                num[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(so.f(t, st), pt[st], num[t], 0, 0, 0);
+        const float den = token_sum(denp) + a.eps;
         const float inv = den != 0.f ? 1.f / den : 0.f;
         float dotp = 0.f;
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int L = 0; L < FPL; ++L) dotp += dO[L] * (num[L / 4][L % 4] * inv);
+        const float dden = -token_sum(dotp) * inv;
+        float dn[FPL];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dotp += dO[t][r] * (num[t][r] * inv);
-        const float dden = -(dotp + __shfl_xor(dotp, 32)) * inv;
-        float dn[T][16];
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dn[t][r] = dO[t][r] * inv;
+        for (int L = 0; L < FPL; ++L) dn[L] = dO[L] * inv;
         // dp~^T = S dnum^T
-        f32x16_t dpt[T];
+        f32x4_t dpt[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int t = 0; t < T; ++t) dpt[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dpt[t][r] = 0.f;
+        for (int st = 0; st < FPL; ++st)
 #pragma unroll
-        for (int tj = 0; tj < T; ++tj)
+            for (int t = 0; t < T; ++t)
+                dpt[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(so.b(t, st), dn[st], dpt[t], 0, 0, 0);
+        // the wave's token tile for p~^T dnum (4-float chunks of row r swapped
+        // within their 16-float group by 4 ((r / 4) % 4): the 16 rows one
+        // write instruction touches then cover all 64 banks)
+        const int swm = 4 * ((m >> 2) & 3);
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const float *row = St + (32 * tj + acc_row(x, h)) * D + m;
+        for (int L = 0; L < FPL; L += 4) {
+            *(f32x4_t *)(Pt + m * LD + ((FPL * q + L) ^ swm)) = (f32x4_t){pt[L], pt[L + 1], pt[L + 2], pt[L + 3]};
+            *(f32x4_t *)(Dn + m * LD + ((FPL * q + L) ^ swm)) = (f32x4_t){dn[L], dn[L + 1], dn[L + 2], dn[L + 3]};
+        }
+        // dq = [q > 0] (R^T dp~ + dden z), held until the next group; dz += dden p
+        float v[FPL];
 #pragma unroll
-                for (int to = 0; to < T; ++to)
-                    dpt[to] = __builtin_amdgcn_mfma_f32_32x32x2f32(row[32 * to], dn[tj][x], dpt[to], 0, 0, 0);
-            }
-        // dq = [q > 0] (R^T dp~ + dden z)
+        for (int L = 0; L < FPL; ++L) v[L] = dpt[L / 4][L % 4];
+        if constexpr (ROPE) rope_rotate_t<FPL / 2>(v, pos, pp, tab);
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int L = 0; L < FPL; ++L) {
+            v[L] = p[L] > 0.f ? v[L] + dden * zr[L] : 0.f;
+            dz[L] += dden * p[L];
+        }
+        bwd_pack<D, ES>(pq.v, v);
+        pq.off = off;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = dpt[t][4 * u + e];
-                if constexpr (ROPE) rope_rotate_t<2>(v, pos, pp[t][u], tab);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * u + e;
-                    v[e] = q[t][r] > 0.f ? v[e] + dden * zr[t][r] : 0.f;
-                }
-                bwd_store4<ES>(rdQ, ro == kOOB ? kOOB : ro + (uint32_t)((32 * t + 8 * u + 4 * h) * ES), v);
-            }
-        // the sums over tokens: dz per lane, p~^T dnum through the wave's tile
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dz[t][r] += dden * p[t][r];
-        const int sw = bwd_swz<D>(m);
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int col = (32 * t + 8 * u + 4 * h) ^ sw;
-                *(f32x4_t *)(Pt + m * D + col) =
-                    (f32x4_t){pt[t][4 * u], pt[t][4 * u + 1], pt[t][4 * u + 2], pt[t][4 * u + 3]};
-                *(f32x4_t *)(Dn + m * D + col) =
-                    (f32x4_t){dn[t][4 * u], dn[t][4 * u + 1], dn[t][4 * u + 2], dn[t][4 * u + 3]};
-            }
-#pragma unroll
-        for (int pi = 0; pi < 16; ++pi) {
-            const int tt = 2 * pi + h, swr = bwd_swz<D>(tt);
+        for (int st = 0; st < 4; ++st) {
+            const int tt = 4 * st + q, swr = 4 * (st & 3);     // the swap of row tt
             float av[T], bv[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                av[t] = Pt[tt * D + ((32 * t + m) ^ swr)];
-                bv[t] = Dn[tt * D + ((32 * t + m) ^ swr)];
+                av[t] = Pt[tt * LD + ((16 * t + m) ^ swr)];
+                bv[t] = Dn[tt * LD + ((16 * t + m) ^ swr)];
             }
 #pragma unroll
             for (int i = 0; i < T; ++i)
 #pragma unroll
                 for (int j = 0; j < T; ++j)
-                    dS[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i], bv[j], dS[i][j], 0, 0, 0);
+                    dS[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], dS[i][j], 0, 0, 0);
         }
     }
+    bwd_flush<D, ES>(rdQ, pq);
     // this split's partials: the four waves' p~^T dnum tiles, then dden p
     __syncthreads();
     float *red = work;
@@ -2959,41 +2970,39 @@ svla_bwd_query(const BwdArgs a)
 #pragma unroll
         for (int j = 0; j < T; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[((wave * T * T + i * T + j) * 16 + r) * 64 + lane] = dS[i][j][r];
+            for (int r = 0; r < 4; ++r) red[((wave * T * T + i * T + j) * 4 + r) * 64 + lane] = dS[i][j][r];
     __syncthreads();
     const auto rS = make_rsrc(a.dS_part + (unit * a.splits + s) * D * D, D * D * 4);
     for (int e = tid * 4; e < D * D; e += kThreads * 4) {
         const int k = e / D, j0 = e % D;
-        const int tile = (k / 32) * T + j0 / 32;
-        const int r = 4 * ((k % 32) / 8) + k % 4, hh = (k % 8) / 4;
+        const int tile = (k / 16) * T + j0 / 16;
+        const int r = k % 4, qq = (k % 16) / 4;
         u32x4_t o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int ln = (j0 + i) % 32 + 32 * hh;
+            const int ln = (j0 + i) % 16 + 16 * qq;
             float v = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) v += red[((w * T * T + tile) * 16 + r) * 64 + ln];
+            for (int w = 0; w < 4; ++w) v += red[((w * T * T + tile) * 4 + r) * 64 + ln];
             o[i] = as_u32(v);
         }
         store16(rS, (uint32_t)e * 4u, o);
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[(wave * 64 + lane) * (16 * T) + 16 * t + r] = dz[t][r];
+    for (int L = 0; L < FPL; ++L) red[(wave * 64 + lane) * FPL + L] = dz[L];
     __syncthreads();
-    // feature f sits in register (t, r) of the lanes of half hh; 256 / D
-    // threads per feature each add a share of the 4 x 32 lanes, then one adds those
-    float *red2 = red + 4 * 64 * 16 * T;
+    // feature f = FPL qq + L sits in register L of the lanes of group qq;
+    // 256 / D threads per feature each add a share of the 4 x 16 lanes, then one adds those
+    float *red2 = red + 4 * 64 * FPL;
     {
         constexpr int PARTS = kThreads / D;
         const int f = tid % D, part = tid / D;
-        const int t = f / 32, r = 4 * ((f % 32) / 8) + f % 4, hh = (f % 8) / 4;
+        const int qq = f / FPL, L = f % FPL;
         float v = 0.f;
-        for (int i = part; i < 128; i += PARTS) {
-            const int w = i / 32, ln = i % 32 + 32 * hh;
-            v += red[(w * 64 + ln) * (16 * T) + 16 * t + r];
+        for (int i = part; i < 64; i += PARTS) {
+            const int w = i / 16, ln = i % 16 + 16 * qq;
+            v += red[(w * 64 + ln) * FPL + L];
         }
         red2[part * D + f] = v;
     }
@@ -3062,16 +3071,18 @@ svla_bwd_scan(const BwdArgs a)
 }
 
 // Key side.  Workgroup = (bh, block c, split s): G_c, H_c in LDS; per
-// 32-token group dv^T = G^T a~^T and da~^T = G v^T (MFMA), dk = [k > 0]
-// (R^T da~ + H).  Split 0 also forms dg_c = <G_c, S_{c-1}> + <H_c, z_{c-1}>.
+// 16-token group dv^T = G^T a~^T and da~^T = G v^T (MFMA), dk = [k > 0]
+// (R^T da~ + H), stored one group later.  Split 0 also forms
+// dg_c = <G_c, S_{c-1}> + <H_c, z_{c-1}>.
 template <int D, int ES, bool ROPE>
 __global__ void __launch_bounds__(kThreads)
 svla_bwd_key(const BwdArgs a)
 {
-    constexpr int T = D / 32;
+    constexpr int T = D / 16;
+    constexpr int FPL = D / 4;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int m = lane & 31, h = lane >> 5;
+    const int m = lane & 15, q = lane >> 4;
     const unsigned per_bh = (unsigned)(a.splits * a.nb);
     const long bh = blockIdx.x / per_bh;
     const int rest = (int)(blockIdx.x - bh * per_bh);
@@ -3092,36 +3103,24 @@ svla_bwd_key(const BwdArgs a)
     const auto rdK = make_rsrc((char *)a.dK + bh * slice, slice);
     const auto rdV = make_rsrc((char *)a.dV + bh * slice, slice);
 
-    const int ngroups = (tok_hi - tok_lo + 31) / 32;
-    auto row_off = [&](int grp) -> uint32_t {
-        const int tok = tok_lo + grp * 32 + m;
-        return grp < ngroups && tok < tok_hi ? (uint32_t)tok * (D * ES) : kOOB;
+    const int ngroups = (tok_hi - tok_lo + 15) / 16;
+    auto lane_off = [&](int grp) -> uint32_t {
+        const int tok = tok_lo + grp * 16 + m;
+        return grp < ngroups && tok < tok_hi ? (uint32_t)(tok * D + FPL * q) * ES : kOOB;
     };
-    Raw4<ES> kr[T][4], vr[T][4];
+    LaneRaw<D, ES> kr, vr;
     int grp = wave;
-    {
-        const uint32_t ro = row_off(grp);
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t off = ro == kOOB ? kOOB : ro + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
-                kr[t][u] = bwd_load4<ES>(rK, off);
-                vr[t][u] = bwd_load4<ES>(rV, off);
-            }
-    }
+    bwd_load<D, ES>(kr, rK, lane_off(grp));
+    bwd_load<D, ES>(vr, rV, lane_off(grp));
     bwd_state_to_lds<D>(a.G + unit * D * D, a.Hz + unit * D, Gs, Gt, hs);
     uint32_t frame_lo = 0;
-    RopePairs<2> pp[T][4];
+    RopePairs<FPL / 2> pp;
     if constexpr (ROPE) {
         frame_lo = fdiv((uint32_t)tok_lo, a.rope.div_hw);
         const uint32_t frame_hi = fdiv((uint32_t)(tok_hi - 1), a.rope.div_hw);
         const int nf = (int)(frame_hi - frame_lo) + 1;
         rope_fill(tab, a.rope, a.rope.t0 + (int)frame_lo, nf);
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) pp[t][u] = rope_pairs<2>(a.rope, 32 * t + 8 * u + 4 * h, nf);
+        pp = rope_pairs<FPL / 2>(a.rope, FPL * q, nf);
     }
     __syncthreads();
     if (s == 0 && a.dg) {
@@ -3139,85 +3138,61 @@ svla_bwd_key(const BwdArgs a)
         __syncthreads();
         if (tid == 0) a.dg[unit] = red[0] + red[1] + red[2] + red[3];
     }
-    float hr[T][16];
+    // G's operands: dv^T = G^T a~^T reads G[F(q, s)][pi(t, m)] (the forward
+    // form), da~^T = G v^T reads G[pi(t, m)][F(q, s)] (the transposed form)
+    StateOps<D, true> go;
+    go.init(Gs, Gt, q, m);
+    float hr[FPL];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) hr[t][r] = hs[32 * t + acc_row(r, h)];
+    for (int L = 0; L < FPL; ++L) hr[L] = hs[FPL * q + L];
 
+    Pending<D, ES> pv, pk;
     for (; grp < ngroups; grp += 4) {
-        const uint32_t ro = row_off(grp);
-        float k[T][16], at[T][16], v[T][16];
+        const uint32_t off = lane_off(grp);
+        float at[FPL], v[FPL];
+        bwd_floats<D, ES>(kr, at);
+        bwd_floats<D, ES>(vr, v);
+        bwd_flush<D, ES>(rdV, pv);             // the previous group's dv, dk
+        bwd_flush<D, ES>(rdK, pk);
+        bwd_load<D, ES>(kr, rK, lane_off(grp + 4));
+        bwd_load<D, ES>(vr, rV, lane_off(grp + 4));
+        __builtin_amdgcn_sched_barrier(0);     // those loads stay ahead of this group's work
+        unsigned live = 0u;                    // bit L: k > 0 (the ReLU's mask)
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                bwd_floats4<ES>(kr[t][u], &k[t][4 * u]);
-                bwd_floats4<ES>(vr[t][u], &v[t][4 * u]);
-            }
-        {
-            const uint32_t rn = row_off(grp + 4);
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t off = rn == kOOB ? kOOB : rn + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
-                    kr[t][u] = bwd_load4<ES>(rK, off);
-                    vr[t][u] = bwd_load4<ES>(rV, off);
-                }
+        for (int L = 0; L < FPL; ++L) {
+            live |= (at[L] > 0.f ? 1u : 0u) << L;
+            at[L] = fmaxf(at[L], 0.f);
         }
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) at[t][r] = fmaxf(k[t][r], 0.f);
         RopePos pos{0, 0, 0};
         if constexpr (ROPE) {
-            const int tok = min(tok_lo + grp * 32 + m, tok_hi - 1);
-            pos = rope_pos((uint32_t)tok, frame_lo, a.rope);
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) rope_rotate<2>(&at[t][4 * u], pos, pp[t][u], tab);
+            pos = rope_pos((uint32_t)min(tok_lo + grp * 16 + m, tok_hi - 1), frame_lo, a.rope);
+            rope_rotate<FPL / 2>(at, pos, pp, tab);
         }
-        // dv^T = G^T a~^T and da~^T = G v^T
-        f32x16_t dv[T], da[T];
+        f32x4_t dv[T], da[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int t = 0; t < T; ++t) dv[t] = da[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { dv[t][r] = 0.f; da[t][r] = 0.f; }
+        for (int st = 0; st < FPL; ++st)
 #pragma unroll
-        for (int tk = 0; tk < T; ++tk)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const int kap = 32 * tk + acc_row(x, h);
-                const float *rowG = Gs + kap * D + m, *rowT = Gt + kap * D + m;
-#pragma unroll
-                for (int to = 0; to < T; ++to) {
-                    dv[to] = __builtin_amdgcn_mfma_f32_32x32x2f32(rowG[32 * to], at[tk][x], dv[to], 0, 0, 0);
-                    da[to] = __builtin_amdgcn_mfma_f32_32x32x2f32(rowT[32 * to], v[tk][x], da[to], 0, 0, 0);
-                }
+            for (int t = 0; t < T; ++t) {
+                dv[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(go.f(t, st), at[st], dv[t], 0, 0, 0);
+                da[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(go.b(t, st), v[st], da[t], 0, 0, 0);
             }
+        float x[FPL], y[FPL];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int L = 0; L < FPL; ++L) {
+            x[L] = dv[L / 4][L % 4];
+            y[L] = da[L / 4][L % 4];
+        }
+        if constexpr (ROPE) rope_rotate_t<FPL / 2>(y, pos, pp, tab);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t off = ro == kOOB ? kOOB : ro + (uint32_t)((32 * t + 8 * u + 4 * h) * ES);
-                float x4[4], y4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x4[e] = dv[t][4 * u + e];
-                    y4[e] = da[t][4 * u + e];
-                }
-                if constexpr (ROPE) rope_rotate_t<2>(y4, pos, pp[t][u], tab);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * u + e;
-                    y4[e] = k[t][r] > 0.f ? y4[e] + hr[t][r] : 0.f;
-                }
-                bwd_store4<ES>(rdV, off, x4);
-                bwd_store4<ES>(rdK, off, y4);
-            }
+        for (int L = 0; L < FPL; ++L) y[L] = (live >> L) & 1u ? y[L] + hr[L] : 0.f;
+        bwd_pack<D, ES>(pv.v, x);
+        bwd_pack<D, ES>(pk.v, y);
+        pv.off = pk.off = off;
     }
+    bwd_flush<D, ES>(rdV, pv);
+    bwd_flush<D, ES>(rdK, pk);
 }
 
 // ---------------------------------------------------------------------------
@@ -3773,8 +3748,8 @@ svla_status forward(const char *fn, svla_op op, svla_dtype dt, int B, int H, int
 // ---- backward ---------------------------------------------------------------
 
 constexpr int kBwdMaxSplits = 4;     // query/key splits per block (the reverse scan reads this many)
-constexpr long kBwdWgs = 2048;       // query/key: workgroups wanted per launch
-constexpr int kBwdMinChunk = 128;    // ... but at least one 32-token group per wave
+constexpr long kBwdWgs = SVLA_BWD_WGS;
+constexpr int kBwdMinChunk = 128;    // ... but at least two 16-token groups per wave
 
 struct BwdPlan {
     Plan fwd;                        // the forward state rebuild: state build + export scan
@@ -3811,7 +3786,12 @@ svla_status make_bwd_plan(const char *fn, svla_dtype dt, int B, int H, int nb, i
                         e, kMaxRopeEntries, p.rope.gh, p.rope.gw);
         bp->tab_bytes = (int)((e * 8 + 255) & ~255L);
     }
-    bp->lds_query = (size_t)bp->tab_bytes + ((size_t)2 * d * d + 64 + 256 * (size_t)d) * 4;
+    // query side: state twice, z, then the per-wave token tiles (2 x 16 rows of
+    // d + 16 floats) or the end-of-workgroup reductions, whichever is larger
+    const size_t tiles = (size_t)128 * (d + 16), red_s = (size_t)1024 * (d / 16) * (d / 16),
+                 red_z = (size_t)64 * d + 256;
+    const size_t work = tiles > red_s ? (tiles > red_z ? tiles : red_z) : (red_s > red_z ? red_s : red_z);
+    bp->lds_query = (size_t)bp->tab_bytes + ((size_t)2 * d * d + 64 + work) * 4;
     bp->lds_key = (size_t)bp->tab_bytes + ((size_t)2 * d * d + 64 + 64) * 4;
     // workspace: the forward's split partials, then the rebuilt prefix states,
     // the query side's partials and the reverse scan's G, H
