@@ -82,15 +82,21 @@ typedef enum svla_status {
     SVLA_ERR_UNSUPPORTED = 5, /* d not in {32,64,128}; RoPE split or grid too large */
     SVLA_ERR_WORKSPACE = 6,   /* workspace smaller than svla_workspace_size() */
     SVLA_ERR_VALUE = 7,       /* eps < 0 or not finite; bad RoPE parameters   */
-    SVLA_ERR_HIP = 8          /* a kernel launch failed                       */
+    SVLA_ERR_HIP = 8,         /* a kernel launch failed                       */
+    /* not statuses: they make the type hold every int, so a C caller's
+       out-of-range value is an unknown status, never undefined in C++ */
+    SVLA_STATUS_INT_MIN_ = -2147483647 - 1,
+    SVLA_STATUS_INT_MAX_ = 2147483647
 } svla_status;
 
 typedef enum svla_dtype {
     SVLA_F32 = 0,   /* IEEE binary32 Q/K/V/O */
     SVLA_BF16 = 1,  /* bfloat16 Q/K/V/O; arithmetic accumulates in fp32 */
-    SVLA_FP8 = 2    /* OCP FP8 E4M3 Q/K/V (1 byte per element; d = 32 only) with a
+    SVLA_FP8 = 2,   /* OCP FP8 E4M3 Q/K/V (1 byte per element; d = 32 only) with a
                        bfloat16 O: the low-precision inputs that the abstract's
                        NVFP4 deployment points to; arithmetic as for bf16 */
+    SVLA_DTYPE_INT_MIN_ = -2147483647 - 1,   /* range markers, as for svla_status */
+    SVLA_DTYPE_INT_MAX_ = 2147483647
 } svla_dtype;
 
 /* Which call a workspace is sized for. */
@@ -101,7 +107,9 @@ typedef enum svla_op {
     SVLA_OP_STATE_BUILD = 3,
     SVLA_OP_STATE_SCAN = 4,
     SVLA_OP_APPLY = 5,
-    SVLA_OP_BACKWARD = 6        /* svla_block_causal_backward */
+    SVLA_OP_BACKWARD = 6,       /* svla_block_causal_backward */
+    SVLA_OP_INT_MIN_ = -2147483647 - 1,      /* range markers, as for svla_status */
+    SVLA_OP_INT_MAX_ = 2147483647
 } svla_op;
 
 /* 3D RoPE on the numerator (host struct; may live on the stack).
