@@ -747,15 +747,27 @@ def copy_calibration():
 
 
 def ceiling(reps: int = 20):
-    """Achievable HBM rates on this GPU: a device-to-device copy of 2 GiB
-    (reads + writes) and a read-only reduction over 2 GiB, each the median of
-    `reps` event-timed runs over four rotating buffers (8 GiB, far past the
-    256 MB Infinity Cache)."""
+    """Achievable HBM rates on this GPU, from the library's bandwidth probes
+    (svla_hbm_probe: 16-byte non-temporal buffer loads, 2048 workgroups each
+    streaming one contiguous MiB): a read of 2 GiB and a copy of 2 GiB (reads +
+    writes), each the median of `reps` event-timed runs over four rotating
+    buffers (8 GiB, far past the 256 MB Infinity Cache)."""
+    import ctypes
     import torch
-    nbytes = 2 << 30
+    import block_causal_linear_relu_amd as svla
+    lib = svla.library()
+    nbytes, wgs = 2 << 30, 2048
     src = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda:0") for _ in range(4)]
     dst = [torch.empty_like(s) for s in src]
-    out = torch.empty((), dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def probe(mode, i):
+        st = lib.svla_hbm_probe(mode, ctypes.c_void_p(src[i % 4].data_ptr()),
+                                ctypes.c_void_p(dst[i % 4].data_ptr()), nbytes,
+                                ctypes.c_void_p(sink.data_ptr()), wgs, stream)
+        if st != 0:
+            raise RuntimeError("svla_hbm_probe failed: %d" % st)
 
     def med(fn):
         for i in range(3):
@@ -771,12 +783,14 @@ def ceiling(reps: int = 20):
             ts.append(a.elapsed_time(b))
         return _pct(ts, 50)
 
-    t_copy = med(lambda i: dst[i % 4].copy_(src[i % 4]))
-    t_read = med(lambda i: torch.sum(src[i % 4], dtype=torch.float32, out=out))
-    res = {"copy_GBps": 2 * nbytes / (t_copy * 1e-3) / 1e9, "read_GBps": nbytes / (t_read * 1e-3) / 1e9,
-           "copy_ms": t_copy, "read_ms": t_read, "bytes": nbytes, "peak_GBps": HBM_PEAK_GBPS}
-    res["copy_frac"] = res["copy_GBps"] / HBM_PEAK_GBPS
+    t_read = med(lambda i: probe(0, i))
+    t_copy = med(lambda i: probe(1, i))
+    t_torch = med(lambda i: dst[i % 4].copy_(src[i % 4]))
+    res = {"read_GBps": nbytes / (t_read * 1e-3) / 1e9, "copy_GBps": 2 * nbytes / (t_copy * 1e-3) / 1e9,
+           "torch_copy_GBps": 2 * nbytes / (t_torch * 1e-3) / 1e9,
+           "read_ms": t_read, "copy_ms": t_copy, "bytes": nbytes, "peak_GBps": HBM_PEAK_GBPS}
     res["read_frac"] = res["read_GBps"] / HBM_PEAK_GBPS
+    res["copy_frac"] = res["copy_GBps"] / HBM_PEAK_GBPS
     print(json.dumps(res), flush=True)
 
 

@@ -331,6 +331,17 @@ svla_status svla_block_causal_backward(svla_dtype dt, int B, int H, int nb, int 
  * copied.  Pass NULL (or n = 0) to stop.  Timing adds no other work. */
 svla_status svla_set_timing_events(void *const *events, int n);
 
+/* HBM bandwidth probes for a benchmark's ceiling measurement (not part of the
+ * method): mode 0 streams `bytes` of src through 16-byte non-temporal loads
+ * (sink: `workgroups` unsigned ints, written only in a case that does not
+ * occur; required), mode 1 copies src to dst (non-overlapping) the same way.
+ * `workgroups` workgroups of 256 threads each take one contiguous range;
+ * bytes must be a multiple of workgroups * 16 KiB, each range below 2 GiB,
+ * pointers 16-byte aligned.  Launches one kernel on `stream`; allocates
+ * nothing.  SVLA_ERR_VALUE (mode, workgroups), _NULL, _SHAPE, _ALIGN, _HIP. */
+svla_status svla_hbm_probe(int mode, const void *src, void *dst, size_t bytes,
+                           unsigned int *sink, int workgroups, svla_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -272,3 +272,15 @@ def test_backward_empty_and_workspace(lib):
     assert _bwd(lib, B=1, H=70, nb=7, n=2640, wsb=n - 1) == 6
     st, _ = _ws(lib, _lib.OP_BACKWARD, _lib.SVLA_BF16, 1, 20, 8, 1760, 128)
     assert st == 5
+
+
+def test_hbm_probe_rejects(lib):
+    f = lib.svla_hbm_probe
+    S = ctypes.c_void_p(0x20000)
+    assert f(2, A, A2, 1 << 24, S, 16, None) == 7           # mode
+    assert f(0, A, None, 1 << 24, S, 0, None) == 7          # no workgroups
+    assert f(0, None, None, 1 << 24, S, 16, None) == 1      # src
+    assert f(0, A, None, 1 << 24, None, 16, None) == 1      # sink for the read
+    assert f(1, A, None, 1 << 24, None, 16, None) == 1      # dst for the copy
+    assert f(0, A, None, (1 << 24) + 16, S, 16, None) == 2  # not whole 16 KiB chunks
+    assert f(1, MIS, A2, 1 << 24, None, 16, None) == 4
