@@ -56,6 +56,8 @@ SOURCE = os.path.join(ROOT, "block_causal_linear_relu_amd", "csrc", "svla.hip")
 KERNEL_SLOTS = {"build": (0, 1), "scan": (2, 3), "apply": (4, 5), "step": (6, 7), "conv": (8, 9),
                 "bwd_query": (10, 11), "bwd_scan": (12, 13), "bwd_key": (14, 15)}
 BWD_METRIC = "block-causal linear-attn backward tokens·heads/s + achieved TFLOP/s vs MI355X fp32 MFMA peak"
+ANCHOR_METRIC = "block-causal softmax anchor tokens·heads/s + achieved TFLOP/s vs MI355X bf16 MFMA peak"
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
 CONV_METRIC = "causal temporal conv frames·positions·channels/s + achieved HBM GB/s vs MI355X peak"
 CONV_UNIT = "frames·positions·channels/s"
@@ -82,6 +84,8 @@ def parse():
                     help="input type of Q, K, V (fp8: OCP E4M3, d = 32 workloads; O stays bf16)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (block-causal training) of the workload")
+    ap.add_argument("--anchor", action="store_true",
+                    help="time the 2.0 hybrid's softmax anchor layer on the gated 720p shape (c5)")
     ap.add_argument("--inplace", action="store_true",
                     help="streaming: commit the state in place (the two-kernel step)")
     ap.add_argument("--rotate", type=int, default=4)
@@ -474,6 +478,74 @@ def measure_backward(w: BackwardWorkload, args, settle_s: float) -> dict:
     }
 
 
+class AnchorWorkload:
+    """One block-causal softmax anchor layer over a whole clip (queries of all
+    nb blocks against all their keys), R rotating input sets."""
+
+    def __init__(self, name: str, rotate: int):
+        import numpy as np
+        import torch
+        import block_causal_linear_relu_amd as svla
+        from workloads import CONFIGS, make_inputs
+
+        self.torch, self.svla = torch, svla
+        self.cfg = cfg = CONFIGS[name]
+        self.name, self.mode, self.stream_mode = name, "anchor", False
+        self.x = x = make_inputs(cfg)
+        dev = torch.device("cuda:0")
+        base = [torch.from_numpy(x[k]).to(dev).to(torch.bfloat16) for k in "QKV"]
+        B, H, N, d = base[0].shape
+        self.B, self.H, self.N, self.d, self.nb, self.n = B, H, N, d, cfg.nb, cfg.n
+        self.sets = []
+        for r in range(rotate):
+            ins = base if r == 0 else [t.clone() for t in base]
+            self.sets.append((ins, torch.empty_like(base[0])))
+        torch.cuda.synchronize()
+
+    @property
+    def tokens_heads(self) -> int:
+        return self.B * self.H * self.N
+
+    def flops(self) -> int:
+        """Matrix flops of the block-causal layer: block c's n queries against
+        (c + 1) n keys, q.k and the weighted sum of v, 2 d flops each."""
+        n, nb, d = self.n, self.nb, self.d
+        return self.B * self.H * 4 * d * n * n * nb * (nb + 1) // 2
+
+    def bytes(self) -> int:
+        return self.B * self.H * self.N * self.d * 2 * 4       # Q, K, V read once, O written once
+
+    def step(self, i: int):
+        (q, k, v), o = self.sets[i % len(self.sets)]
+        self.svla.softmax_attention(q, k, v, self.nb, out=o)
+
+    def describe(self) -> dict:
+        c = self.cfg
+        return {"workload": "%s anchor: block-causal softmax attention on the shape of %s" % (c.name, c.description),
+                "B": c.B, "H": c.H, "N": c.N, "d": c.d, "blocks": c.nb, "block_tokens": c.n,
+                "input_dtype": "bf16", "scale": "1/sqrt(d)", "mode": "one call over all %d blocks" % c.nb,
+                "rotating_input_sets": len(self.sets)}
+
+
+def anchor_cpu_baseline(w: AnchorWorkload, budget_s: float = 10.0) -> dict:
+    """The numpy fp64 softmax oracle on the host, head by head, until about
+    `budget_s` seconds have passed."""
+    from oracle.softmax import softmax_attention
+    x = w.x
+    heads, secs = 0, 0.0
+    while secs < budget_s and heads < w.B * w.H:
+        b, h = divmod(heads, w.H)
+        sl = lambda a: a[b:b + 1, h:h + 1]
+        t = time.perf_counter()
+        softmax_attention(sl(x["Q"]), sl(x["K"]), sl(x["V"]), w.nb)
+        secs += time.perf_counter() - t
+        heads += 1
+    return {"value": heads * w.N / secs, "unit": UNIT, "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) slices of the %s anchor (numpy fp64; its matrix products "
+                      "use the BLAS threads), %.1f s" % (heads, w.B * w.H, w.name, secs)}
+
+
 def conv_cpu_baseline(w: ConvWorkload, budget_s: float = 10.0) -> dict:
     """The numpy fp64 oracle of the temporal convolution on the host, repeated
     over the full workload until about `budget_s` seconds have passed."""
@@ -819,6 +891,25 @@ def main():
         ceiling()
         return
 
+    if args.anchor:
+        aw = AnchorWorkload("c5" if args.config == "c4" else args.config, args.rotate)
+        settled = settle(aw, args.settle) if args.settle > 0 else 0
+        t = time_steps(aw, args.steps, args.warmup)
+        ms = t["mean_ms"]
+        tf = aw.flops() / (ms * 1e-3) / 1e12
+        line = {"metric": ANCHOR_METRIC, "value": aw.tokens_heads / (ms * 1e-3), "unit": UNIT, "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "settle_steps": settled, "ms_per_step": ms,
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic (seeded N(0,1) Q, K, V, bf16-rounded)", "config": aw.describe(),
+                "timing": {k: t[k] for k in ("median_ms", "p10_ms", "p90_ms")},
+                "roofline": {"bound": "mfma", "kernel": "void svla_softmax_fwd<%d>" % aw.d, "achieved": tf,
+                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                             "traffic": None, "algorithmic_flops_per_launch": aw.flops(),
+                             "avg_launch_ms": ms, "hbm_GBps": aw.bytes() / (ms * 1e-3) / 1e9},
+                "source": "block_causal_linear_relu_amd/csrc/svla_softmax.hip",
+                "cpu_baseline": None if args.no_cpu_baseline else anchor_cpu_baseline(aw)}
+        print(json.dumps(line), flush=True)
+        return
     if args.backward:
         if args.config not in ("c3", "c2") or args.dtype != "bf16":
             print("bench.py: --backward times the bf16 d = 32 training shapes (c3, c2)", file=sys.stderr)

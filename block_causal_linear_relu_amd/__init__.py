@@ -27,7 +27,7 @@ from . import _lib
 from ._lib import SvlaError, rope_struct  # noqa: F401
 
 __all__ = ["noncausal", "block_causal", "block_step", "block_step_noalloc", "state_build",
-           "state_scan", "apply", "temporal_conv", "block_causal_backward",
+           "state_scan", "apply", "temporal_conv", "block_causal_backward", "softmax_attention",
            "workspace_size", "describe", "set_timing_events", "SvlaError", "library"]
 
 _DT = {torch.bfloat16: _lib.SVLA_BF16, torch.float32: _lib.SVLA_F32,
@@ -423,3 +423,35 @@ def block_causal_backward(Q, K, V, dO, nb: int, S0=None, z0=None, g=None, rope=N
         _ptr(out.get("dS0")), _ptr(out.get("dz0")), _ptr(ws), nbytes, _stream(Q.device))
     _lib.check(lib, st)
     return out
+
+
+def softmax_attention(Q, K, V, nb: int, scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None):
+    """Block-causal softmax attention (the 2.0 hybrid's anchor layers): Q
+    [B,H,nb*n,d] against K, V [B,H,Nk,d], Nk >= nb*n (the first Nk - nb*n keys
+    are a cache of earlier blocks); query i of block c sees keys
+    0 .. Nk - nb*n + (c+1)*n - 1.  scale defaults to 1/sqrt(d).  bf16."""
+    for t, name in ((Q, "Q"), (K, "K"), (V, "V")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+    if Q.dim() != 4 or K.dim() != 4 or V.shape != K.shape:
+        raise ValueError("Q must be [B,H,Nq,d] and K, V one [B,H,Nk,d] shape")
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    if tuple(K.shape[:2]) != (B, H) or K.shape[3] != d:
+        raise ValueError("K, V must be [B,H,Nk,d] with Q's B, H and d")
+    if nb <= 0 or Nq % nb:
+        raise ValueError("Nq=%d is not a multiple of nb=%d" % (Nq, nb))
+    if Nk < Nq:
+        raise ValueError("Nk=%d is smaller than Nq=%d" % (Nk, Nq))
+    _shape(out, Q.shape, "out")
+    _dev(Q, "Q", torch.bfloat16)
+    _dev(K, "K", torch.bfloat16)
+    _dev(V, "V", torch.bfloat16)
+    lib = library()
+    O = torch.empty(Q.shape, dtype=torch.bfloat16, device=Q.device) if out is None else _dev(out, "out", torch.bfloat16)
+    s = (1.0 / float(d) ** 0.5) if scale is None else float(scale)
+    st = lib.svla_softmax_attention(_lib.SVLA_BF16, B, H, nb, Nq // nb, Nk, d, _ptr(Q), _ptr(K), _ptr(V),
+                                    _ptr(O), s, _stream(Q.device))
+    _lib.check(lib, st)
+    return O

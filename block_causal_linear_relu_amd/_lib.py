@@ -62,6 +62,7 @@ PROTOTYPES = {
                                         _rp, _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "svla_set_timing_events": (_i, [ctypes.POINTER(_vp), _i]),
     "svla_hbm_probe": (_i, [_i, _vp, _vp, _sz, _vp, _i, _vp]),
+    "svla_softmax_attention": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _vp]),
     "svla_describe": (_i, [_i, _i, _i, _i, _i, _i, _i, _rp, ctypes.c_char_p, _sz]),
 }
 

@@ -1,0 +1,305 @@
+// svla_softmax_attention: the softmax "anchor" layers of the SANA-Video 2.0
+// hybrid (2.0 news page, the hybrid linear-softmax attention paragraph:
+// periodic softmax layers among gated linear ones, three to one; comfyui-wiki
+// model page, the 2.0 section: dense softmax anchors), on the block schedule
+// of the linear layers (talk, block-by-block generation): queries of nb blocks
+// of n tokens against Nk >= nb*n cached keys; query i (block c = i / n) sees
+// keys 0 .. Nk - nb*n + (c+1)*n - 1, and
+//     O_i = sum_j softmax_j(scale * q_i . k_j) v_j.
+// bf16 Q, K, V, O; fp32 logits, weights and sums.  The kernel is kept in a
+// source of its own.
+//
+// Workgroup = (b,h, tile of 128 queries), four waves of 32 queries each; the
+// tiles are launched heaviest first (the last query tiles see the most keys).
+// The keys stream through LDS in tiles of 64, the next tile's K and V loaded
+// into registers while the current one is used.  Per 32-key half, on
+// v_mfma_f32_32x32x16_bf16:
+//   S^T = K Q^T   rows = keys, columns = queries: the K tile is the A operand
+//                 (16-byte LDS reads of its rows), the wave's Q rows the B
+//                 operand, held in registers for the whole kernel; lane
+//                 (n, h) ends with 16 of the 32 keys' logits of query n, so a
+//                 query's running max and sum need one lane swap.
+//   O^T += V^T P^T  rows = features, columns = queries: P is the B operand
+//                 straight from the lane's own registers (the k-slots of a
+//                 contraction over keys may be taken in any order as long as
+//                 both operands agree), V^T the A operand from a transposed
+//                 LDS copy of the V tile; the A operand's rows are ordered so
+//                 that lane (n, h) accumulates 16 contiguous features of its
+//                 query per output tile (two 16-byte stores at the end).
+// Online softmax in base 2 (logits scaled by scale * log2 e): running max m
+// and per-lane partial sum l per query; the accumulator is rescaled only when
+// some query of the wave raised its max.  Keys past a query's visible range
+// (only in the last tiles of a workgroup) get weight zero.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/svla.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+
+constexpr int kSmThreads = 256;        // four waves
+constexpr int kQTile = 128;            // queries per workgroup (32 per wave)
+constexpr int kKTile = 64;             // keys per LDS tile
+constexpr uint32_t kSmOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sm_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t sm_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ unsigned int sm_pack_bf16(float lo, float hi)
+{
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+struct SoftmaxArgs {
+    const void *Q, *K, *V;
+    void *O;
+    int Nq, Nk, n;                 // queries (nb * n), keys, tokens per block
+    int qtiles;                    // query tiles per (b,h)
+    long BH;
+    float c2;                      // scale * log2(e)
+};
+
+// Feature that row m of output tile t holds (see the header comment): lane
+// (n, h) register r of tile t is feature 32 t + 16 h + r.
+__device__ __forceinline__ int sm_feat(int t, int m)
+{
+    return 32 * t + 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kSmThreads)
+svla_softmax_fwd(const SoftmaxArgs a)
+{
+    constexpr int KK = D / 16;                 // 16-feature steps of the logit product
+    constexpr int T = D / 32;                  // output tiles of 32 features
+    constexpr int LDK = D + 8;                 // K tile row, bf16 elements
+    constexpr int LDV = kKTile + 8;            // V^T tile row, bf16 elements
+    constexpr int CPT = kKTile * D / 8 / kSmThreads;   // 16-byte chunks per thread per tensor
+    __shared__ __attribute__((aligned(16))) unsigned short Ks[kKTile * LDK];
+    __shared__ __attribute__((aligned(16))) unsigned short Vt[D * LDV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 31, h = lane >> 5;
+    const long bh = blockIdx.x % a.BH;
+    const int qt = a.qtiles - 1 - (int)(blockIdx.x / a.BH);     // heaviest tiles first
+    const int q0 = qt * kQTile;
+    const uint32_t qslice = (uint32_t)a.Nq * D * 2, kslice = (uint32_t)a.Nk * D * 2;
+    const auto rQ = sm_rsrc((const char *)a.Q + bh * qslice, qslice);
+    const auto rO = sm_rsrc((char *)a.O + bh * qslice, qslice);
+    const auto rK = sm_rsrc((const char *)a.K + bh * kslice, kslice);
+    const auto rV = sm_rsrc((const char *)a.V + bh * kslice, kslice);
+
+    // visible keys of a query row: Nk - Nq + (block + 1) n; rows past Nq see none
+    auto limit_of = [&](int row) -> int {
+        return row < a.Nq ? a.Nk - a.Nq + (row / a.n + 1) * a.n : 0;
+    };
+    const int qrow = q0 + 32 * wave + m;          // this lane's query
+    const int lim = limit_of(qrow);
+    // the workgroup's key range: up to the largest limit of its rows; tiles
+    // below the smallest limit need no mask
+    const int last_row = min(q0 + kQTile, a.Nq) - 1;
+    const int kmax = limit_of(last_row);
+    const int kmin = limit_of(q0);
+    const int ntiles = (kmax + kKTile - 1) / kKTile;
+
+    // Q rows of the wave (B operand of S^T = K Q^T): 16 features per step
+    u32x4_t qv[KK];
+    {
+        const uint32_t off = qrow < a.Nq ? (uint32_t)qrow * D * 2 : kSmOOB;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qv[kk] = sm_load16(rQ, off == kSmOOB ? kSmOOB : off + (uint32_t)(16 * kk + 8 * h) * 2);
+    }
+    // tile loader: thread -> CPT 16-byte chunks of K and of V
+    u32x4_t kreg[CPT], vreg[CPT];
+    auto issue = [&](int tile) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int idx = tid + c * kSmThreads;            // chunk index in the tile
+            const int key = idx / (D / 8), ch = idx % (D / 8);
+            const int kg = tile * kKTile + key;
+            const uint32_t off = kg < kmax ? ((uint32_t)kg * D + ch * 8) * 2 : kSmOOB;
+            kreg[c] = sm_load16(rK, off);
+            vreg[c] = sm_load16(rV, off);
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int idx = tid + c * kSmThreads;
+            const int key = idx / (D / 8), ch = idx % (D / 8);
+            *(u32x4_t *)(Ks + key * LDK + ch * 8) = kreg[c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Vt[(ch * 8 + 2 * e) * LDV + key] = (unsigned short)(vreg[c][e] & 0xFFFFu);
+                Vt[(ch * 8 + 2 * e + 1) * LDV + key] = (unsigned short)(vreg[c][e] >> 16);
+            }
+        }
+    };
+
+    f32x16_t acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+    float mrun = -INFINITY, lsum = 0.f;
+
+    if (ntiles > 0) issue(0);
+    for (int it = 0; it < ntiles; ++it) {
+        __syncthreads();                 // the previous tile's LDS reads are done
+        stage();
+        __syncthreads();
+        if (it + 1 < ntiles) issue(it + 1);
+        __builtin_amdgcn_sched_barrier(0);   // those loads stay ahead of this tile's work
+        const int k0 = it * kKTile;
+        // logits of the two 32-key halves: lane (n, h) holds keys
+        // 32 half + 8 (r / 4) + 4 h + r % 4 of query n
+        f32x16_t s[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[hf][r] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const u32x4_t kv = *(const u32x4_t *)(Ks + (32 * hf + m) * LDK + 16 * kk + 8 * h);
+                s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
+                                                                __builtin_bit_cast(bf16x8_t, qv[kk]),
+                                                                s[hf], 0, 0, 0);
+            }
+        }
+        // scale, mask, running max
+        const bool masked = k0 + kKTile > kmin;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = s[hf][r] * a.c2;
+                if (masked) {
+                    const int key = k0 + 32 * hf + 8 * (r >> 2) + 4 * h + (r & 3);
+                    x = key < lim ? x : -INFINITY;
+                }
+                s[hf][r] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mnew = fmaxf(mrun, tmax);
+        const float muse = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = exp2f(mrun - muse);
+        mrun = mnew;
+        // the weights, their sum, and P as bf16 (the B operand of O^T += V^T P^T)
+        unsigned int pw[2][8];
+        float psum = 0.f;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = exp2f(s[hf][r] - muse), p1 = exp2f(s[hf][r + 1] - muse);
+                psum += p0 + p1;
+                pw[hf][r / 2] = sm_pack_bf16(p0, p1);
+            }
+        lsum = lsum * alpha + psum;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+        }
+        // O^T += V^T P^T: per 32-key half two 16-key steps; k-slot i of lane
+        // half h in step st is the lane's register 8 st + i, i.e. key
+        // 32 hf + 16 st + 8 (i / 4) + 4 h + i % 4
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const u32x4_t pb = {pw[hf][4 * st], pw[hf][4 * st + 1], pw[hf][4 * st + 2], pw[hf][4 * st + 3]};
+                const int kb = 32 * hf + 16 * st + 4 * h;
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const unsigned short *row = Vt + sm_feat(t, m) * LDV + kb;
+                    const u32x2_t lo = *(const u32x2_t *)row;
+                    const u32x2_t hi = *(const u32x2_t *)(row + 8);
+                    const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                                     __builtin_bit_cast(bf16x8_t, pb),
+                                                                     acc[t], 0, 0, 0);
+                }
+            }
+    }
+    // O = acc / l: lane (n, h) holds features 32 t + 16 h + r of its query
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (qrow < a.Nq) {
+        const uint32_t off = (uint32_t)qrow * D * 2;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4_t o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = sm_pack_bf16(acc[t][8 * c + 2 * e] * inv, acc[t][8 * c + 2 * e + 1] * inv);
+                __builtin_amdgcn_raw_buffer_store_b128(o, rO, (int)(off + (uint32_t)(32 * t + 16 * h + 8 * c) * 2), 0, 0);
+            }
+    }
+}
+
+bool sm_overlap(const void *x, size_t nx, const void *y, size_t ny)
+{
+    if (!x || !y) return false;
+    const uintptr_t a = (uintptr_t)x, b = (uintptr_t)y;
+    return a < b + ny && b < a + nx;
+}
+
+}  // namespace
+
+extern "C" svla_status svla_softmax_attention(svla_dtype dt, int B, int H, int nb, int n, int Nk,
+                                              int d, const void *Q, const void *K, const void *V,
+                                              void *O, float scale, svla_stream stream)
+{
+    if (dt != SVLA_BF16) return SVLA_ERR_DTYPE;
+    if (B < 0 || H < 0 || nb < 0 || n < 0 || Nk < 0) return SVLA_ERR_SHAPE;
+    if (d != 64 && d != 128) return SVLA_ERR_UNSUPPORTED;
+    const long long Nq = (long long)nb * n;
+    if (Nk < Nq) return SVLA_ERR_SHAPE;
+    if ((long long)Nk * d * 2 >= (1LL << 31)) return SVLA_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return SVLA_ERR_VALUE;
+    const long long BH = (long long)B * H;
+    if (BH == 0 || Nq == 0) return SVLA_OK;
+    if (!Q || !K || !V || !O) return SVLA_ERR_NULL;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15) return SVLA_ERR_ALIGN;
+    const size_t qb = (size_t)(BH * Nq * d * 2), kb = (size_t)(BH * Nk * d * 2);
+    if (sm_overlap(O, qb, Q, qb) || sm_overlap(O, qb, K, kb) || sm_overlap(O, qb, V, kb))
+        return SVLA_ERR_VALUE;
+    const int qtiles = (int)((Nq + kQTile - 1) / kQTile);
+    if (BH * qtiles >= (1LL << 31)) return SVLA_ERR_SHAPE;
+    SoftmaxArgs a;
+    memset(&a, 0, sizeof a);
+    a.Q = Q; a.K = K; a.V = V; a.O = O;
+    a.Nq = (int)Nq; a.Nk = Nk; a.n = n; a.qtiles = qtiles; a.BH = BH;
+    a.c2 = scale * 1.4426950408889634f;
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    const unsigned grid = (unsigned)(BH * qtiles);
+    if (d == 128) svla_softmax_fwd<128><<<grid, kSmThreads, 0, s>>>(a);
+    else svla_softmax_fwd<64><<<grid, kSmThreads, 0, s>>>(a);
+    return hipGetLastError() == hipSuccess ? SVLA_OK : SVLA_ERR_HIP;
+}

@@ -318,6 +318,27 @@ svla_status svla_block_causal_backward(svla_dtype dt, int B, int H, int nb, int 
                                        float *dS0, float *dz0, void *ws, size_t ws_bytes,
                                        svla_stream stream);
 
+/* ---- the 2.0 hybrid's softmax anchors -------------------------------------------- */
+
+/* Softmax attention on the block schedule of the linear layers: the dense
+ * softmax "anchor" layers that SANA-Video 2.0 interleaves with its gated linear
+ * layers ([2.0 news], the hybrid linear-softmax attention paragraph; [Model
+ * page], the 2.0 section), bidirectional inside a block and causal across
+ * blocks ([Talk], block-by-block generation).  Queries of nb blocks of n tokens
+ * (Q, O [B,H,nb*n,d]) attend Nk >= nb*n keys (K, V [B,H,Nk,d]) whose first
+ * Nk - nb*n come before the queries' first block (a KV cache): query i, in
+ * block c = i / n, sees keys 0 .. Nk - nb*n + (c+1)*n - 1, and
+ *     O_i = sum_j softmax_j(scale * q_i . k_j) v_j.
+ * One call over all blocks is Nk = nb*n; a streaming step of block c is nb = 1,
+ * Nk = (c+1)*n.  bf16 only (SVLA_ERR_DTYPE otherwise); d = 64 or 128
+ * (SVLA_ERR_UNSUPPORTED otherwise); scale > 0 and finite (SVLA_ERR_VALUE; the
+ * usual choice is 1/sqrt(d)); O must not overlap Q, K or V (SVLA_ERR_VALUE);
+ * one (b,h) slice of K below 2 GiB.  Logits, weights and sums are fp32; O is
+ * rounded once to bf16.  No workspace; one kernel on `stream`. */
+svla_status svla_softmax_attention(svla_dtype dt, int B, int H, int nb, int n, int Nk, int d,
+                                   const void *Q, const void *K, const void *V, void *O,
+                                   float scale, svla_stream stream);
+
 /* ---- instrumentation ----------------------------------------------------------- */
 
 /* For benchmarks that time each kernel with HIP events.  While set, every

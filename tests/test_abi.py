@@ -284,3 +284,17 @@ def test_hbm_probe_rejects(lib):
     assert f(1, A, None, 1 << 24, None, 16, None) == 1      # dst for the copy
     assert f(0, A, None, (1 << 24) + 16, S, 16, None) == 2  # not whole 16 KiB chunks
     assert f(1, MIS, A2, 1 << 24, None, 16, None) == 4
+
+
+def test_softmax_attention_rejects(lib):
+    f = lib.svla_softmax_attention
+    bf = _lib.SVLA_BF16
+    assert f(_lib.SVLA_F32, 1, 2, 2, 64, 128, 128, A, A, A, A2, 0.1, None) == 3
+    assert f(bf, 1, 2, 2, 64, 128, 32, A, A, A, A2, 0.1, None) == 5          # d
+    assert f(bf, 1, 2, 2, 64, 100, 128, A, A, A, A2, 0.1, None) == 2         # Nk < nb*n
+    assert f(bf, 1, 2, 2, 64, 128, 128, A, A, A, A2, 0.0, None) == 7         # scale
+    assert f(bf, 1, 2, 2, 64, 128, 128, A, A, None, A2, 0.1, None) == 1
+    assert f(bf, 1, 2, 2, 64, 128, 128, MIS, A, A, A2, 0.1, None) == 4
+    assert f(bf, 1, 2, 2, 64, 128, 128, A, A, A, A, 0.1, None) == 7          # O overlaps Q
+    assert f(bf, 0, 2, 2, 64, 128, 128, None, None, None, None, 0.1, None) == 0
+    assert f(bf, 1, 2, 1, 1 << 24, 1 << 24, 128, A, A, A, A2, 0.1, None) == 2  # a K slice past 2 GiB

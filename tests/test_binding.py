@@ -93,3 +93,12 @@ def test_backward_shapes(kw, name):
 
 def test_backward_block_count():
     _raises("multiple", svla.block_causal_backward, *qkv(), qkv()[0], 3)
+
+
+def test_softmax_attention_shapes():
+    Q = torch.zeros(B, H, N, 64, dtype=torch.bfloat16)
+    K = torch.zeros(B, H, N + 8, 64, dtype=torch.bfloat16)
+    _raises("multiple", svla.softmax_attention, Q, K, K, 3)
+    _raises("smaller", svla.softmax_attention, Q, K[:, :, :N - 4], K[:, :, :N - 4], 4)
+    _raises("one", svla.softmax_attention, Q, K, K[:, :, :N], 4)
+    _raises("out", svla.softmax_attention, Q, K, K, 4, out=torch.zeros(B, H, N, 32))
