@@ -11,8 +11,8 @@
 //
 // Workgroup = (b,h, tile of 128 queries), four waves of 32 queries each; the
 // tiles are launched heaviest first (the last query tiles see the most keys).
-// The keys stream through LDS in tiles of 64, the next tile's K and V loaded
-// into registers while the current one is used.  Per 32-key half, on
+// The keys stream through two LDS stages in tiles of 64; each tile's K and V
+// are loaded into registers two tiles ahead and staged one tile ahead.  Per 32-key half, on
 // v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T   rows = keys, columns = queries: the K tile is the A operand
 //                 (16-byte LDS reads of its rows), the wave's Q rows the B
@@ -84,6 +84,20 @@ __device__ __forceinline__ int sm_feat(int t, int m)
     return 32 * t + 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 }
 
+// LDS hand-off barrier that waits for this wave's LDS operations only (a
+// __syncthreads() would also wait for every global load in flight, i.e. for
+// the prefetched key tiles).
+__device__ __forceinline__ void sm_lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D>
+struct SmTile {                                 // one key tile's K and V chunks in registers
+    static constexpr int CPT = kKTile * D / 8 / kSmThreads;
+    u32x4_t k[CPT], v[CPT];
+};
+
 template <int D>
 __global__ void __launch_bounds__(kSmThreads)
 svla_softmax_fwd(const SoftmaxArgs a)
@@ -92,9 +106,10 @@ svla_softmax_fwd(const SoftmaxArgs a)
     constexpr int T = D / 32;                  // output tiles of 32 features
     constexpr int LDK = D + 8;                 // K tile row, bf16 elements
     constexpr int LDV = kKTile + 8;            // V^T tile row, bf16 elements
-    constexpr int CPT = kKTile * D / 8 / kSmThreads;   // 16-byte chunks per thread per tensor
-    __shared__ __attribute__((aligned(16))) unsigned short Ks[kKTile * LDK];
-    __shared__ __attribute__((aligned(16))) unsigned short Vt[D * LDV];
+    constexpr int CPT = SmTile<D>::CPT;        // 16-byte chunks per thread per tensor
+    constexpr int KSZ = kKTile * LDK, VSZ = D * LDV;
+    // two LDS stages of [K tile | V^T tile]
+    extern __shared__ __attribute__((aligned(16))) unsigned short sm_lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 31, h = lane >> 5;
@@ -120,7 +135,61 @@ svla_softmax_fwd(const SoftmaxArgs a)
     const int kmin = limit_of(q0);
     const int ntiles = (kmax + kKTile - 1) / kKTile;
 
-    // Q rows of the wave (B operand of S^T = K Q^T): 16 features per step
+    // K: thread -> 16-byte chunk (key, ch), consecutive lanes along a row.
+    // V: thread -> (key pair j, chunk ch) with j fastest: the rows 2j and 2j+1
+    // of the chunk, written to V^T as one 4-byte word (keys 2j, 2j+1) per
+    // feature, so the 32 lanes of a half-wave fill one V^T row segment and
+    // the two half-waves rows 8 features apart (32 banks apart).
+    auto issue = [&](SmTile<D> &r, int tile) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int idx = tid + c * kSmThreads;            // chunk index in the tile
+            const int key = idx / (D / 8), ch = idx % (D / 8);
+            const int kg = tile * kKTile + key;
+            const uint32_t off = tile < ntiles && kg < kmax ? ((uint32_t)kg * D + ch * 8) * 2 : kSmOOB;
+            r.k[c] = sm_load16(rK, off);
+        }
+#pragma unroll
+        for (int c = 0; c < CPT / 2; ++c) {
+            const int idx = tid + c * kSmThreads;
+            const int j = idx % (kKTile / 2), ch = idx / (kKTile / 2);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int kg = tile * kKTile + 2 * j + e;
+                const uint32_t off = tile < ntiles && kg < kmax ? ((uint32_t)kg * D + ch * 8) * 2 : kSmOOB;
+                r.v[2 * c + e] = sm_load16(rV, off);
+            }
+        }
+    };
+    auto stage = [&](const SmTile<D> &r, int buf) {
+        unsigned short *Ks = sm_lds + buf * (KSZ + VSZ), *Vt = Ks + KSZ;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int idx = tid + c * kSmThreads;
+            const int key = idx / (D / 8), ch = idx % (D / 8);
+            *(u32x4_t *)(Ks + key * LDK + ch * 8) = r.k[c];
+        }
+#pragma unroll
+        for (int c = 0; c < CPT / 2; ++c) {
+            const int idx = tid + c * kSmThreads;
+            const int j = idx % (kKTile / 2), ch = idx / (kKTile / 2);
+            const u32x4_t v0 = r.v[2 * c], v1 = r.v[2 * c + 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // features ch*8 + 2e (low halves) and ch*8 + 2e + 1 (high halves)
+                *(unsigned int *)(Vt + (ch * 8 + 2 * e) * LDV + 2 * j) =
+                    (v0[e] & 0xFFFFu) | (v1[e] << 16);
+                *(unsigned int *)(Vt + (ch * 8 + 2 * e + 1) * LDV + 2 * j) =
+                    (v0[e] >> 16) | (v1[e] & 0xFFFF0000u);
+            }
+        }
+    };
+
+    // the first two key tiles' loads, then the wave's Q rows (B operand of
+    // S^T = K Q^T, 16 features per step), held for the whole kernel
+    SmTile<D> ra, rb;
+    issue(ra, 0);
+    issue(rb, 1);
     u32x4_t qv[KK];
     {
         const uint32_t off = qrow < a.Nq ? (uint32_t)qrow * D * 2 : kSmOOB;
@@ -128,32 +197,6 @@ svla_softmax_fwd(const SoftmaxArgs a)
         for (int kk = 0; kk < KK; ++kk)
             qv[kk] = sm_load16(rQ, off == kSmOOB ? kSmOOB : off + (uint32_t)(16 * kk + 8 * h) * 2);
     }
-    // tile loader: thread -> CPT 16-byte chunks of K and of V
-    u32x4_t kreg[CPT], vreg[CPT];
-    auto issue = [&](int tile) {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int idx = tid + c * kSmThreads;            // chunk index in the tile
-            const int key = idx / (D / 8), ch = idx % (D / 8);
-            const int kg = tile * kKTile + key;
-            const uint32_t off = kg < kmax ? ((uint32_t)kg * D + ch * 8) * 2 : kSmOOB;
-            kreg[c] = sm_load16(rK, off);
-            vreg[c] = sm_load16(rV, off);
-        }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int idx = tid + c * kSmThreads;
-            const int key = idx / (D / 8), ch = idx % (D / 8);
-            *(u32x4_t *)(Ks + key * LDK + ch * 8) = kreg[c];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Vt[(ch * 8 + 2 * e) * LDV + key] = (unsigned short)(vreg[c][e] & 0xFFFFu);
-                Vt[(ch * 8 + 2 * e + 1) * LDV + key] = (unsigned short)(vreg[c][e] >> 16);
-            }
-        }
-    };
 
     f32x16_t acc[T];
 #pragma unroll
@@ -162,13 +205,9 @@ svla_softmax_fwd(const SoftmaxArgs a)
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
     float mrun = -INFINITY, lsum = 0.f;
 
-    if (ntiles > 0) issue(0);
-    for (int it = 0; it < ntiles; ++it) {
-        __syncthreads();                 // the previous tile's LDS reads are done
-        stage();
-        __syncthreads();
-        if (it + 1 < ntiles) issue(it + 1);
-        __builtin_amdgcn_sched_barrier(0);   // those loads stay ahead of this tile's work
+    // key tile it from LDS stage `buf`
+    auto compute = [&](int it, int buf) {
+        const unsigned short *Ks = sm_lds + buf * (KSZ + VSZ), *Vt = Ks + KSZ;
         const int k0 = it * kKTile;
         // logits of the two 32-key halves: lane (n, h) holds keys
         // 32 half + 8 (r / 4) + 4 h + r % 4 of query n
@@ -243,6 +282,28 @@ svla_softmax_fwd(const SoftmaxArgs a)
                                                                      acc[t], 0, 0, 0);
                 }
             }
+    };
+    // Tile t's loads go to register set t % 2 (ra even, rb odd) and are staged
+    // into LDS stage t % 2 during tile t - 1, after which the set is refilled
+    // with tile t + 2: two tiles of compute cover each load.  One barrier per
+    // tile: it publishes the staged tile and frees the stage just read.
+    if (ntiles > 0) {
+        stage(ra, 0);
+        issue(ra, 2);
+        sm_lds_barrier();
+    }
+    for (int it = 0; it < ntiles; it += 2) {
+        stage(rb, 1);                         // tile it + 1 (zeros past the range)
+        issue(rb, it + 3);
+        __builtin_amdgcn_sched_barrier(0);    // those loads stay ahead of this tile's work
+        compute(it, 0);
+        sm_lds_barrier();
+        if (it + 1 >= ntiles) break;
+        stage(ra, 0);                         // tile it + 2
+        issue(ra, it + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(it + 1, 1);
+        sm_lds_barrier();
     }
     // O = acc / l: lane (n, h) holds features 32 t + 16 h + r of its query
     const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -261,6 +322,9 @@ svla_softmax_fwd(const SoftmaxArgs a)
             }
     }
 }
+
+template <int D>
+constexpr size_t sm_lds_bytes() { return (size_t)2 * (kKTile * (D + 8) + D * (kKTile + 8)) * 2; }
 
 bool sm_overlap(const void *x, size_t nx, const void *y, size_t ny)
 {
@@ -299,7 +363,7 @@ extern "C" svla_status svla_softmax_attention(svla_dtype dt, int B, int H, int n
     (void)hipGetLastError();
     hipStream_t s = (hipStream_t)stream;
     const unsigned grid = (unsigned)(BH * qtiles);
-    if (d == 128) svla_softmax_fwd<128><<<grid, kSmThreads, 0, s>>>(a);
-    else svla_softmax_fwd<64><<<grid, kSmThreads, 0, s>>>(a);
+    if (d == 128) svla_softmax_fwd<128><<<grid, kSmThreads, sm_lds_bytes<128>(), s>>>(a);
+    else svla_softmax_fwd<64><<<grid, kSmThreads, sm_lds_bytes<64>(), s>>>(a);
     return hipGetLastError() == hipSuccess ? SVLA_OK : SVLA_ERR_HIP;
 }
