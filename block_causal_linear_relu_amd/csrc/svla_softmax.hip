@@ -12,7 +12,7 @@
 // Workgroup = (b,h, tile of 128 queries), four waves of 32 queries each; the
 // tiles are launched heaviest first (the last query tiles see the most keys).
 // The keys stream through two LDS stages in tiles of 64; each tile's K and V
-// are loaded into registers two tiles ahead and staged one tile ahead.  Per 32-key half, on
+// are loaded into registers one tile ahead.  Per 32-key half, on
 // v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T   rows = keys, columns = queries: the K tile is the A operand
 //                 (16-byte LDS reads of its rows), the wave's Q rows the B
@@ -28,7 +28,9 @@
 //                 query per output tile (two 16-byte stores at the end).
 // Online softmax in base 2 (logits scaled by scale * log2 e): running max m
 // and per-lane partial sum l per query; the accumulator is rescaled only when
-// some query of the wave raised its max.  Keys past a query's visible range
+// some query of the wave raised its max.  The weights use the hardware's
+// 2^x (v_exp_f32) directly: its arguments are <= 0, and a weight below 2^-126
+// (flushed to zero) is below bf16's resolution of the sum it enters.  Keys past a query's visible range
 // (only in the last tiles of a workgroup) get weight zero.
 #include <hip/hip_runtime.h>
 
@@ -38,6 +40,10 @@
 #include <string.h>
 
 #include "../../include/svla.h"
+
+#ifndef SVLA_SM_WAVES
+#define SVLA_SM_WAVES 2            // waves per SIMD the register allocation must allow
+#endif
 
 namespace {
 
@@ -99,7 +105,7 @@ struct SmTile {                                 // one key tile's K and V chunks
 };
 
 template <int D>
-__global__ void __launch_bounds__(kSmThreads)
+__global__ void __launch_bounds__(kSmThreads, SVLA_SM_WAVES)
 svla_softmax_fwd(const SoftmaxArgs a)
 {
     constexpr int KK = D / 16;                 // 16-feature steps of the logit product
@@ -185,11 +191,10 @@ svla_softmax_fwd(const SoftmaxArgs a)
         }
     };
 
-    // the first two key tiles' loads, then the wave's Q rows (B operand of
+    // the first key tile's loads, then the wave's Q rows (B operand of
     // S^T = K Q^T, 16 features per step), held for the whole kernel
-    SmTile<D> ra, rb;
+    SmTile<D> ra;
     issue(ra, 0);
-    issue(rb, 1);
     u32x4_t qv[KK];
     {
         const uint32_t off = qrow < a.Nq ? (uint32_t)qrow * D * 2 : kSmOOB;
@@ -224,34 +229,37 @@ svla_softmax_fwd(const SoftmaxArgs a)
                                                                 s[hf], 0, 0, 0);
             }
         }
-        // scale, mask, running max
-        const bool masked = k0 + kKTile > kmin;
+        // mask, running max (of the raw logits: the scale is positive, so it
+        // is applied once, inside the exponent's fused multiply-add)
+        if (k0 + kKTile > kmin) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * hf + 8 * (r >> 2) + 4 * h + (r & 3);
+                    s[hf][r] = key < lim ? s[hf][r] : -INFINITY;
+                }
+        }
         float tmax = -INFINITY;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = s[hf][r] * a.c2;
-                if (masked) {
-                    const int key = k0 + 32 * hf + 8 * (r >> 2) + 4 * h + (r & 3);
-                    x = key < lim ? x : -INFINITY;
-                }
-                s[hf][r] = x;
-                tmax = fmaxf(tmax, x);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[hf][r]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.c2;
         const float mnew = fmaxf(mrun, tmax);
         const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(mrun - muse);
+        const float alpha = __builtin_amdgcn_exp2f(mrun - muse);
         mrun = mnew;
-        // the weights, their sum, and P as bf16 (the B operand of O^T += V^T P^T)
+        // the weights 2^(c2 s - m), their sum, and P as bf16 (the B operand of
+        // O^T += V^T P^T)
         unsigned int pw[2][8];
         float psum = 0.f;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float p0 = exp2f(s[hf][r] - muse), p1 = exp2f(s[hf][r + 1] - muse);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[hf][r], a.c2, -muse));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[hf][r + 1], a.c2, -muse));
                 psum += p0 + p1;
                 pw[hf][r / 2] = sm_pack_bf16(p0, p1);
             }
@@ -283,27 +291,16 @@ svla_softmax_fwd(const SoftmaxArgs a)
                 }
             }
     };
-    // Tile t's loads go to register set t % 2 (ra even, rb odd) and are staged
-    // into LDS stage t % 2 during tile t - 1, after which the set is refilled
-    // with tile t + 2: two tiles of compute cover each load.  One barrier per
-    // tile: it publishes the staged tile and frees the stage just read.
-    if (ntiles > 0) {
-        stage(ra, 0);
-        issue(ra, 2);
+    // Tile t is loaded into registers during tile t - 1 and staged into LDS
+    // stage t % 2 at the start of its own turn; one barrier per tile publishes
+    // it, and (every wave having passed it only after its previous tile's
+    // work) frees the stage the next tile overwrites.
+    for (int it = 0; it < ntiles; ++it) {
+        stage(ra, it & 1);
+        issue(ra, it + 1);
         sm_lds_barrier();
-    }
-    for (int it = 0; it < ntiles; it += 2) {
-        stage(rb, 1);                         // tile it + 1 (zeros past the range)
-        issue(rb, it + 3);
-        __builtin_amdgcn_sched_barrier(0);    // those loads stay ahead of this tile's work
-        compute(it, 0);
-        sm_lds_barrier();
-        if (it + 1 >= ntiles) break;
-        stage(ra, 0);                         // tile it + 2
-        issue(ra, it + 4);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(it + 1, 1);
-        sm_lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);    // the next tile's loads stay ahead of this tile's work
+        compute(it, it & 1);
     }
     // O = acc / l: lane (n, h) holds features 32 t + 16 h + r of its query
     const float ltot = lsum + __shfl_xor(lsum, 32);
