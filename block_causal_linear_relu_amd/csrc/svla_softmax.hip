@@ -9,8 +9,9 @@
 // bf16 Q, K, V, O; fp32 logits, weights and sums.  The kernel is kept in a
 // source of its own.
 //
-// Workgroup = (b,h, tile of 128 queries), four waves of 32 queries each; the
-// tiles are launched heaviest first (the last query tiles see the most keys).
+// Workgroup = (b,h, tile of 32 W queries), W waves of 32 queries each (W = 8
+// at d = 128, 4 at d = 64); the tiles are launched heaviest first (the last
+// query tiles see the most keys).
 // The keys stream through two LDS stages in tiles of 64; each tile's K and V
 // are loaded into registers one tile ahead.  Per 32-key half, on
 // v_mfma_f32_32x32x16_bf16:
@@ -44,6 +45,9 @@
 #ifndef SVLA_SM_WAVES
 #define SVLA_SM_WAVES 2            // waves per SIMD the register allocation must allow
 #endif
+#ifndef SVLA_SM_W128
+#define SVLA_SM_W128 8             // waves per workgroup at d = 128 (32 queries each)
+#endif
 
 namespace {
 
@@ -52,8 +56,6 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
-constexpr int kSmThreads = 256;        // four waves
-constexpr int kQTile = 128;            // queries per workgroup (32 per wave)
 constexpr int kKTile = 64;             // keys per LDS tile
 constexpr uint32_t kSmOOB = 0x80000000u;
 
@@ -98,16 +100,23 @@ __device__ __forceinline__ void sm_lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Waves per workgroup (32 queries each): eight at d = 128, so a key tile
+// staged in LDS serves 256 queries; four at d = 64.
+template <int D>
+constexpr int sm_waves() { return D == 128 ? SVLA_SM_W128 : 4; }
+
 template <int D>
 struct SmTile {                                 // one key tile's K and V chunks in registers
-    static constexpr int CPT = kKTile * D / 8 / kSmThreads;
+    static constexpr int CPT = kKTile * D / 8 / (64 * sm_waves<D>());
     u32x4_t k[CPT], v[CPT];
 };
 
 template <int D>
-__global__ void __launch_bounds__(kSmThreads, SVLA_SM_WAVES)
+__global__ void __launch_bounds__(64 * sm_waves<D>(), SVLA_SM_WAVES)
 svla_softmax_fwd(const SoftmaxArgs a)
 {
+    constexpr int kSmThreads = 64 * sm_waves<D>();
+    constexpr int kQTile = 32 * sm_waves<D>();   // queries per workgroup
     constexpr int KK = D / 16;                 // 16-feature steps of the logit product
     constexpr int T = D / 32;                  // output tiles of 32 features
     constexpr int LDK = D + 8;                 // K tile row, bf16 elements
@@ -350,7 +359,8 @@ extern "C" svla_status svla_softmax_attention(svla_dtype dt, int B, int H, int n
     const size_t qb = (size_t)(BH * Nq * d * 2), kb = (size_t)(BH * Nk * d * 2);
     if (sm_overlap(O, qb, Q, qb) || sm_overlap(O, qb, K, kb) || sm_overlap(O, qb, V, kb))
         return SVLA_ERR_VALUE;
-    const int qtiles = (int)((Nq + kQTile - 1) / kQTile);
+    const int qtile = 32 * (d == 128 ? sm_waves<128>() : sm_waves<64>());
+    const int qtiles = (int)((Nq + qtile - 1) / qtile);
     if (BH * qtiles >= (1LL << 31)) return SVLA_ERR_SHAPE;
     SoftmaxArgs a;
     memset(&a, 0, sizeof a);
@@ -360,7 +370,7 @@ extern "C" svla_status svla_softmax_attention(svla_dtype dt, int B, int H, int n
     (void)hipGetLastError();
     hipStream_t s = (hipStream_t)stream;
     const unsigned grid = (unsigned)(BH * qtiles);
-    if (d == 128) svla_softmax_fwd<128><<<grid, kSmThreads, sm_lds_bytes<128>(), s>>>(a);
-    else svla_softmax_fwd<64><<<grid, kSmThreads, sm_lds_bytes<64>(), s>>>(a);
+    if (d == 128) svla_softmax_fwd<128><<<grid, 64 * sm_waves<128>(), sm_lds_bytes<128>(), s>>>(a);
+    else svla_softmax_fwd<64><<<grid, 64 * sm_waves<64>(), sm_lds_bytes<64>(), s>>>(a);
     return hipGetLastError() == hipSuccess ? SVLA_OK : SVLA_ERR_HIP;
 }
