@@ -389,6 +389,17 @@ __device__ __forceinline__ double rope_freq(double f, double q, int m)
     return f;
 }
 
+// (cos, sin) of pair m at position pos: the angle in turns reduced in fp64,
+// then an fp32 sin/cos of pi times twice the fraction.
+__device__ __forceinline__ float2 rope_cs(double freq0, double ratio, int pos, int m)
+{
+    double turns = (double)pos * rope_freq(freq0, ratio, m);
+    turns -= floor(turns);
+    float s, c;
+    sincospif(2.0f * (float)turns, &s, &c);
+    return make_float2(c, s);
+}
+
 __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
 {
     const int pt = r.dt / 2, ph = r.dh / 2;
@@ -409,13 +420,118 @@ __device__ void rope_fill(float2 *tab, const RopeK &r, int f0, int nf)
             const int x = e - nT - nH; m = x / r.gw; pos = x - m * r.gw; a = 2;
         }
         const double fa = a == 0 ? fT : a == 1 ? fH : fW, qa = a == 0 ? qT : a == 1 ? qH : qW;
-        double turns = (double)pos * rope_freq(fa, qa, m);
-        turns -= floor(turns);
-        float s, c;
-        sincospif(2.0f * (float)turns, &s, &c);
-        tab[e] = make_float2(c, s);
+        tab[e] = rope_cs(fa, qa, pos, m);
     }
     if (threadIdx.x == 0) tab[total] = make_float2(1.f, 0.f);   // identity, for unrotated dims
+}
+
+// Table of the one-launch step: the same angles with the pair index fastest,
+// [nf frames][dt/2 pairs], then [gh rows][dh/2 pairs], then [gw columns][dw/2
+// pairs], then two identity entries.  With dt, dh and dw multiples of 4, the
+// two pairs of a 4-feature group belong to one axis and are one 16-byte read.
+__device__ void gtab_fill(float2 *tab, const RopeK &r, int nf)
+{
+    const int pt = r.dt / 2, ph = r.dh / 2, pw = r.dw / 2;
+    const int nT = nf * pt, nH = r.gh * ph, total = nT + nH + r.gw * pw;
+    const double fT = sreg_f64(r.freq0[0]), fH = sreg_f64(r.freq0[1]), fW = sreg_f64(r.freq0[2]);
+    const double qT = sreg_f64(r.ratio[0]), qH = sreg_f64(r.ratio[1]), qW = sreg_f64(r.ratio[2]);
+    for (int e = threadIdx.x; e < total; e += blockDim.x) {
+        int pos, m, a;
+        if (e < nT) {
+            pos = e / pt; m = e - pos * pt; pos += r.t0; a = 0;
+        } else if (e < nT + nH) {
+            const int x = e - nT; pos = x / ph; m = x - pos * ph; a = 1;
+        } else {
+            const int x = e - nT - nH; pos = x / pw; m = x - pos * pw; a = 2;
+        }
+        const double fa = a == 0 ? fT : a == 1 ? fH : fW, qa = a == 0 ? qT : a == 1 ? qH : qW;
+        tab[e] = rope_cs(fa, qa, pos, m);
+    }
+    if (threadIdx.x < 2) tab[total + threadIdx.x] = make_float2(1.f, 0.f);
+}
+
+// LDS byte offset of a lane's two 4-feature groups (features 8 c + 4 G .. + 3
+// of chunk c) for a token at (frame, row, column): base + frame st + row sh +
+// column sw, at most one of st, sh, sw nonzero (none: the identity entries).
+struct GroupAddr {
+    int base[2], st[2], sh[2], sw[2];
+};
+
+__device__ __forceinline__ GroupAddr gtab_groups(const RopeK &r, int chunk, int nf)
+{
+    GroupAddr g;
+    const int pt = r.dt / 2, ph = r.dh / 2, pw = r.dw / 2;
+    const int offH = nf * pt, offW = offH + r.gh * ph, offI = offW + r.gw * pw;
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+        const int P = 4 * chunk + 2 * G;           // the group's first pair
+        int e = offI, st = 0, sh = 0, sw = 0;
+        if (P < pt) {
+            e = P; st = pt;
+        } else if (P < pt + ph) {
+            e = offH + P - pt; sh = ph;
+        } else if (P < pt + ph + pw) {
+            e = offW + P - pt - ph; sw = pw;
+        }
+        g.base[G] = 8 * e; g.st[G] = 8 * st; g.sh[G] = 8 * sh; g.sw[G] = 8 * sw;
+    }
+    return g;
+}
+
+__device__ __forceinline__ int gtab_off(const GroupAddr &g, int G, int fr, int row, int col)
+{
+    return g.base[G] + fr * g.st[G] + row * g.sh[G] + col * g.sw[G];
+}
+
+// Rotate features x[0..3] (two pairs) by the group's (cos, sin, cos, sin).
+__device__ __forceinline__ void rot_group(float *x, const f32x4_t cs)
+{
+    const float x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+    x[0] = x0 * cs[0] - x1 * cs[1];
+    x[1] = x0 * cs[1] + x1 * cs[0];
+    x[2] = x2 * cs[2] - x3 * cs[3];
+    x[3] = x2 * cs[3] + x3 * cs[2];
+}
+
+// A lane's token walk through the grid: the token advances by a fixed count
+// (dF frames, dR < gh rows, dC < gw columns) per step, the row and column
+// carry, and the table offsets of the lane's two groups follow by adds: per
+// step k0, plus k1 when the column wraps, plus k2 when the row wraps.
+struct GroupWalk {
+    int off[2], k0[2], k1[2], k2[2];
+    int row, col, dR, dC, gh, gw;
+};
+
+__device__ __forceinline__ GroupWalk group_walk(const GroupAddr &g, const RopeK &r, uint32_t tok0, uint32_t step)
+{
+    GroupWalk w;
+    const uint32_t hw = (uint32_t)(r.gh * r.gw);
+    const uint32_t f0 = fdiv(tok0, r.div_hw), r0 = tok0 - f0 * hw, y0 = fdiv(r0, r.div_w);
+    const uint32_t df = fdiv(step, r.div_hw), dr = step - df * hw, dy = fdiv(dr, r.div_w);
+    w.row = (int)y0; w.col = (int)(r0 - y0 * (uint32_t)r.gw);
+    w.dR = (int)dy; w.dC = (int)(dr - dy * (uint32_t)r.gw);
+    w.gh = r.gh; w.gw = r.gw;
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+        w.off[G] = g.base[G] + (int)f0 * g.st[G] + w.row * g.sh[G] + w.col * g.sw[G];
+        w.k0[G] = (int)df * g.st[G] + w.dR * g.sh[G] + w.dC * g.sw[G];
+        w.k1[G] = g.sh[G] - r.gw * g.sw[G];
+        w.k2[G] = g.st[G] - r.gh * g.sh[G];
+    }
+    return w;
+}
+
+__device__ __forceinline__ void walk_step(GroupWalk &w)
+{
+    int c = w.col + w.dC;
+    const bool cc = c >= w.gw;
+    c = cc ? c - w.gw : c;
+    int r = w.row + w.dR + (cc ? 1 : 0);
+    const bool cr = r >= w.gh;
+    r = cr ? r - w.gh : r;
+    w.row = r; w.col = c;
+#pragma unroll
+    for (int G = 0; G < 2; ++G) w.off[G] += w.k0[G] + (cc ? w.k1[G] : 0) + (cr ? w.k2[G] : 0);
 }
 
 // Per-thread description of the 4 (bf16 chunk) or 2 (fp32 chunk) pairs of
@@ -2140,8 +2256,8 @@ svla_apply_f32(const ApplyArgs a)
 
 // ---------------------------------------------------------------------------
 // svla_step_fused: a one-block call (a block step, or a non-causal call over
-// a short sequence) of bf16 inputs at d = 32 in one launch, with no hand-off
-// between workgroups.
+// a short sequence) of bf16 or fp8 inputs at d = 32 in one launch, with no
+// hand-off between workgroups.
 //
 // Workgroup = (bh, tile t), `tiles` workgroups per (bh), all on one XCD (the
 // tiles of a bh are 8 workgroup ids apart and the dispatch is round-robin over
@@ -2154,18 +2270,27 @@ svla_apply_f32(const ApplyArgs a)
 // workgroup of a launch reads memory that another one writes, and nothing
 // waits on another workgroup.
 //
-// Build: W waves, wave w takes every W-th 16-token stage of the block (one
-// token row chunk of 16 bytes per lane and tensor, PF stages of K/V loads in
-// flight in registers); phi (and with RoPE the rotation, the key split into
-// bf16 hi + lo) is applied in registers, the stage goes through a
-// wave-private LDS slot, and the token contraction runs on
-// v_mfma_f32_32x32x16_bf16 from transposing reads; z sums the unrotated
-// phi(k) on the vector ALU.  The W tiles are summed in wave order.
+// Order: every wave issues the K/V loads of its first 16-token stage, the
+// RoPE table is filled (the one barrier before the build), then the other
+// prefetched stages, the tile's Q rows and the carried state are issued, so
+// the build starts while the loads still stream in.
+//
+// Build: W waves, wave w takes stages w, w + W, ... of the block (one token
+// row chunk of 16 bytes per lane and tensor, PF stages in flight in
+// registers, exactly the stages the wave owns); phi (and with RoPE the
+// rotation, the key split into bf16 hi + lo) is applied in registers, the
+// stage goes through a wave-private LDS slot, and the token contraction runs
+// on v_mfma_f32_32x32x16_bf16 from transposing reads; z sums the unrotated
+// phi(k) on the vector ALU.  A lane's token advances by 16 W per stage, so its
+// grid position is stepped with carries instead of divided out, and its two
+// 4-feature groups read their (cos, sin) pairs as two 16-byte entries.
+// Epilogue: each wave stores its 32x32 tile and its z sums (reduced across
+// the wave by DPP and lane swaps) in an LDS area of its own, so it does not
+// wait for the other waves' stage slots; after one barrier thread e sums
+// element e of the W tiles in wave order, adds the decayed carried state and
+// writes a transposed copy for the read-out (tile 0 also the new state).
 // Read-out: O^T = S^T phi~(Q)^T on v_mfma_f32_16x16x32_bf16 with the state
-// as the A operand in registers; the tile's Q groups (wave w: groups w,
-// w + W, ..., at most QG) are loaded into registers right after the first K/V
-// stages, so they arrive while the state is built.  The RoPE table covers the
-// whole block and serves both halves.
+// as the A operand in registers.
 // ---------------------------------------------------------------------------
 struct StepArgs {
     const void *Q, *K, *V;
@@ -2175,11 +2300,32 @@ struct StepArgs {
     float *S_out, *z_out;          // new state or null
     int n;                         // tokens of the block
     int tiles, tile;               // workgroups per bh, tokens per workgroup (multiple of 16)
-    int work_bytes;                // dynamic LDS: stage slots / epilogue, after the RoPE table
+    int work_bytes;                // dynamic LDS after the RoPE table (stage slots, tiles, state)
     long BH;
     float eps;
     RopeK rope;
 };
+
+// Sum over the lanes of a wave that share lane % 4: rotations by 4 and 8
+// inside each row of 16 lanes, then swaps of rows and of halves.
+__device__ __forceinline__ float wave_sum_mod4(float v)
+{
+    v += as_f32((unsigned int)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), 0x124, 0xF, 0xF, false));
+    v += as_f32((unsigned int)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), 0x128, 0xF, 0xF, false));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
+    v = as_f32(r16[0]) + as_f32(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+    return as_f32(r32[0]) + as_f32(r32[1]);
+}
+
+// LDS bytes of the one-launch step after the RoPE table: W stage slots, W
+// tiles of 32 x 32 floats, W z sums, the transposed state and z.
+constexpr int fused_slot_bytes(bool rope) { return (rope ? 3 : 2) * 1024; }
+constexpr int kFusedSLD = 36;                 // row stride (floats) of the transposed state
+constexpr int fused_work_bytes(bool rope, int W)
+{
+    return W * fused_slot_bytes(rope) + W * 4096 + W * 128 + (32 * kFusedSLD + 32) * 4;
+}
 
 template <bool ROPE, int W, int PF, int QG, int IN = 2>
 __global__ void __launch_bounds__(64 * W)
@@ -2190,7 +2336,11 @@ svla_step_fused(const StepArgs a)
     constexpr int TILEB = 16 * ROWB;      // one 16-token stage of one tensor
     constexpr int NK = ROPE ? 2 : 1;      // K tiles per stage: (rotated) hi, lo
     constexpr int SLOTB = (NK + 1) * TILEB;
-    static_assert(2 * PF + QG < 64, "the loads issued together must fit the vmcnt counter");
+    constexpr int SLD = kFusedSLD;
+    constexpr int EPT = 1024 / (64 * W);  // state elements per thread in the epilogue
+    static_assert(SLOTB == fused_slot_bytes(ROPE), "slot size");
+    static_assert(16 % W == 0, "W divides 16");
+    static_assert(2 * PF + QG + EPT + 1 < 64, "the loads issued together must fit the vmcnt counter");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -2210,12 +2360,14 @@ svla_step_fused(const StepArgs a)
     const auto rQ = make_rsrc((const char *)a.Q + bh * islice, islice);
     const auto rO = make_rsrc((char *)a.O + bh * slice, slice);
 
-    float2 *tab = (float2 *)lds;
+    unsigned char *tabp = lds;
     unsigned char *work = lds + (ROPE ? a.rope.tab_bytes : 0);
-    float *st = (float *)(work + a.work_bytes);           // the new state, S[k][v] then z
+    float *red = (float *)(work + W * SLOTB);              // W tiles, [c][lane][4] each
+    float *zred = red + W * 1024;                          // W x D z sums
+    float *stT = zred + W * D;                             // S^T [v][SLD], then z
 
-    // 1. the first PF stages of K and V: stage st = wave + W i; lane -> row
-    // lane / 4 of the stage, chunk lane % 4
+    // 1. the K/V loads of this wave's first stage: stage st = wave + W i;
+    // lane -> row lane / 4 of the stage, chunk lane % 4
     const int row = lane >> 2, q = lane & 3;
     const int nst = (n + 15) / 16;
     const int nw = nst > wave ? (nst - wave + W - 1) / W : 0;
@@ -2224,15 +2376,26 @@ svla_step_fused(const StepArgs a)
         return t < n ? (uint32_t)(t * D + q * 8) * (uint32_t)IN : kOOB;
     };
     u32x4_t kreg[PF], vreg[PF];
+    kreg[0] = load8f<IN, 0>(rK, kv_off(0));
+    vreg[0] = load8f<IN, 0>(rV, kv_off(0));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. the RoPE table, frames of every row of the padded stages
+    const int nf = ROPE ? (16 * nst - 1) / (a.rope.gh * a.rope.gw) + 1 : 1;
+    if constexpr (ROPE) {
+        gtab_fill((float2 *)tabp, a.rope, nf);
+        lds_barrier();
+    }
+
+    // 3. the other prefetched stages, this wave's Q groups of the tile (in
+    // the read-out's operand layout: token lane % 16 of the group, features
+    // 8 (lane / 16) ..), the carried state elements of this thread
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
+    for (int p = 1; p < PF; ++p) {
         kreg[p] = load8f<IN, 0>(rK, kv_off(p));
         vreg[p] = load8f<IN, 0>(rV, kv_off(p));
         __builtin_amdgcn_sched_barrier(0);
     }
-    // 2. this wave's Q groups of the tile, in the read-out's operand layout
-    // (token lane % 16 of the group, features 8 (lane / 16) ..): issued now,
-    // after the first K/V stages, so they land while the state is built
     const int kg = lane >> 4, tl = lane & 15;
     u32x4_t qreg[QG];
 #pragma unroll
@@ -2241,127 +2404,120 @@ svla_step_fused(const StepArgs a)
         qreg[j] = load8f<IN, SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * kg) * (uint32_t)IN : kOOB);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 3. the carried state: thread -> S elements 4 tid .. (and z for tid < d / 4)
+    // element e = c 256 + l 4 + r' of the epilogue is register 4 c + r' of
+    // lane l of a tile: S[8 c + 4 (l / 32) + r'][l % 32]
+    auto elem_k = [](int e) { return 8 * (e >> 8) + 4 * ((e >> 7) & 1) + (e & 3); };
+    auto elem_v = [](int e) { return (e >> 2) & 31; };
     const float gb = a.g ? a.g[bh] : 1.f;
-    f32x4_t s_in = {0.f, 0.f, 0.f, 0.f}, z_in = {0.f, 0.f, 0.f, 0.f};
-    const int e0 = 4 * tid;
+    float s_in[EPT], z_in = 0.f;
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) s_in[u] = 0.f;
     if (a.S_in) {
-        if (e0 < D * D) s_in = *(const f32x4_t *)(a.S_in + bh * D * D + e0);
-        if (e0 < D) z_in = *(const f32x4_t *)(a.z_in + bh * D + e0);
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = tid + 64 * W * u;
+            s_in[u] = a.S_in[bh * D * D + elem_k(e) * D + elem_v(e)];
+        }
+        if (tid < D) z_in = a.z_in[bh * D + tid];
     }
 
-    // 4. the RoPE table of the whole block, while the loads are in flight
-    const int nf = ROPE ? (n - 1) / (a.rope.gh * a.rope.gw) + 1 : 1;
-    RopePairs<4> ppk;
-    if constexpr (ROPE) {
-        rope_fill(tab, a.rope, a.rope.t0, nf);
-        ppk = rope_pairs<4>(a.rope, q * 8, nf);
-        lds_barrier();
-    }
+    // RoPE: this lane's table groups, walked from its first token by 16 W
+    // tokens per stage
+    GroupWalk walk{};
+    if constexpr (ROPE) walk = group_walk(gtab_groups(a.rope, q, nf), a.rope, (uint32_t)(16 * wave + row), 16u * W);
     unsigned char *slot = work + wave * SLOTB;
 
-    // 5. the block's state
+    // 4. the block's state, this wave's stages
     f32x16_t acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     float zacc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zacc[e] = 0.f;
-    const int m = lane & 31, g = lane >> 5;
     const int fl = trb_offset<D>(lane, 0);
-    const int nwr = (nw + PF - 1) / PF * PF;
-    for (int i0 = 0; i0 < nwr; i0 += PF) {
+    // stage i (ring slot p = i % PF): phi, rotation, split, the slot, the
+    // refill with stage i + PF (past the wave's last stage: an offset out of
+    // range, read as zeros), the contraction
+    auto stage = [&](int i, u32x4_t &kr, u32x4_t &vr) {
+        float kf[8];
+        feat8<IN, true>(kr, kf);
 #pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int i = i0 + p;
-            float kf[8];
-            feat8<IN, true>(kreg[p], kf);
+        for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
+        if constexpr (ROPE) {
+            rot_group(kf, *(const f32x4_t *)(tabp + walk.off[0]));
+            rot_group(kf + 4, *(const f32x4_t *)(tabp + walk.off[1]));
+            walk_step(walk);
+            u32x4_t hi, lo;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) zacc[e] += kf[e];
-            if constexpr (ROPE) {
-                const int tok = 16 * (wave + W * i) + row;
-                rope_rotate<4>(kf, rope_pos((uint32_t)tok, 0, a.rope), ppk, tab);
-                u32x4_t hi, lo;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    hi[e] = pack_bf16(kf[2 * e], kf[2 * e + 1]);
-                    lo[e] = pack_bf16(kf[2 * e] - bf16lo(hi[e]), kf[2 * e + 1] - bf16hi(hi[e]));
-                }
-                *(u32x4_t *)(slot + row * ROWB + q * 16) = hi;
-                *(u32x4_t *)(slot + TILEB + row * ROWB + q * 16) = lo;
-            } else {
-                *(u32x4_t *)(slot + row * ROWB + q * 16) = bf16x8_of<IN, true>(kreg[p]);
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = pack_bf16(kf[2 * e], kf[2 * e + 1]);
+                lo[e] = pack_bf16(kf[2 * e] - bf16lo(hi[e]), kf[2 * e + 1] - bf16hi(hi[e]));
             }
-            *(u32x4_t *)(slot + NK * TILEB + row * ROWB + q * 16) = bf16x8_of<IN, false>(vreg[p]);
-            // refill this register slot with the stage PF ahead
-            __builtin_amdgcn_sched_barrier(0);
-            kreg[p] = load8f<IN, 0>(rK, kv_off(i + PF));
-            vreg[p] = load8f<IN, 0>(rV, kv_off(i + PF));
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8_t av = trb_load<D>(slot, fl);
-            const bf16x8_t bv = trb_load<D>(slot + NK * TILEB, fl);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
-            if constexpr (ROPE) {
-                const bf16x8_t al = trb_load<D>(slot + TILEB, fl);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc, 0, 0, 0);
-            }
+            *(u32x4_t *)(slot + row * ROWB + q * 16) = hi;
+            *(u32x4_t *)(slot + TILEB + row * ROWB + q * 16) = lo;
+        } else {
+            *(u32x4_t *)(slot + row * ROWB + q * 16) = bf16x8_of<IN, true>(kr);
         }
+        *(u32x4_t *)(slot + NK * TILEB + row * ROWB + q * 16) = bf16x8_of<IN, false>(vr);
+        __builtin_amdgcn_sched_barrier(0);
+        kr = load8f<IN, 0>(rK, kv_off(i + PF));
+        vr = load8f<IN, 0>(rV, kv_off(i + PF));
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8_t av = trb_load<D>(slot, fl);
+        const bf16x8_t bv = trb_load<D>(slot + NK * TILEB, fl);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+        if constexpr (ROPE) {
+            const bf16x8_t al = trb_load<D>(slot + TILEB, fl);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc, 0, 0, 0);
+        }
+    };
+    // whole rounds of PF stages (no exit inside a round, so every wait in the
+    // loop counts the same PF - 1 stages of loads behind it), then the rest
+    const int rounds = nw / PF;
+    for (int i0 = 0; i0 < rounds * PF; i0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) stage(i0 + p, kreg[p], vreg[p]);
     }
+#pragma unroll
+    for (int p = 0; p + 1 < PF; ++p)
+        if (rounds * PF + p < nw) stage(rounds * PF + p, kreg[p], vreg[p]);
 
-    // 6. the W tiles summed in a fixed order, plus the decayed carried state:
-    // with more than 8 waves, wave w + 8 first adds its tile into wave w's
-    // (through LDS), then the 8 tiles are summed in wave order
-    constexpr int WR = W > 8 ? 8 : W;           // tiles in the final sum
-    static_assert(W <= 16 && (W <= 8 || W == 16), "W = 1 .. 8 or 16");
-    float *red = (float *)work;                 // WR x D x D floats
-    float *zw = red + WR * D * D;               // W x D floats
-    auto tile_pos = [&](int r) { return (8 * (r >> 2) + 4 * g + (r & 3)) * D + m; };
-    __syncthreads();                            // every wave is done with its slot (and its loads)
-    if constexpr (W > 8) {
-        if (wave >= 8) {
+    // 5. this wave's tile and z sums into its own LDS area
+    {
+        f32x4_t *dst = (f32x4_t *)(red + wave * 1024) + lane;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[(wave - 8) * D * D + tile_pos(r)] = acc[r];
-        }
-        __syncthreads();
-        if (wave < 8) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] += red[wave * D * D + tile_pos(r)];
-        }
-        __syncthreads();
-    }
-    if (wave < WR) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[wave * D * D + tile_pos(r)] = acc[r];
+        for (int c = 0; c < 4; ++c)
+            dst[64 * c] = (f32x4_t){acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float v = zacc[e];
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        zacc[e] = v;
-    }
+    for (int e = 0; e < 8; ++e) zacc[e] = wave_sum_mod4(zacc[e]);
     if (lane < 4) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zw[wave * D + lane * 8 + e] = zacc[e];
+        f32x4_t *zd = (f32x4_t *)(zred + wave * D + 8 * lane);
+        zd[0] = (f32x4_t){zacc[0], zacc[1], zacc[2], zacc[3]};
+        zd[1] = (f32x4_t){zacc[4], zacc[5], zacc[6], zacc[7]};
     }
-    __syncthreads();
-    if (e0 < D * D) {
-        f32x4_t t = *(const f32x4_t *)(red + e0);
+    lds_barrier();
+
+    // 6. element e summed over the W tiles in wave order, plus the decayed
+    // carried state; the transposed copy for the read-out, the new state
 #pragma unroll
-        for (int w = 1; w < WR; ++w) t += *(const f32x4_t *)(red + w * D * D + e0);
-        const f32x4_t s = gb * s_in + t;
-        *(f32x4_t *)(st + e0) = s;
-        if (tile == 0 && a.S_out) *(f32x4_t *)(a.S_out + bh * D * D + e0) = s;
+    for (int u = 0; u < EPT; ++u) {
+        const int e = tid + 64 * W * u;
+        float t = red[e];
+#pragma unroll
+        for (int w = 1; w < W; ++w) t += red[w * 1024 + e];
+        const float s = gb * s_in[u] + t;
+        const int k = elem_k(e), v = elem_v(e);
+        stT[v * SLD + k] = s;
+        if (tile == 0 && a.S_out) a.S_out[bh * D * D + k * D + v] = s;
     }
-    if (e0 < D) {
-        f32x4_t t = *(const f32x4_t *)(zw + e0);
+    if (tid < D) {
+        float t = zred[tid];
 #pragma unroll
-        for (int w = 1; w < W; ++w) t += *(const f32x4_t *)(zw + w * D + e0);
-        const f32x4_t z = gb * z_in + t;
-        *(f32x4_t *)(st + D * D + e0) = z;
-        if (tile == 0 && a.z_out) *(f32x4_t *)(a.z_out + bh * D + e0) = z;
+        for (int w = 1; w < W; ++w) t += zred[w * D + tid];
+        const float z = gb * z_in + t;
+        stT[D * SLD + tid] = z;
+        if (tile == 0 && a.z_out) a.z_out[bh * D + tid] = z;
     }
     lds_barrier();
 
@@ -2369,18 +2525,21 @@ svla_step_fused(const StepArgs a)
     bf16x8_t sf[2];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
-        const int f = op_col(mi, tl);
-        u32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = pack_bf16(st[(8 * kg + 2 * e) * D + f], st[(8 * kg + 2 * e + 1) * D + f]);
+        const float *col = stT + op_col(mi, tl) * SLD + 8 * kg;
+        const f32x4_t lo = *(const f32x4_t *)col, hi = *(const f32x4_t *)(col + 4);
+        const u32x4_t w = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
+                           pack_bf16(hi[2], hi[3])};
         sf[mi] = __builtin_bit_cast(bf16x8_t, w);
     }
     float zf[8];
+    {
+        const f32x4_t z0 = *(const f32x4_t *)(stT + D * SLD + 8 * kg);
+        const f32x4_t z1 = *(const f32x4_t *)(stT + D * SLD + 8 * kg + 4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zf[e] = st[D * D + 8 * kg + e];
-    RopePairs<4> ppq;
-    if constexpr (ROPE) ppq = rope_pairs<4>(a.rope, 8 * kg, nf);
+        for (int e = 0; e < 4; ++e) { zf[e] = z0[e]; zf[4 + e] = z1[e]; }
+    }
+    GroupAddr gq{};
+    if constexpr (ROPE) gq = gtab_groups(a.rope, kg, nf);
 
     // 8. read-out of this wave's groups of the tile
     const int ngroups = t_hi > t_lo ? (t_hi - t_lo + 15) / 16 : 0;
@@ -2401,7 +2560,13 @@ svla_step_fused(const StepArgs a)
         float den = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) den = fmaf(pf[e], zf[e], den);
-        if constexpr (ROPE) rope_rotate<4>(pf, rope_pos((uint32_t)tok, 0, a.rope), ppq, tab);
+        if constexpr (ROPE) {
+            const uint32_t hw = (uint32_t)(a.rope.gh * a.rope.gw);
+            const uint32_t fr = fdiv((uint32_t)tok, a.rope.div_hw), rem = (uint32_t)tok - fr * hw;
+            const uint32_t rw = fdiv(rem, a.rope.div_w), cl = rem - rw * (uint32_t)a.rope.gw;
+            rot_group(pf, *(const f32x4_t *)(tabp + gtab_off(gq, 0, (int)fr, (int)rw, (int)cl)));
+            rot_group(pf + 4, *(const f32x4_t *)(tabp + gtab_off(gq, 1, (int)fr, (int)rw, (int)cl)));
+        }
         if constexpr (ROPE || IN != 2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) pq[e] = pack_bf16(pf[2 * e], pf[2 * e + 1]);
@@ -3410,8 +3575,11 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
               p->splits + 1 <= (p->rope.on ? kFoldMaxPartsRope : kFoldMaxParts);
     // the one-launch step: one block of bf16 or fp8 at d = 32, short enough for every
     // workgroup of a (b,h) to build the whole block state itself
+    // (with RoPE: axis widths that are multiples of 4, so each 4-feature group
+    // of the step's table reads lies on one axis)
     p->fused = (op == SVLA_OP_NONCAUSAL || op == SVLA_OP_BLOCK_CAUSAL || op == SVLA_OP_BLOCK_STEP) &&
-               p->esize <= 2 && d == 32 && nb == 1 && n > 0 && n <= SVLA_FUSED_MAX_N && p->BH > 0;
+               p->esize <= 2 && d == 32 && nb == 1 && n > 0 && n <= SVLA_FUSED_MAX_N && p->BH > 0 &&
+               (!p->rope.on || (p->rope.dt % 4 == 0 && p->rope.dh % 4 == 0 && p->rope.dw % 4 == 0));
     if (p->fused) {
         // at most one workgroup per CU: (a second round of workgroups would
         // repeat the whole build); at least one per (b,h)
@@ -3424,18 +3592,17 @@ svla_status make_plan(const char *fn, svla_op op, svla_dtype dt, int B, int H, i
         const int gpt = (int)((ngr + T - 1) / T);
         p->ftile = 16 * gpt;
         p->ftiles = (ngr + gpt - 1) / gpt;
-        const int slotb = (p->rope.on ? 3 : 2) * 1024;
-        const int epi = ((SVLA_FUSED_W > 8 ? 8 : SVLA_FUSED_W) * d * d + SVLA_FUSED_W * d) * 4;
-        p->fwork = SVLA_FUSED_W * slotb > epi ? SVLA_FUSED_W * slotb : epi;
+        p->fwork = fused_work_bytes(p->rope.on, SVLA_FUSED_W);
         p->ftab = 0;
         if (p->rope.on) {
-            const long nf = (n - 1) / ((long)p->rope.gh * p->rope.gw) + 1;
+            // frames of every row of the padded 16-token stages, two identity entries
+            const long nf = (16L * ngr - 1) / ((long)p->rope.gh * p->rope.gw) + 1;
             const long e = nf * (p->rope.dt / 2) + (long)p->rope.gh * (p->rope.dh / 2) +
-                           (long)p->rope.gw * (p->rope.dw / 2) + 1;
+                           (long)p->rope.gw * (p->rope.dw / 2) + 2;
             if (e > kMaxRopeEntries) p->fused = false;          // (the split build takes it)
             p->ftab = (int)((e * 8 + 255) & ~255L);
         }
-        p->lds_fused = (size_t)p->ftab + p->fwork + (d * d + d) * 4;   // (+ the static Q rows)
+        p->lds_fused = (size_t)p->ftab + p->fwork;
     }
     p->tile = (p->esize == 2 && d >= 64) ? SVLA_APPLY_TILE_LDS
               : d == 128 ? SVLA_APPLY_TILE128
@@ -3913,6 +4080,7 @@ const char *svla_status_string(svla_status s)
     case SVLA_ERR_WORKSPACE: return "SVLA_ERR_WORKSPACE";
     case SVLA_ERR_VALUE: return "SVLA_ERR_VALUE";
     case SVLA_ERR_HIP: return "SVLA_ERR_HIP";
+    default: break;
     }
     return "SVLA_ERR_UNKNOWN";
 }
