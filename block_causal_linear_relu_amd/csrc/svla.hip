@@ -62,7 +62,13 @@
 #define SVLA_MIN_SPLIT_ROPE 5      // builds with RoPE: tokens per split >= this * d
 #endif
 #ifndef SVLA_MIN_SPLIT_128
-#define SVLA_MIN_SPLIT_128 4       // d = 128 build without RoPE: tokens per split >= this * d
+#define SVLA_MIN_SPLIT_128 1       // d = 128 build without RoPE: tokens per split >= this * d
+#endif
+#ifndef SVLA_FOLD_MAX_PARTS
+#define SVLA_FOLD_MAX_PARTS 8      // one-block calls: partials the apply sums itself (no scan) at most
+#endif
+#ifndef SVLA_FOLD_MAX_PARTS_ROPE
+#define SVLA_FOLD_MAX_PARTS_ROPE 8 // ... with RoPE
 #endif
 #ifndef SVLA_ROPE_PF
 #define SVLA_ROPE_PF 3             // state build with RoPE: stages in flight per wave
@@ -119,7 +125,7 @@
 #define SVLA_TCONV_YAUX 2          // ... and of the Y stores (non-temporal)
 #endif
 #ifndef SVLA_FUSED_MAX_N
-#define SVLA_FUSED_MAX_N 2048      // one-launch block step (bf16, d = 32): longest block
+#define SVLA_FUSED_MAX_N 3072      // one-launch block step (bf16, d = 32): longest block
 #endif
 #ifndef SVLA_FUSED_WGS
 #define SVLA_FUSED_WGS 256         // ... workgroups per launch at most (one per CU), unless B*H is larger
@@ -131,7 +137,8 @@
 #define SVLA_FUSED_PF 3            // ... K/V stages in flight per wave
 #endif
 #ifndef SVLA_FUSED_QG
-#define SVLA_FUSED_QG 2            // ... Q groups of 16 tokens per wave (tile <= 16 * W * QG)
+#define SVLA_FUSED_QG 4            // ... Q groups of 16 tokens per wave at most (tile <= 16 * W * QG);
+                                   // tiles of up to 16 * W * 2 tokens take an instance with 2
 #endif
 #ifndef SVLA_BWD_HOLD_Q
 #define SVLA_BWD_HOLD_Q 1          // backward query side: state operands in registers (1) or LDS (0)
@@ -165,8 +172,8 @@ typedef __attribute__((ext_vector_type(2))) short i16x2_t;
 namespace {
 
 constexpr int kThreads = 256;                 // build and apply: 4 waves of 64
-constexpr int kFoldMaxParts = 6;              // partials a scan folded into the apply sums at most
-constexpr int kFoldMaxPartsRope = 8;          // ... with RoPE (block steps cut into more splits)
+constexpr int kFoldMaxParts = SVLA_FOLD_MAX_PARTS;           // partials a scan folded into the apply sums at most
+constexpr int kFoldMaxPartsRope = SVLA_FOLD_MAX_PARTS_ROPE;  // ... with RoPE (block steps cut into more splits)
 constexpr int kScanLongChain = 16;            // scan: blocks from which the chain is cut four ways
 constexpr uint32_t kOOB = 0x80000000u;        // an offset past every resource
 constexpr int kMaxRopeEntries = 4096;         // (cos, sin) pairs per workgroup
@@ -3462,10 +3469,13 @@ constexpr int rope_tokens(int d) { return rope_u(d) * 64 / ((d == 128 ? 64 : d) 
 // Splits of a block's tokens over workgroups: about `target` workgroups per
 // launch, but never fewer than min_per_d * d tokens per split, so the fp32
 // partial state (4 d^2 bytes) stays a small fraction of the K/V bytes it
-// summarises (1/8 at the default, 1/4 for the d = 128 build without RoPE,
-// whose workgroups take whole rows).  Measured: the build without RoPE runs
-// best with one or two long-lived workgroups per CU, the RoPE build with
-// many.
+// summarises (1/8 at the default).  The d = 128 build without RoPE takes
+// min_per_d = 1: with many blocks the target binds first (three splits per
+// block at 20 heads x 8 blocks), and a call with few blocks (a block step of
+// 20 heads) is bound by how many workgroups stream its K and V, not by the
+// partials' bytes (measured: 23.1 -> 13.6 us for the 1760-token gated step).
+// Measured: the build without RoPE runs best with one or two long-lived
+// workgroups per CU, the RoPE build with many.
 int pick_splits(long units, int n, int d, long target, int *chunk_out,
                 int min_per_d = SVLA_MIN_SPLIT_PER_D)
 {
@@ -3799,15 +3809,19 @@ void launch_fused(const Plan &p, const StepArgs &args, hipStream_t s)
     a.rope.tab_bytes = p.ftab;
     const unsigned grid = (unsigned)(8L * p.ftiles * ((p.BH + 7) / 8));
     constexpr int W = SVLA_FUSED_W, PF = SVLA_FUSED_PF, QG = SVLA_FUSED_QG;
+    // a tile of at most 2 groups per wave takes the instance with 2 Q
+    // registers (measured: the minute-long step is 1 % slower with 4)
+    const bool q2 = QG > 2 && p.ftile <= 16 * W * 2;
     char nm[96];
     snprintf(nm, sizeof nm, "void svla_step_fused<%s, %d, %d, %d, %d>", p.rope.on ? "true" : "false", W, PF,
-             QG, p.esize);
+             q2 ? 2 : QG, p.esize);
+    auto go = [&](auto k) { launch(k, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W); };
     if (p.esize == 2) {
-        if (p.rope.on) launch(svla_step_fused<true, W, PF, QG>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
-        else launch(svla_step_fused<false, W, PF, QG>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+        if (p.rope.on) q2 ? go(svla_step_fused<true, W, PF, 2>) : go(svla_step_fused<true, W, PF, QG>);
+        else q2 ? go(svla_step_fused<false, W, PF, 2>) : go(svla_step_fused<false, W, PF, QG>);
     } else {
-        if (p.rope.on) launch(svla_step_fused<true, W, PF, QG, 1>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
-        else launch(svla_step_fused<false, W, PF, QG, 1>, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W);
+        if (p.rope.on) q2 ? go(svla_step_fused<true, W, PF, 2, 1>) : go(svla_step_fused<true, W, PF, QG, 1>);
+        else q2 ? go(svla_step_fused<false, W, PF, 2, 1>) : go(svla_step_fused<false, W, PF, QG, 1>);
     }
 }
 

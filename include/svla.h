@@ -143,7 +143,7 @@ svla_status svla_workspace_size(svla_op op, svla_dtype dt, int B, int H,
  * memory, `len` bytes including the terminating zero): split count, tokens
  * per split, apply tile, workspace bytes, and for each kernel its name (as
  * profilers report it), grid, block and dynamic LDS ("kernels").  A one-block
- * call of bf16 at d = 32 up to 2048 tokens runs as one launch ("fused": true,
+ * call of bf16 at d = 32 up to 3072 tokens runs as one launch ("fused": true,
  * "step_tiles" workgroups of "step_tile" tokens per (b,h)) unless its new
  * state overlaps the state it reads; "in_place_kernels" then lists the launches
  * of that case.  Launches nothing.  SVLA_ERR_VALUE if the text does not fit. */
@@ -191,7 +191,7 @@ svla_status svla_block_causal_gated(svla_dtype dt, int B, int H, int nb, int n, 
  * denoising loop does before a block is final, or commit into the other of
  * two state buffers).  With RoPE, rope->t0 is the absolute frame index of
  * this block's first token.
- * Launches: bf16 at d = 32 with n <= 2048 and S_out/z_out sharing no byte
+ * Launches: bf16 at d = 32 with n <= 3072 and S_out/z_out sharing no byte
  * with S_in/z_in runs as one kernel (every workgroup of a (b,h) builds the
  * block state itself, nothing waits on another workgroup); otherwise, and
  * always when the new state overlaps the old one, a state build and a read-out

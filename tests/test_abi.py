@@ -167,9 +167,9 @@ def test_workspace_covers_every_plan():
         # as long as the block's splits fit the apply's partial count: the
         # minute-long block step does)
         if nb == 1 and d == 32:
-            # up to 2048 tokens: one launch, or (new state over the old one)
+            # up to 3072 tokens: one launch, or (new state over the old one)
             # build and apply
-            short = n <= 2048
+            short = n <= 3072
             key = "in_place_kernels" if short else "kernels"
             assert plain["fused"] is short and rot["fused"] is short
             assert [k["slot"] for k in plain[key]] == ["build", "apply"]

@@ -240,8 +240,11 @@ def test_chained_steps_equal_one_shot(svla, dtype, gate, d, with_rope, commit):
 @pytest.mark.parametrize("B,H,n,rope,gate", [
     (1, 3, 1, False, False),        # one token
     (1, 3, 15, True, True),         # less than one 16-token group
-    (2, 5, 2048, True, False),      # the longest one-launch block
-    (1, 2, 2049, True, True),       # one token longer: the two-kernel step
+    (2, 5, 2048, True, False),      # many tiles of few groups
+    (1, 70, 2640, False, True),     # the 720p step: four Q groups per wave
+    (1, 200, 3000, False, False),   # 200 heads, three tiles of up to four groups per wave
+    (2, 5, 3072, True, False),      # the longest one-launch block
+    (1, 2, 3073, True, True),       # one token longer: the two-kernel step
     (1, 70, 1170, True, True),      # the minute-long step's shape
     (3, 100, 333, False, True),     # 300 heads: one workgroup per head
     (1, 7, 512 * 5 + 17, False, False)])
