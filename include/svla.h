@@ -195,7 +195,8 @@ svla_status svla_block_causal_gated(svla_dtype dt, int B, int H, int nb, int n, 
  * with S_in/z_in runs as one kernel (every workgroup of a (b,h) builds the
  * block state itself, nothing waits on another workgroup); otherwise, and
  * always when the new state overlaps the old one, a state build and a read-out
- * that folds the scan in (two kernels; three for d >= 64 or fp32). */
+ * that folds the scan in (two kernels, for bf16 or fp8 at d = 32 whose block
+ * is cut into at most 7 splits; otherwise build, scan and read-out). */
 svla_status svla_block_step(svla_dtype dt, int B, int H, int n, int d,
                             const void *Q, const void *K, const void *V, void *O,
                             const float *S_in, const float *z_in,
