@@ -724,7 +724,8 @@ def measure(w: Workload, args, settle_s: float) -> dict:
     dur_s = kern[dominant] * 1e-3
     achieved = ab["per_launch"][dominant] / dur_s / 1e9
     kernel_full = {k["slot"]: k["name"] for k in plan["kernels"]}[dominant]
-    tag = w.name + ("_" + w.mode if (w.name == "c4" or w.stream_mode) else "") + ("_fp8" if w.cfg.dtype == "fp8" else "")
+    stream_tag = w.name == "c4" or (w.stream_mode and w.name in ("c3", "c5"))
+    tag = w.name + ("_" + w.mode if stream_tag else "") + ("_fp8" if w.cfg.dtype == "fp8" else "")
     ms = t["mean_ms"]
     path_gbps = ab["path"] / (ms * 1e-3) / 1e9
     mf = load_mfma(tag, kernel_full)

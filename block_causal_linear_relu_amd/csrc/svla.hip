@@ -136,6 +136,9 @@
 #ifndef SVLA_FUSED_PF
 #define SVLA_FUSED_PF 3            // ... K/V stages in flight per wave
 #endif
+#ifndef SVLA_FUSED_PRE
+#define SVLA_FUSED_PRE 2           // ... stages of K/V loads issued before the RoPE table is filled
+#endif
 #ifndef SVLA_FUSED_QG
 #define SVLA_FUSED_QG 4            // ... Q groups of 16 tokens per wave at most (tile <= 16 * W * QG);
                                    // tiles of up to 16 * W * 2 tokens take an instance with 2
@@ -2277,10 +2280,12 @@ svla_apply_f32(const ApplyArgs a)
 // workgroup of a launch reads memory that another one writes, and nothing
 // waits on another workgroup.
 //
-// Order: every wave issues the K/V loads of its first 16-token stage, the
-// RoPE table is filled (the one barrier before the build), then the other
-// prefetched stages, the tile's Q rows and the carried state are issued, so
-// the build starts while the loads still stream in.
+// Order: every wave issues the K/V loads of its first two 16-token stages,
+// the RoPE table is filled (the one barrier before the build), then the
+// third prefetched stage, the tile's Q rows and the carried state are
+// issued, so the build starts while the loads still stream in.  (Measured on
+// the minute-long step: one stage before the table 11.3 us, two 10.9, all
+// three 10.9; every prefetched load including Q before it was slower.)
 //
 // Build: W waves, wave w takes stages w, w + W, ... of the block (one token
 // row chunk of 16 bytes per lane and tensor, PF stages in flight in
@@ -2373,7 +2378,7 @@ svla_step_fused(const StepArgs a)
     float *zred = red + W * 1024;                          // W x D z sums
     float *stT = zred + W * D;                             // S^T [v][SLD], then z
 
-    // 1. the K/V loads of this wave's first stage: stage st = wave + W i;
+    // 1. the K/V loads of this wave's first PRE stages: stage st = wave + W i;
     // lane -> row lane / 4 of the stage, chunk lane % 4
     const int row = lane >> 2, q = lane & 3;
     const int nst = (n + 15) / 16;
@@ -2383,9 +2388,13 @@ svla_step_fused(const StepArgs a)
         return t < n ? (uint32_t)(t * D + q * 8) * (uint32_t)IN : kOOB;
     };
     u32x4_t kreg[PF], vreg[PF];
-    kreg[0] = load8f<IN, 0>(rK, kv_off(0));
-    vreg[0] = load8f<IN, 0>(rV, kv_off(0));
-    __builtin_amdgcn_sched_barrier(0);
+    constexpr int PRE = SVLA_FUSED_PRE < PF ? SVLA_FUSED_PRE : PF;   // stages issued before the table
+#pragma unroll
+    for (int p = 0; p < PRE; ++p) {
+        kreg[p] = load8f<IN, 0>(rK, kv_off(p));
+        vreg[p] = load8f<IN, 0>(rV, kv_off(p));
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     // 2. the RoPE table, frames of every row of the padded stages
     const int nf = ROPE ? (16 * nst - 1) / (a.rope.gh * a.rope.gw) + 1 : 1;
@@ -2398,7 +2407,7 @@ svla_step_fused(const StepArgs a)
     // the read-out's operand layout: token lane % 16 of the group, features
     // 8 (lane / 16) ..), the carried state elements of this thread
 #pragma unroll
-    for (int p = 1; p < PF; ++p) {
+    for (int p = PRE; p < PF; ++p) {
         kreg[p] = load8f<IN, 0>(rK, kv_off(p));
         vreg[p] = load8f<IN, 0>(rV, kv_off(p));
         __builtin_amdgcn_sched_barrier(0);

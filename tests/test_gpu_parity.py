@@ -265,6 +265,39 @@ def test_one_launch_step_sizes(svla, B, H, n, rope, gate):
     _check(x, (_np(O), S.cpu().numpy(), z.cpu().numpy()), ref)
 
 
+@pytest.mark.parametrize("H,n,d,gate,commit,slots", [
+    # the 720p step committed in place: build, then a read-out that sums the
+    # block's six split partials and the carried state itself (7 partials)
+    (70, 2640, 32, False, "in_place", ["build", "apply"]),
+    # the same into a second buffer: one launch, four Q groups per wave
+    (70, 2640, 32, True, "double_buffer", ["step"]),
+    # the gated d = 128 step: ten 192-token splits, scanned, read out
+    (20, 1760, 128, True, "in_place", ["build", "scan", "apply"]),
+    (20, 1760, 128, True, "double_buffer", ["build", "scan", "apply"])])
+def test_block_step_at_workload_shapes(svla, H, n, d, gate, commit, slots):
+    """One block step at the 720p (d = 32) and gated 2.0 (d = 128) block
+    shapes, with a carried state, against the oracle; the launch plan is the
+    one the shape is meant to take."""
+    x = _small("bf16", 1, H, 1, n, d, seed=31)
+    rng = np.random.default_rng(32)
+    S_in = (rng.standard_normal((1, H, d, d)) * 20).astype(np.float32)
+    z_in = np.abs(rng.standard_normal((1, H, d)) * 80).astype(np.float32)
+    g = rng.uniform(0.3, 1.0, (1, H)).astype(np.float32) if gate else None
+    plan = svla.describe("block_step", torch.bfloat16, 1, H, 1, n, d)
+    key = "in_place_kernels" if (commit == "in_place" and plan.get("fused")) else "kernels"
+    assert [k["slot"] for k in plan[key]] == slots, plan
+    Q, K, V = (_t(x[k], torch.bfloat16) for k in "QKV")
+    S, z = _t(S_in, torch.float32), _t(z_in, torch.float32)
+    gt = None if g is None else _t(g, torch.float32)
+    if commit == "in_place":
+        O, S_o, z_o = svla.block_step(Q, K, V, S, z, S_out=S, z_out=z, g=gt)
+    else:
+        O, S_o, z_o = svla.block_step(Q, K, V, S, z, g=gt)
+    torch.cuda.synchronize()
+    ref = oracle.step(x["Q"], x["K"], x["V"], S_in, z_in, g=g, eps=x["eps"])
+    _check(x, (_np(O), S_o.cpu().numpy(), z_o.cpu().numpy()), ref)
+
+
 def test_step_without_commit_leaves_state(svla):
     """S_out != S_in: a denoising loop can evaluate a block several times."""
     x = _small("bf16", 1, 2, 1, 300, 32)
