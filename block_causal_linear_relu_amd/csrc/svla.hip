@@ -134,10 +134,16 @@
 #define SVLA_FUSED_W 16            // ... waves per workgroup
 #endif
 #ifndef SVLA_FUSED_PF
-#define SVLA_FUSED_PF 3            // ... K/V stages in flight per wave
+#define SVLA_FUSED_PF 3            // ... K/V stages in flight per wave (without RoPE)
+#endif
+#ifndef SVLA_FUSED_PF_ROPE
+#define SVLA_FUSED_PF_ROPE 2       // ... and with RoPE
 #endif
 #ifndef SVLA_FUSED_PRE
 #define SVLA_FUSED_PRE 2           // ... stages of K/V loads issued before the RoPE table is filled
+#endif
+#ifndef SVLA_FUSED_QLATE
+#define SVLA_FUSED_QLATE 0         // ... Q rows issued after the build (1) or after the RoPE table (0)
 #endif
 #ifndef SVLA_FUSED_QG
 #define SVLA_FUSED_QG 4            // ... Q groups of 16 tokens per wave at most (tile <= 16 * W * QG);
@@ -2280,12 +2286,17 @@ svla_apply_f32(const ApplyArgs a)
 // workgroup of a launch reads memory that another one writes, and nothing
 // waits on another workgroup.
 //
-// Order: every wave issues the K/V loads of its first two 16-token stages,
-// the RoPE table is filled (the one barrier before the build), then the
-// third prefetched stage, the tile's Q rows and the carried state are
-// issued, so the build starts while the loads still stream in.  (Measured on
-// the minute-long step: one stage before the table 11.3 us, two 10.9, all
-// three 10.9; every prefetched load including Q before it was slower.)
+// Order: every wave issues the K/V loads of its first PRE (2) 16-token
+// stages, the RoPE table is filled (the one barrier before the build), then
+// the other prefetched stages, the tile's Q rows and the carried state are
+// issued, so the build starts while the loads still stream in.  With RoPE
+// two stages are in flight per wave, without it three.  (Measured on the
+// minute-long step, us per step: 3 in flight with 1 before the table 11.3,
+// with 2 10.9, with 3 10.9; 2 in flight with 2 before the table 10.5, with
+// 1 10.8; 1 in flight 11.0; 4 in flight 11.4 - 11.5; every prefetched load
+// including Q before the table was slower, and so was Q issued only after
+// the build, 10.7.  On the 720p step without RoPE, 3 in flight beat 2 by
+// 1.5 %.)
 //
 // Build: W waves, wave w takes stages w, w + W, ... of the block (one token
 // row chunk of 16 bytes per lane and tensor, PF stages in flight in
@@ -2414,12 +2425,15 @@ svla_step_fused(const StepArgs a)
     }
     const int kg = lane >> 4, tl = lane & 15;
     u32x4_t qreg[QG];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int j = 0; j < QG; ++j) {
-        const int tok = t_lo + 16 * (wave + W * j) + tl;
-        qreg[j] = load8f<IN, SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * kg) * (uint32_t)IN : kOOB);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < QG; ++j) {
+            const int tok = t_lo + 16 * (wave + W * j) + tl;
+            qreg[j] = load8f<IN, SVLA_Q_AUX>(rQ, tok < t_hi ? (uint32_t)(tok * D + 8 * kg) * (uint32_t)IN : kOOB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (!SVLA_FUSED_QLATE) load_q();
     // element e = c 256 + l 4 + r' of the epilogue is register 4 c + r' of
     // lane l of a tile: S[8 c + 4 (l / 32) + r'][l % 32]
     auto elem_k = [](int e) { return 8 * (e >> 8) + 4 * ((e >> 7) & 1) + (e & 3); };
@@ -2497,6 +2511,8 @@ svla_step_fused(const StepArgs a)
 #pragma unroll
     for (int p = 0; p + 1 < PF; ++p)
         if (rounds * PF + p < nw) stage(rounds * PF + p, kreg[p], vreg[p]);
+
+    if constexpr (SVLA_FUSED_QLATE) load_q();
 
     // 5. this wave's tile and z sums into its own LDS area
     {
@@ -3817,19 +3833,19 @@ void launch_fused(const Plan &p, const StepArgs &args, hipStream_t s)
     a.rope = p.rope;
     a.rope.tab_bytes = p.ftab;
     const unsigned grid = (unsigned)(8L * p.ftiles * ((p.BH + 7) / 8));
-    constexpr int W = SVLA_FUSED_W, PF = SVLA_FUSED_PF, QG = SVLA_FUSED_QG;
+    constexpr int W = SVLA_FUSED_W, PF = SVLA_FUSED_PF, PFR = SVLA_FUSED_PF_ROPE, QG = SVLA_FUSED_QG;
     // a tile of at most 2 groups per wave takes the instance with 2 Q
     // registers (measured: the minute-long step is 1 % slower with 4)
     const bool q2 = QG > 2 && p.ftile <= 16 * W * 2;
     char nm[96];
-    snprintf(nm, sizeof nm, "void svla_step_fused<%s, %d, %d, %d, %d>", p.rope.on ? "true" : "false", W, PF,
-             q2 ? 2 : QG, p.esize);
+    snprintf(nm, sizeof nm, "void svla_step_fused<%s, %d, %d, %d, %d>", p.rope.on ? "true" : "false", W,
+             p.rope.on ? PFR : PF, q2 ? 2 : QG, p.esize);
     auto go = [&](auto k) { launch(k, grid, p.lds_fused, s, SLOT_STEP, a, nm, 64 * W); };
     if (p.esize == 2) {
-        if (p.rope.on) q2 ? go(svla_step_fused<true, W, PF, 2>) : go(svla_step_fused<true, W, PF, QG>);
+        if (p.rope.on) q2 ? go(svla_step_fused<true, W, PFR, 2>) : go(svla_step_fused<true, W, PFR, QG>);
         else q2 ? go(svla_step_fused<false, W, PF, 2>) : go(svla_step_fused<false, W, PF, QG>);
     } else {
-        if (p.rope.on) q2 ? go(svla_step_fused<true, W, PF, 2, 1>) : go(svla_step_fused<true, W, PF, QG, 1>);
+        if (p.rope.on) q2 ? go(svla_step_fused<true, W, PFR, 2, 1>) : go(svla_step_fused<true, W, PFR, QG, 1>);
         else q2 ? go(svla_step_fused<false, W, PF, 2, 1>) : go(svla_step_fused<false, W, PF, QG, 1>);
     }
 }
