@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of block-causal ReLU linear attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4|c2|c3|c5]
-                    [--c4-mode both|stream|oneshot] [--inplace] [--rotate R] [--settle S]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4|c2|c3|c5|t3|t4]
+                    [--c4-mode both|stream|oneshot] [--inplace] [--stream] [--dtype fp8]
+                    [--backward] [--anchor] [--rotate R] [--settle S] [--no-cpu-baseline]
 
 A step is one pass of the whole path over one batch of the workload's
 synthetic input, with the inputs resident in HBM.  R copies of the inputs and
@@ -957,6 +957,10 @@ def main():
     from workloads import CONFIGS, make_inputs, scaled_config
     if args.dtype == "fp8" and CONFIGS[args.config].d != 32:
         print("bench.py: fp8 inputs are for the d = 32 workloads", file=sys.stderr)
+        sys.exit(2)
+    if args.stream and args.config not in ("c3", "c5"):
+        print("bench.py: --stream is for c3 and c5 (c4 takes --c4-mode; c2 is one block)",
+              file=sys.stderr)
         sys.exit(2)
     x = make_inputs(scaled_config(CONFIGS[args.config], dtype=args.dtype))
     c4 = args.config == "c4"
