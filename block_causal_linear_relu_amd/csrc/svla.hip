@@ -152,6 +152,9 @@
 #ifndef SVLA_BWD_HOLD_Q
 #define SVLA_BWD_HOLD_Q 1          // backward query side: state operands in registers (1) or LDS (0)
 #endif
+#ifndef SVLA_BWD_BF16
+#define SVLA_BWD_BF16 1            // backward query side, bf16 inputs at d = 32: bf16 hi + lo products
+#endif
 #ifndef SVLA_BWD_WGS
 #define SVLA_BWD_WGS 2048          // backward query/key kernels: workgroups wanted per launch
 #endif
@@ -2814,8 +2817,11 @@ svla_temporal_conv_k(const ConvArgs a)
 // Three kernels after the forward state is rebuilt (state build + export
 // scan): the query side (dq and each split's share of the sums of G and H),
 // the reverse scan over blocks (G_c, H_c, dS0, dz0) and the key side (dk,
-// dv, dg).  All arithmetic is fp32: every product over features or tokens
-// runs on v_mfma_f32_16x16x4f32.
+// dv, dg).  All sums are fp32.  Every product over features or tokens runs
+// on v_mfma_f32_16x16x4f32, except for bf16 inputs at d = 32: there the
+// fp32 operands are split into bf16 hi + lo and the products run on the
+// bf16 matrix instructions (hi hi + hi lo + lo hi, about 2^-16 relative; a
+// bf16 value's lo part is zero and its products are skipped).
 //
 // Lane layout of the per-token work: the kernels run on
 // v_mfma_f32_16x16x4f32 with the MFMA's output rows as features and its
@@ -2988,6 +2994,37 @@ struct StateOps {
     }
 };
 
+// An fp32 operand as bf16 hi + lo (hi = the value rounded to bf16, lo = the
+// remainder rounded to bf16): hi + lo keeps about 16 bits of the value, and a
+// product of two such operands taken as hi hi + hi lo + lo hi on the bf16
+// matrix instructions (exact products, fp32 sums) is accurate to about 2^-16
+// relative, against the bf16 output rounding of 2^-9.
+__device__ __forceinline__ void split_bf16x8(const float *x, bf16x8_t &hi, bf16x8_t &lo)
+{
+    u32x4_t h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
+        l[e] = pack_bf16(x[2 * e] - bf16lo(h[e]), x[2 * e + 1] - bf16hi(h[e]));
+    }
+    hi = __builtin_bit_cast(bf16x8_t, h);
+    lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void split_bf16x4(const float *x, i16x4_t &hi, i16x4_t &lo)
+{
+    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+    u32x2_t h, l;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        h[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
+        l[e] = pack_bf16(x[2 * e] - bf16lo(h[e]), x[2 * e + 1] - bf16hi(h[e]));
+    }
+    hi = __builtin_bit_cast(i16x4_t, h);
+    lo = __builtin_bit_cast(i16x4_t, l);
+}
+
 // Sum of x over the four lanes (q = 0..3) of a token.
 __device__ __forceinline__ float token_sum(float x)
 {
@@ -3060,6 +3097,26 @@ svla_bwd_query(const BwdArgs a)
     float zr[FPL];
 #pragma unroll
     for (int L = 0; L < FPL; ++L) zr[L] = zs[FPL * q + L];
+    // bf16 inputs at d = 32: the three products on the bf16 matrix
+    // instructions with hi + lo operands (split_bf16x8).  A lane's 8
+    // features are one k-group of v_mfma_f32_16x16x32_bf16 (k-slot i of lane
+    // group q is feature F(q, i), in A and B alike), and the state operand of
+    // tile t holds the same entries as the fp32 path's 8 steps.
+    constexpr bool BF = SVLA_BWD_BF16 && ES == 2 && D == 32;
+    bf16x8_t afh[BF ? T : 1], afl[BF ? T : 1], abh[BF ? T : 1], abl[BF ? T : 1];
+    if constexpr (BF) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float xf[8], xb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xf[i] = so.f(t, i);
+                xb[i] = so.b(t, i);
+            }
+            split_bf16x8(xf, afh[t], afl[t]);
+            split_bf16x8(xb, abh[t], abl[t]);
+        }
+    }
 
     f32x4_t dS[T][T];
 #pragma unroll
@@ -3098,11 +3155,23 @@ svla_bwd_query(const BwdArgs a)
         f32x4_t num[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) num[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF) {
+            bf16x8_t bh, bl;
+            split_bf16x8(pt, bh, bl);
 #pragma unroll
-        for (int st = 0; st < FPL; ++st)
+            for (int t = 0; t < T; ++t) {
+                // (without RoPE p~ = phi(q) is a bf16 value: its lo part vanishes)
+                num[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afh[t], bh, num[t], 0, 0, 0);
+                if constexpr (ROPE) num[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afh[t], bl, num[t], 0, 0, 0);
+                num[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afl[t], bh, num[t], 0, 0, 0);
+            }
+        } else {
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                num[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(so.f(t, st), pt[st], num[t], 0, 0, 0);
+            for (int st = 0; st < FPL; ++st)
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    num[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(so.f(t, st), pt[st], num[t], 0, 0, 0);
+        }
         const float den = token_sum(denp) + a.eps;
         const float inv = den != 0.f ? 1.f / den : 0.f;
         float dotp = 0.f;
@@ -3116,11 +3185,22 @@ svla_bwd_query(const BwdArgs a)
         f32x4_t dpt[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) dpt[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF) {
+            bf16x8_t bh, bl;
+            split_bf16x8(dn, bh, bl);
 #pragma unroll
-        for (int st = 0; st < FPL; ++st)
+            for (int t = 0; t < T; ++t) {
+                dpt[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abh[t], bh, dpt[t], 0, 0, 0);
+                dpt[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abh[t], bl, dpt[t], 0, 0, 0);
+                dpt[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abl[t], bh, dpt[t], 0, 0, 0);
+            }
+        } else {
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                dpt[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(so.b(t, st), dn[st], dpt[t], 0, 0, 0);
+            for (int st = 0; st < FPL; ++st)
+#pragma unroll
+                for (int t = 0; t < T; ++t)
+                    dpt[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(so.b(t, st), dn[st], dpt[t], 0, 0, 0);
+        }
         // the wave's token tile for p~^T dnum (4-float chunks of row r swapped
         // within their 16-float group by 4 ((r / 4) % 4): the 16 rows one
         // write instruction touches then cover all 64 banks)
@@ -3142,20 +3222,50 @@ svla_bwd_query(const BwdArgs a)
         }
         bwd_pack<D, ES>(pq.v, v);
         pq.off = off;
+        if constexpr (BF) {
+            // the group's 16 tokens as the k-slots of v_mfma_f32_16x16x16_bf16:
+            // lane (m, q) holds tokens 4 st + q, st < 4, of feature 16 t + m
+            float av[T][4], bv[T][4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int tt = 4 * st + q, swr = 4 * (st & 3);     // the swap of row tt
-            float av[T], bv[T];
+            for (int st = 0; st < 4; ++st) {
+                const int tt = 4 * st + q, swr = 4 * (st & 3);
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    av[t][st] = Pt[tt * LD + ((16 * t + m) ^ swr)];
+                    bv[t][st] = Dn[tt * LD + ((16 * t + m) ^ swr)];
+                }
+            }
+            i16x4_t ah[T], al[T], bh[T], bl[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                av[t] = Pt[tt * LD + ((16 * t + m) ^ swr)];
-                bv[t] = Dn[tt * LD + ((16 * t + m) ^ swr)];
+                split_bf16x4(av[t], ah[t], al[t]);
+                split_bf16x4(bv[t], bh[t], bl[t]);
             }
 #pragma unroll
             for (int i = 0; i < T; ++i)
 #pragma unroll
-                for (int j = 0; j < T; ++j)
-                    dS[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], dS[i][j], 0, 0, 0);
+                for (int j = 0; j < T; ++j) {
+                    dS[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah[i], bh[j], dS[i][j], 0, 0, 0);
+                    dS[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah[i], bl[j], dS[i][j], 0, 0, 0);
+                    if constexpr (ROPE)        // (p~ unrotated is a bf16 value)
+                        dS[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al[i], bh[j], dS[i][j], 0, 0, 0);
+                }
+        } else {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int tt = 4 * st + q, swr = 4 * (st & 3);     // the swap of row tt
+                float av[T], bv[T];
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    av[t] = Pt[tt * LD + ((16 * t + m) ^ swr)];
+                    bv[t] = Dn[tt * LD + ((16 * t + m) ^ swr)];
+                }
+#pragma unroll
+                for (int i = 0; i < T; ++i)
+#pragma unroll
+                    for (int j = 0; j < T; ++j)
+                        dS[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], dS[i][j], 0, 0, 0);
+            }
         }
     }
     bwd_flush<D, ES>(rdQ, pq);
@@ -3342,6 +3452,24 @@ svla_bwd_key(const BwdArgs a)
     float hr[FPL];
 #pragma unroll
     for (int L = 0; L < FPL; ++L) hr[L] = hs[FPL * q + L];
+    // bf16 inputs at d = 32: both products on v_mfma_f32_16x16x32_bf16 with G
+    // as bf16 hi + lo (as on the query side); v, and a~ without RoPE, are
+    // bf16 values, so their lo parts vanish and two products suffice
+    constexpr bool BF = SVLA_BWD_BF16 && ES == 2 && D == 32;
+    bf16x8_t gfh[BF ? T : 1], gfl[BF ? T : 1], gbh[BF ? T : 1], gbl[BF ? T : 1];
+    if constexpr (BF) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float xf[8], xb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xf[i] = go.f(t, i);
+                xb[i] = go.b(t, i);
+            }
+            split_bf16x8(xf, gfh[t], gfl[t]);
+            split_bf16x8(xb, gbh[t], gbl[t]);
+        }
+    }
 
     Pending<D, ES> pv, pk;
     for (; grp < ngroups; grp += 4) {
@@ -3368,13 +3496,27 @@ svla_bwd_key(const BwdArgs a)
         f32x4_t dv[T], da[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) dv[t] = da[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < FPL; ++st)
+        if constexpr (BF) {
+            bf16x8_t ah, al, vh, vl;
+            split_bf16x8(at, ah, al);
+            split_bf16x8(v, vh, vl);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                dv[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(go.f(t, st), at[st], dv[t], 0, 0, 0);
-                da[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(go.b(t, st), v[st], da[t], 0, 0, 0);
+                dv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gfh[t], ah, dv[t], 0, 0, 0);
+                if constexpr (ROPE) dv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gfh[t], al, dv[t], 0, 0, 0);
+                dv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gfl[t], ah, dv[t], 0, 0, 0);
+                da[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gbh[t], vh, da[t], 0, 0, 0);
+                da[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gbl[t], vh, da[t], 0, 0, 0);
             }
+        } else {
+#pragma unroll
+            for (int st = 0; st < FPL; ++st)
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    dv[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(go.f(t, st), at[st], dv[t], 0, 0, 0);
+                    da[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(go.b(t, st), v[st], da[t], 0, 0, 0);
+                }
+        }
         float x[FPL], y[FPL];
 #pragma unroll
         for (int L = 0; L < FPL; ++L) {
