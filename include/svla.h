@@ -305,8 +305,10 @@ svla_status svla_temporal_conv(svla_dtype dt, int B, int nb, int F, int P, int C
  * (R phi(q)) dnum^T + g_{c+1} G_{c+1} (H_c likewise with dden phi(q)) is the
  * gradient reaching S_c; dv = G_c^T R phi(k), dk = [k > 0] (R^T G_c v + H_c);
  * dg_c = <G_c, S_{c-1}> + <H_c, z_{c-1}>.  The derivative of phi at 0 is 0, and
- * a token whose denominator is 0 passes no gradient.  Arithmetic is fp32
- * throughout (the gradients are rounded once, to the output dtype).
+ * a token whose denominator is 0 passes no gradient.  Sums are fp32 and the
+ * gradients are rounded once, to the output dtype; for SVLA_BF16 at d = 32 the
+ * products take their fp32 operands as bf16 hi + lo pairs (about 2^-16
+ * relative), otherwise they are fp32 products.
  * dt: SVLA_F32 or SVLA_BF16 (SVLA_FP8: SVLA_ERR_UNSUPPORTED); d: 32 or 64
  * (128: SVLA_ERR_UNSUPPORTED).  dQ, dK, dV must not overlap each other or the
  * inputs (SVLA_ERR_VALUE).  Workspace: svla_workspace_size(SVLA_OP_BACKWARD).
