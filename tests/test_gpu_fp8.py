@@ -132,6 +132,27 @@ def test_chained_steps(svla, commit, with_rope, gate):
     assert eo <= TOL_O and nerr(S.cpu().numpy(), ref["S"]) <= TOL_S and nerr(z.cpu().numpy(), ref["z"]) <= TOL_S
 
 
+@pytest.mark.parametrize("with_rope", [False, True])
+def test_one_launch_step_four_q_groups(svla, with_rope):
+    """An fp8 block step of 70 heads x 2640 tokens: one launch whose waves
+    read out four 16-token Q groups each, against the oracle's step."""
+    H, n = 70, 2640
+    x = _inputs(1, H, 1, n, seed=27)
+    rng = np.random.default_rng(28)
+    S_in = (rng.standard_normal((1, H, 32, 32)) * 20).astype(np.float32)
+    z_in = np.abs(rng.standard_normal((1, H, 32)) * 80).astype(np.float32)
+    rope = Rope(8, 12, 12, 5, 7, 4, 1e4) if with_rope else None
+    plan = svla.describe("block_step", F8, 1, H, 1, n, 32, rope=rope)
+    assert [k["slot"] for k in plan["kernels"]] == ["step"] and plan["step_tile"] > 16 * 16 * 2, plan
+    Q, K, V = (_f8(x[k + "_bits"]) for k in "QKV")
+    O, S, z = svla.block_step(Q, K, V, torch.from_numpy(S_in).to(DEV), torch.from_numpy(z_in).to(DEV),
+                              rope=rope)
+    torch.cuda.synchronize()
+    ref = oracle.step(x["Q"], x["K"], x["V"], S_in, z_in, rope=rope, eps=x["eps"])
+    assert nerr(O.float().cpu().numpy(), ref["O"]) <= TOL_O
+    assert nerr(S.cpu().numpy(), ref["S"]) <= TOL_S and nerr(z.cpu().numpy(), ref["z"]) <= TOL_S
+
+
 @pytest.mark.parametrize("name", ["c2", "c3", "c4"])
 def test_full_size_every_head(svla, name):
     """The 480p, 720p and minute-long shapes with fp8 inputs (the minute-long

@@ -242,6 +242,7 @@ def test_chained_steps_equal_one_shot(svla, dtype, gate, d, with_rope, commit):
     (1, 3, 15, True, True),         # less than one 16-token group
     (2, 5, 2048, True, False),      # many tiles of few groups
     (1, 70, 2640, False, True),     # the 720p step: four Q groups per wave
+    (1, 70, 2640, True, False),     # ... with RoPE
     (1, 200, 3000, False, False),   # 200 heads, three tiles of up to four groups per wave
     (2, 5, 3072, True, False),      # the longest one-launch block
     (1, 2, 3073, True, True),       # one token longer: the two-kernel step
