@@ -32,6 +32,11 @@ Also:
                                profiles/counters_<T>.json
   --summarize-mfma M --tag T   fold a rocprofv3 --pmc run of the matrix-core
                                counters into profiles/mfma_<T>.json
+  --summarize-kernels CSV --tag T
+                               profiles/kernels_<workload>.md from a rocprofv3
+                               --kernel-trace --stats kernel_stats.csv
+  --summarize-tables           the traffic and matrix-core tables in profiles/
+                               from the current source's summaries
 """
 from __future__ import annotations
 
@@ -99,6 +104,10 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=4,
                     metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     ap.add_argument("--summarize-mfma", metavar="DIR")
+    ap.add_argument("--summarize-kernels", metavar="KERNEL_STATS_CSV",
+                    help="write profiles/kernels_<workload>.md for --tag from a rocprofv3 --stats CSV")
+    ap.add_argument("--summarize-tables", action="store_true",
+                    help="rewrite the traffic and matrix-core tables in profiles/ from the summaries")
     ap.add_argument("--tag", help="name of the summary written by --summarize-*")
     return ap.parse_args()
 
@@ -823,6 +832,103 @@ def summarize_mfma(mdir, tag):
     print(json.dumps(out, indent=1))
 
 
+# profile summaries: tag -> (kernel table file, workload title, bench options)
+PROFILE_TAGS = {
+    "c4_stream": ("kernels_c4_minute_rope_stream.md", "c4 minute-long streaming (80 one-launch block steps of B1 H70 1170 tokens d32, bf16, RoPE, HIP graph)", "--config c4 --c4-mode stream"),
+    "c4_oneshot": ("kernels_c4_minute_rope_oneshot.md", "c4 minute-long one shot (B1 H70, 80 blocks x 1170 tokens d32, bf16, RoPE)", "--config c4 --c4-mode oneshot"),
+    "c3": ("kernels_c3_720p_block_causal.md", "c3 720p block-causal (B1 H70, 7 blocks x 2640 tokens d32, bf16)", "--config c3"),
+    "c3_stream": ("kernels_c3_720p_block_steps.md", "c3 720p as 7 block steps (B1 H70, 2640 tokens d32, bf16, one-launch step, HIP graph)", "--config c3 --stream"),
+    "c3_bwd": ("kernels_c3_720p_backward.md", "c3 720p backward (B1 H70, 7 blocks x 2640 tokens d32, bf16 in and out)", "--config c3 --backward"),
+    "c2": ("kernels_c2_480p_noncausal.md", "c2 480p non-causal (B2 H70, 8190 tokens d32, bf16)", "--config c2"),
+    "c5": ("kernels_c5_gated_d128.md", "c5 2.0-style gated (B1 H20, 8 blocks x 1760 tokens d128, bf16)", "--config c5"),
+    "c5_stream": ("kernels_c5_gated_d128_stream.md", "c5 2.0-style gated as 8 block steps (B1 H20, 1760 tokens d128, bf16, gate per step, HIP graph)", "--config c5 --stream"),
+    "t3": ("kernels_t3_720p_temporal_conv.md", "t3 720p temporal convolution (B1, 7 blocks x 3 frames, 22x40 positions, 2240 channels, bf16)", "--config t3"),
+    "t4": ("kernels_t4_minute_temporal_conv_stream.md", "t4 minute-long temporal convolution (80 block steps of 3 frames, 15x26 positions, 2240 channels, bf16, cache carried)", "--config t4"),
+    "c4_stream_fp8": ("kernels_c4_minute_rope_stream_fp8.md", "c4 minute-long streaming with fp8 (E4M3) Q, K, V (80 one-launch block steps, bf16 O, RoPE, HIP graph)", "--config c4 --c4-mode stream --dtype fp8"),
+    "c3_fp8": ("kernels_c3_720p_block_causal_fp8.md", "c3 720p block-causal with fp8 (E4M3) Q, K, V (bf16 O)", "--config c3 --dtype fp8"),
+}
+
+
+def summarize_kernels(stats_csv, tag):
+    """profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace --stats
+    kernel_stats.csv of `python bench.py <options of tag> --steps 5 --warmup 2
+    --no-cpu-baseline`: the six kernels with the most GPU time."""
+    fn, title, opts = PROFILE_TAGS[tag]
+    rows = list(csv.DictReader(open(stats_csv)))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+
+    def short(n):
+        n = n.replace("(anonymous namespace)::", "")
+        return n if len(n) <= 90 else n[:87] + "..."
+    out = ["# rocprofv3 kernel statistics: " + title, "",
+           "Library source sha256 prefix: `%s` (block_causal_linear_relu_amd/csrc/svla.hip)." % source_hash(), "",
+           "Command (run from the repository root; `<out>` is a scratch directory), then this table with "
+           "`python bench.py --summarize-kernels <out>/kt_kernel_stats.csv --tag %s`:" % tag, "", "```",
+           "rocprofv3 --kernel-trace --stats -d <out> -o kt --output-format csv -- python -u bench.py %s "
+           "--steps 5 --warmup 2 --no-cpu-baseline" % opts, "```", "",
+           "The bench process also runs its clock-settling steps, the warm-up steps, the per-kernel event "
+           "loop and the input set-up copies; every libsvla kernel of every step is listed.", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows[:6]:
+        out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
+            short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, 100 * float(r["TotalDurationNs"]) / tot))
+    with open(os.path.join(ROOT, "profiles", fn), "w") as fh:
+        fh.write("\n".join(out) + "\n")
+
+
+def summarize_tables():
+    """profiles/hbm_traffic_counters.md and profiles/mfma_utilisation.md from
+    the counter summaries of the current source (counters_<tag>.json,
+    mfma_<tag>.json); a summary of other kernels is left out."""
+    h = source_hash()
+    fetch_f = write_f = None
+    traffic = ["| tag | bench option | kernel | fetch (KiB) | write (KiB) | HBM bytes per launch |",
+               "|---|---|---|---|---|---|"]
+    mfma = ["| tag | kernel | MfmaUtil (%) | VALUBusy (%) | bf16 MFMA flops per launch |", "|---|---|---|---|---|"]
+    for tag, (_, _, opts) in PROFILE_TAGS.items():
+        c = _load_summary("counters", tag)
+        if c is not None:
+            fetch_f, write_f = c["fetch_factor"], c["write_factor"]
+            for k, v in c["kernels"].items():
+                traffic.append("| %s | `%s` | `%s` | %.0f | %.0f | %.2f MB |" % (
+                    tag, opts, k, v["fetch_kib"] or 0, v["write_kib"] or 0, v["hbm_bytes_per_dispatch"] / 1e6))
+        m = _load_summary("mfma", tag)
+        if m is not None:
+            for k, v in m["kernels"].items():
+                mfma.append("| %s | `%s` | %.1f | %.1f | %.3g |" % (
+                    tag, k, v["MfmaUtil"] or 0, v["VALUBusy"] or 0, v["MfmaFlopsBF16"] or 0))
+    pmc = "--steps 2 --warmup 1 --settle 0 --no-cpu-baseline"
+    t = ["# HBM traffic per kernel launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+         "Each counter was collected in a run of its own (run from the repository root; `<out>` is a "
+         "scratch directory; `<args>` is the workload's bench option in the table below):", "", "```",
+         "rocprofv3 --pmc FETCH_SIZE -d <out>/<tag>/f -o f --output-format csv -- python -u bench.py <args> " + pmc,
+         "rocprofv3 --pmc WRITE_SIZE -d <out>/<tag>/w -o w --output-format csv -- python -u bench.py <args> " + pmc,
+         "rocprofv3 --pmc FETCH_SIZE -d <out>/copy/f -o f --output-format csv -- python -u bench.py --copy-calibration",
+         "rocprofv3 --pmc WRITE_SIZE -d <out>/copy/w -o w --output-format csv -- python -u bench.py --copy-calibration",
+         "python bench.py --summarize-counters <out>/<tag>/f <out>/<tag>/w <out>/copy/f <out>/copy/w --tag <tag>",
+         "python bench.py --summarize-tables", "```", ""]
+    if fetch_f is not None:
+        t += ["Calibration: a plain device copy of 512 MiB (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = "
+              "%.3f x and WRITE_SIZE = %.3f x its size in KiB, so fetch KiB x 1024 x %.3f and write KiB x "
+              "1024 x %.3f are bytes." % (1 / fetch_f, 1 / write_f, fetch_f, write_f), ""]
+    t += ["Library source sha256 prefix: `%s`." % h, ""] + traffic
+    mm = ["# Matrix-core and vector-ALU utilisation per kernel (rocprofv3 derived counters)", "",
+          "One `--pmc` pass per workload (run from the repository root):", "", "```",
+          "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 VALUBusy GRBM_GUI_ACTIVE -d <out>/<tag>/m -o m "
+          "--output-format csv -- python -u bench.py <args> " + pmc,
+          "python bench.py --summarize-mfma <out>/<tag>/m --tag <tag>", "python bench.py --summarize-tables", "```", "",
+          "MfmaUtil = 100 x sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs): the share of the "
+          "kernel's time the matrix cores were busy. MfmaFlopsBF16 = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 per "
+          "dispatch (bf16 matrix flops, the backward's bf16 hi + lo products included; fp32 products are not "
+          "counted there). VALUBusy: the share of time the vector ALUs issued.", "",
+          "Library source sha256 prefix: `%s`." % h, ""] + mfma
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic_counters.md"), "w") as fh:
+        fh.write("\n".join(t) + "\n")
+    with open(os.path.join(ROOT, "profiles", "mfma_utilisation.md"), "w") as fh:
+        fh.write("\n".join(mm) + "\n")
+
+
 def copy_calibration():
     import torch
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
@@ -890,6 +996,12 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, tag=args.tag or args.config)
+        return
+    if args.summarize_kernels:
+        summarize_kernels(args.summarize_kernels, args.tag)
+        return
+    if args.summarize_tables:
+        summarize_tables()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: measures one GPU only (the path shards by (batch, head) with no "
